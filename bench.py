@@ -1,0 +1,428 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,gdp]
+
+Three legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+  prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
+           (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
+           q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
+           the headline `value`.
+  decode:  one token for each of 128 requests (16 padding) over a
+           [256, 32, 128, 128] fp32 slot cache; reported as state GB/s.  The
+           256 MB last-level cache is flushed (1 GiB write) before every launch,
+           outside the timed launch.
+  gdp:     gated delta product, 2 Householder sub-steps, B=1, T=65536, H=32,
+           K = V = 128, bf16, chunk 128 tokens; tokens/s.
+Per-launch kernel durations come from HIP events on the launch stream.  The
+roofline object is for the headline prefill kernel: algorithmic HBM bytes per
+launch (inputs read once, outputs and states written once) over the mean launch
+time, against 8 TB/s.  The CPU baseline is the fp64 oracle on a bounded sample
+of the prefill workload, on all host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (H=32,K=V=128) + decode state GB/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2516.6   # dense fp16/bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="prefill,decode,gdp")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="value heads of the prefill workload the CPU oracle runs")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="a short run for hardware-counter profiling: 3 prefill and 3 decode "
+                         "launches plus a device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-db", metavar="DB",
+                    help="print a text summary of a rocprofv3 results database and exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="derive HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE "
+                         "profile of --profile-run, write profiles/traffic.json and exit")
+    return ap.parse_args()
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_BYTES = 1 << 30     # the calibration copy reads and writes 1 GiB each
+
+
+def kernel_source_hash(name):
+    """sha256 of a kernel source file: ties stored counter data to the code measured."""
+    import hashlib
+    path = os.path.join(ROOT, "gated_delta_rule_71_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel, source):
+    """Counter-measured HBM bytes per launch for `kernel`, if taken on this source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("source_sha") != kernel_source_hash(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def summarize_db(db):
+    """Kernel durations and hardware counters per kernel from a rocprofv3 database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    tabs = {r[0] for r in con.execute("select name from sqlite_master")}
+    if "top_kernels" in tabs and con.execute("select count(*) from top_kernels").fetchone()[0]:
+        print("kernel durations (ns): name | calls | total | average | percent")
+        for name, calls, tot, avg, pct in con.execute(
+                "select name, total_calls, total_duration, average, percentage "
+                "from top_kernels order by total_duration desc"):
+            print(f"  {name[:110]} | {calls} | {tot:.0f} | {avg:.1f} | {pct:.2f}")
+    if "pmc_events" in tabs and con.execute("select count(*) from pmc_events").fetchone()[0]:
+        print("counters per dispatch (summed over instances): dispatch | kernel | counter | value")
+        rows = con.execute(
+            "select dispatch_id, name, counter_name, sum(counter_value) from pmc_events "
+            "group by dispatch_id, counter_name order by dispatch_id").fetchall()
+        for d, name, cn, val in rows:
+            print(f"  {d} | {name[:90]} | {cn} | {val:.6g}")
+
+
+def traffic_from(fetch_db, write_db):
+    """HBM bytes per launch of the prefill and decode kernels from two counter profiles.
+
+    Each counter is scaled by what it reads for the calibration copy of
+    COPY_PROBE_BYTES (the largest device copy in the profile), so the result is
+    in bytes whatever unit or coverage the counter has on this part.
+    """
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute(
+            "select dispatch_id, name, sum(counter_value) from pmc_events where counter_name = ? "
+            "group by dispatch_id", (counter,)).fetchall()
+        copy = max(v for _, n, v in rows if "copyBuffer" in n)
+        scale = COPY_PROBE_BYTES / copy
+        out = {}
+        for key, pat in (("prefill_varlen", "prefill_kernel"), ("decode", "decode_kernel")):
+            vals = [v for _, n, v in rows if pat in n]
+            out[key] = (float(np.mean(vals)) * scale, len(vals))
+        return out, scale
+
+    fetch, fs = per_kernel(fetch_db, "FETCH_SIZE")
+    write, ws = per_kernel(write_db, "WRITE_SIZE")
+    data = {}
+    for key, src in (("prefill_varlen", "prefill.hip"), ("decode", "decode.hip")):
+        data[key] = {"source_sha": kernel_source_hash(src),
+                     "fetch_bytes": fetch[key][0], "write_bytes": write[key][0],
+                     "bytes_per_launch": fetch[key][0] + write[key][0],
+                     "launches": fetch[key][1]}
+    data["calibration"] = {"copy_bytes": COPY_PROBE_BYTES, "fetch_scale": fs, "write_scale": ws,
+                           "note": "counter value x scale = bytes; scale from the copy probe"}
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(data, indent=1))
+
+
+def up(a):
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def nbytes(*arrays):
+    return int(sum(a.nbytes for a in arrays if a is not None))
+
+
+def time_launches(launch, steps, warmup, before=None):
+    """Run `launch` warmup + steps times; returns (wall ms/step, mean event ms/launch)."""
+    import torch
+    for _ in range(warmup):
+        if before:
+            before()
+        launch()
+    torch.cuda.synchronize()
+    evs = []
+    stream = torch.cuda.current_stream()
+    wall = 0.0
+    if before is None:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        evs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    else:
+        # per-launch preparation (cache flush) stays outside the timed launches
+        for i in range(steps):
+            before()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            launch()
+            e.record(stream)
+            torch.cuda.synchronize()
+            evs.append(s.elapsed_time(e))
+        wall = float(np.mean(evs))
+    return wall, float(np.mean(evs))
+
+
+def prefill_bytes(wl, out_bytes_per_elem=2):
+    """Algorithmic HBM bytes of one prefill: inputs once, output once, states in and out."""
+    B, T, Hk, Hv, K, V = wl.shape
+    N = wl.num_seqs
+    tokens = B * T
+    io = nbytes(wl.q, wl.k, wl.v, wl.g, wl.beta) + tokens * Hv * V * out_bytes_per_elem
+    states = 2 * N * Hv * K * V * 4
+    return io + states
+
+
+def prefill_flops_per_token(wl, chunk_tokens):
+    """Dense-tile flops per token of the chunked form (measurement)."""
+    B, T, Hk, Hv, K, V = wl.shape
+    n_h = wl.num_householder
+    C = chunk_tokens
+    if n_h == 1:
+        return Hk * 4 * C * K + Hv * (2 * C * K + 4 * C * V + 6 * K * V)
+    return Hv * ((4 * n_h + 2) * K * V + 2 * n_h * n_h * C * (2 * K + V) + 2 * n_h * C * (K + V))
+
+
+def run_prefill_leg(wl, steps, warmup):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    d = {n: up(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")}
+    cu = up(wl.cu_seqlens)
+    idx = up(wl.state_indices)
+    h0 = up(wl.initial_state)
+    out = torch.empty((wl.q.shape[0], wl.q.shape[1], wl.v.shape[-2], wl.v.shape[-1]),
+                      dtype=torch.bfloat16, device="cuda")
+    fs = torch.empty_like(h0) if idx is None else h0
+    # one checked call through the Python binding, then the same C call with the
+    # argument struct built once, so the timed launches carry no Python marshalling
+    gdr.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                               chunk_size=wl.chunk_size, initial_state=h0,
+                               output_final_state=True, cu_seqlens=cu, state_indices=idx,
+                               out=out, final_state=fs)
+    args = gdr.prefill_args(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=wl.chunk_size,
+                            initial_state=h0, final_state=fs, cu_seqlens=cu,
+                            state_indices=idx, out=out)
+    lib = gdr.library()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.gdr_chunk_gated_delta_rule(args, stream)
+        assert rc == 0, rc
+
+    wall, kern = time_launches(launch, steps, warmup)
+    return wall, kern
+
+
+def profile_run():
+    """3 prefill launches, 3 decode launches (cache flushed before each) and a copy probe."""
+    import torch
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import gated_delta_rule_71_amd as gdr
+    from gated_delta_rule_71_amd import workloads as W
+    wl2 = W.config2()
+    run_prefill_leg(wl2, 3, 0)
+    wl3 = W.config3()
+    d = [up(x) for x in (wl3.q, wl3.k, wl3.v, wl3.g, wl3.beta)]
+    cache, idx = up(wl3.cache), up(wl3.batch_indices)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        flush.zero_()
+        gdr.ssm_decode(*d, cache, batch_indices=idx)
+    src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile run done", file=sys.stderr)
+
+
+def main():
+    args = parse()
+    if args.summarize_db:
+        summarize_db(args.summarize_db)
+        return
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import gated_delta_rule_71_amd as gdr
+    from gated_delta_rule_71_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile_run:
+        profile_run()
+        return
+    legs = set(args.legs.split(","))
+    res = {}
+    t_start = time.perf_counter()
+
+    # ---- headline: packed varlen prefill, Hv = 32 ----------------------------------
+    wl2 = W.config2()
+    tokens2 = wl2.tokens
+    print(f"[bench] prefill workload {wl2.name}: {tokens2} tokens, lengths "
+          f"{wl2.meta['lengths']}", file=sys.stderr, flush=True)
+    if "prefill" in legs:
+        wall, kern = run_prefill_leg(wl2, args.steps, args.warmup)
+        byt = prefill_bytes(wl2)
+        F = prefill_flops_per_token(wl2, wl2.chunk_size)
+        res["prefill"] = dict(wall_ms=wall, kernel_ms=kern, tokens=tokens2, bytes=byt,
+                              flops=F * tokens2, flops_per_token=F)
+        print(f"[bench] prefill: {wall:.3f} ms/step, kernel {kern:.3f} ms", file=sys.stderr,
+              flush=True)
+
+    # ---- decode ------------------------------------------------------------------------
+    if "decode" in legs:
+        wl3 = W.config3()
+        d = [up(x) for x in (wl3.q, wl3.k, wl3.v, wl3.g, wl3.beta)]
+        cache = up(wl3.cache)
+        idx = up(wl3.batch_indices)
+        out = torch.empty((wl3.q.shape[0], wl3.v.shape[1], wl3.v.shape[2]),
+                          dtype=torch.bfloat16, device="cuda")
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        gdr.ssm_decode(*d, cache, batch_indices=idx, out=out)
+        dargs = gdr.decode_args(*d, cache, batch_indices=idx, out=out)
+        lib = gdr.library()
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def launch_dec():
+            rc = lib.gdr_ssm_decode(dargs, stream)
+            assert rc == 0, rc
+
+        wall, kern = time_launches(launch_dec, args.steps, args.warmup,
+                                   before=lambda: flush.zero_())
+        n_real = int((wl3.batch_indices >= 0).sum())
+        Hv, K, V = wl3.cache.shape[1:]
+        state_bytes = 2 * n_real * Hv * K * V * 4
+        res["decode"] = dict(wall_ms=wall, kernel_ms=kern, state_bytes=state_bytes,
+                             workload=wl3.name, n_real=n_real)
+        print(f"[bench] decode: kernel {kern:.4f} ms", file=sys.stderr, flush=True)
+        del cache, flush
+
+    # ---- gated delta product, long context ----------------------------------------------
+    if "gdp" in legs:
+        wl4 = W.config4()
+        wall, kern = run_prefill_leg(wl4, max(2, args.steps // 4), min(args.warmup, 2))
+        byt = prefill_bytes(wl4)
+        F = prefill_flops_per_token(wl4, wl4.chunk_size)
+        res["gdp"] = dict(wall_ms=wall, kernel_ms=kern, tokens=wl4.tokens, bytes=byt,
+                          flops=F * wl4.tokens, flops_per_token=F, workload=wl4.name)
+        print(f"[bench] gdp: kernel {kern:.3f} ms", file=sys.stderr, flush=True)
+        del wl4
+
+    # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from gated_delta_rule_71_amd.workloads import as_f64
+        Hv = wl2.v.shape[-2]
+        Hk = wl2.q.shape[-2]
+        nh = min(args.cpu_heads, Hv)
+        heads = list(range(0, nh))
+        kh = sorted(set(h * Hk // Hv for h in heads))
+        sel_k = {hk: i for i, hk in enumerate(kh)}
+        q = as_f64(wl2.q[:, :, kh])
+        k = as_f64(wl2.k[:, :, kh])
+        v = as_f64(wl2.v[:, :, heads])
+        g = wl2.g[:, :, heads].astype(np.float64)
+        beta = wl2.beta[:, :, heads].astype(np.float64)
+        cache = as_f64(wl2.initial_state[:, heads]).copy()
+        # grouping is preserved: the selected v heads map onto the selected k heads
+        assert all(sel_k[h * Hk // Hv] == h * len(kh) // nh for h in heads)
+        threads = oracle.threads_used(0)
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, g, beta, cu_seqlens=wl2.cu_seqlens, initial_state=cache,
+                       state_indices=wl2.state_indices, final_state_out=cache, threads=threads)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=tokens2 * nh / Hv / dt, unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"{wl2.name}: all {tokens2} tokens of the 8 sequences, {nh} of "
+                          f"{Hv} value heads ({dt:.1f} s), scaled to all heads")
+        print(f"[bench] cpu oracle: {dt:.1f} s on {threads} threads", file=sys.stderr,
+              flush=True)
+
+    # ---- report -----------------------------------------------------------------------
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16/f32", "data": "synthetic"}
+    if "prefill" in res:
+        p = res["prefill"]
+        tps = p["tokens"] / (p["wall_ms"] * 1e-3)
+        achieved = p["bytes"] / (p["kernel_ms"] * 1e-3) / 1e9
+        line.update(value=tps, unit="tokens/s", ms_per_step=p["wall_ms"])
+        line["config"] = {
+            "workload": wl2.name, "tokens": p["tokens"], "seq_lens": wl2.meta["lengths"],
+            "num_qk_heads": int(wl2.q.shape[2]), "num_v_heads": int(wl2.v.shape[-2]),
+            "head_k": 128, "head_v": 128, "chunk_size": wl2.chunk_size, "qkv": "bf16",
+            "state": "fp32 slot cache", "parallelism": "single GPU"}
+        line["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                            "traffic": stored_traffic("prefill_varlen", "prefill.hip"),
+                            "kernel": "prefill_kernel", "bytes_per_launch": p["bytes"],
+                            "kernel_ms": p["kernel_ms"]}
+        tf = p["flops"] / (p["kernel_ms"] * 1e-3) / 1e12
+        line["mfma"] = {"flops_per_token": p["flops_per_token"], "achieved_tflops": tf,
+                        "peak_tflops": MFMA_PEAK_TFLOPS, "frac": tf / MFMA_PEAK_TFLOPS}
+    if "decode" in res:
+        dd = res["decode"]
+        gbs = dd["state_bytes"] / (dd["kernel_ms"] * 1e-3) / 1e9
+        line["decode"] = {"workload": dd["workload"], "value": gbs, "unit": "GB/s",
+                          "kernel_ms": dd["kernel_ms"], "state_bytes": dd["state_bytes"],
+                          "real_requests": dd["n_real"],
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                       "traffic": stored_traffic("decode", "decode.hip")}}
+        if "prefill" not in res:
+            line.update(value=gbs, unit="GB/s", ms_per_step=dd["wall_ms"])
+    if "gdp" in res:
+        gg = res["gdp"]
+        tps = gg["tokens"] / (gg["wall_ms"] * 1e-3)
+        gbs = gg["bytes"] / (gg["kernel_ms"] * 1e-3) / 1e9
+        tf = gg["flops"] / (gg["kernel_ms"] * 1e-3) / 1e12
+        line["gdp"] = {"workload": gg["workload"], "value": tps, "unit": "tokens/s",
+                       "kernel_ms": gg["kernel_ms"],
+                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+                       "mfma": {"flops_per_token": gg["flops_per_token"],
+                                "achieved_tflops": tf, "frac": tf / MFMA_PEAK_TFLOPS}}
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    line["bench_wall_s"] = time.perf_counter() - t_start
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

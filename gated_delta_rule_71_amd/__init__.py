@@ -1,0 +1,220 @@
+"""MI355X (gfx950) gated delta rule: chunked prefill and slot-indexed decode.
+
+Python face of libgdr.so (C ABI in include/gdr.h).  These functions only
+marshal arguments: torch tensors provide device memory and the current HIP
+stream, and every step of the computation runs in the library's kernels.
+
+    o, final_state = chunk_gated_delta_rule(q, k, v, g, beta, scale=None,
+        chunk_size=64, initial_state=None, output_final_state=False,
+        use_qk_l2norm_in_kernel=False, cu_seqlens=None, **kwargs)
+    o = ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, ...)
+
+The signature of chunk_gated_delta_rule follows torch_chunk_gated_delta_rule on
+the Megatron Core API page "core.ssm.gated_delta_net.gdn" (extra keyword
+arguments are accepted and ignored there too); ssm_decode follows ssm_decode on
+the pages "core.ssm.gated_delta_net.gdn" / "core.ssm.gated_delta_product".
+"""
+from __future__ import annotations
+
+import math
+
+from . import _lib
+
+__all__ = ["chunk_gated_delta_rule", "ssm_decode", "library", "abi_version"]
+
+
+def library():
+    """The loaded libgdr.so (raises if it has not been built)."""
+    return _lib.load()
+
+
+def abi_version() -> int:
+    return int(library().gdr_abi_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return _lib.GDR_DTYPE_F32
+    if dt == torch.bfloat16:
+        return _lib.GDR_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() not in (ndim if isinstance(ndim, tuple) else (ndim,)):
+        raise ValueError(f"{name} has {t.dim()} dims")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes_stream(s)
+
+
+def ctypes_stream(s):
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def _raise(code, what):
+    if code != _lib.GDR_OK:
+        raise RuntimeError(f"{what} failed: {_lib.status_string(code)}")
+
+
+def prefill_args(q, k, v, g, beta, *, scale=None, chunk_size=64, initial_state=None,
+                 final_state=None, use_qk_l2norm_in_kernel=False, cu_seqlens=None,
+                 state_indices=None, out=None):
+    """Fill a gdr_prefill_args struct from tensors (no checks beyond shapes)."""
+    B, T, Hk, K = q.shape
+    n_h = k.shape[2] if k.dim() == 5 else 1
+    Hv, V = v.shape[-2], v.shape[-1]
+    a = _lib.PrefillArgs()
+    a.batch, a.seqlen = B, T
+    a.num_seqs = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    a.num_qk_heads, a.num_v_heads, a.head_k, a.head_v = Hk, Hv, K, V
+    a.num_householder = n_h
+    a.chunk_size = int(chunk_size)
+    a.qkv_dtype = _dtype_code(q.dtype)
+    a.out_dtype = _dtype_code(out.dtype)
+    a.use_qk_l2norm = int(bool(use_qk_l2norm_in_kernel))
+    a.scale = float("nan") if scale is None else float(scale)
+    a.num_slots = initial_state.shape[0] if (state_indices is not None and
+                                             initial_state is not None) else (
+        final_state.shape[0] if (state_indices is not None and final_state is not None) else 0)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.state_indices = _ptr(state_indices)
+    a.initial_state = _ptr(initial_state)
+    a.final_state = _ptr(final_state)
+    a.out = _ptr(out)
+    a.workspace = None
+    a.workspace_bytes = 0
+    return a
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None,
+                           output_final_state=False, use_qk_l2norm_in_kernel=False,
+                           cu_seqlens=None, *, state_indices=None, out_dtype=None, out=None,
+                           final_state=None, stream=None, **kwargs):
+    """Chunked prefill of the gated delta rule (packed or batched sequences).
+
+    q [B,T,Hk,K]; k [B,T,Hk,K] or [B,T,n_h,Hk,K]; v [B,T,Hv,V] or [B,T,n_h,Hv,V]
+    (float32 or bfloat16, one dtype); g [B,T,Hv] and beta [B,T,Hv] /
+    [B,T,n_h,Hv] float32; cu_seqlens int32 [N+1] (B must be 1).
+    initial_state float32 [N,Hv,K,V]; with ``state_indices`` (int32 [N]) it is a
+    slot cache [slots,Hv,K,V], read at max(idx, 0) and written back in place at
+    idx >= 0 (or into ``final_state`` if given).
+    Returns (o [B,T,Hv,V], final_state or None).
+    """
+    torch = _torch()
+    lib = library()
+    _check(q, "q", ndim=4)
+    _check(k, "k", dtype=q.dtype, ndim=(4, 5))
+    _check(v, "v", dtype=q.dtype, ndim=(4, 5))
+    _check(g, "g", dtype=torch.float32, ndim=3)
+    _check(beta, "beta", dtype=torch.float32, ndim=(3, 4))
+    B, T, Hk, K = q.shape
+    n_h = k.shape[2] if k.dim() == 5 else 1
+    Hv, V = v.shape[-2], v.shape[-1]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if state_indices is not None:
+        _check(state_indices, "state_indices", dtype=torch.int32, ndim=1)
+        if state_indices.numel() != N:
+            raise ValueError("state_indices needs one entry per sequence")
+        if initial_state is None and final_state is None:
+            raise ValueError("state_indices needs the slot cache as initial_state")
+        if final_state is None:
+            final_state = initial_state
+    elif output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=q.device)
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        if st is not None:
+            _check(st, name, dtype=torch.float32, ndim=4)
+    if out is None:
+        od = v.dtype if out_dtype is None else out_dtype
+        out = torch.empty((B, T, Hv, V), dtype=od, device=q.device)
+    else:
+        _check(out, "out", ndim=4)
+    a = prefill_args(q, k, v, g, beta, scale=scale, chunk_size=chunk_size,
+                     initial_state=initial_state, final_state=final_state,
+                     use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
+                     state_indices=state_indices, out=out)
+    _raise(lib.gdr_chunk_gated_delta_rule(a, _stream(stream)), "gdr_chunk_gated_delta_rule")
+    ret_state = final_state if (output_final_state or state_indices is not None) else None
+    return out, ret_state
+
+
+def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,
+                use_qk_l2norm_in_kernel=False, out=None):
+    n, Hk, K = q.shape
+    n_h = k.shape[1] if k.dim() == 4 else 1
+    Hv, V = v.shape[-2], v.shape[-1]
+    a = _lib.DecodeArgs()
+    a.batch, a.num_qk_heads, a.num_v_heads, a.head_k, a.head_v = n, Hk, Hv, K, V
+    a.num_householder = n_h
+    a.num_slots = ssm_state.shape[0]
+    a.qkv_dtype = _dtype_code(q.dtype)
+    a.out_dtype = _dtype_code(out.dtype)
+    a.use_qk_l2norm = int(bool(use_qk_l2norm_in_kernel))
+    a.scale = float("nan") if scale is None else float(scale)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.state = _ptr(ssm_state)
+    a.batch_indices = _ptr(batch_indices)
+    a.out = _ptr(out)
+    return a
+
+
+def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
+               use_qk_l2norm_in_kernel=False, *, out_dtype=None, out=None, stream=None):
+    """One decode token per request, updating ``ssm_state`` [slots,Hv,K,V] in place.
+
+    q [n,Hk,K]; k [n,Hk,K] or [n,n_h,Hk,K]; v [n,Hv,V] or [n,n_h,Hv,V];
+    g [n,Hv]; beta [n,Hv] or [n,n_h,Hv] (float32); batch_indices int32 [n]
+    (-1: padding, reads slot 0, writes nothing) or None (request i <-> slot i).
+    Returns o [n,Hv,V].
+    """
+    torch = _torch()
+    lib = library()
+    _check(q, "q", ndim=3)
+    _check(k, "k", dtype=q.dtype, ndim=(3, 4))
+    _check(v, "v", dtype=q.dtype, ndim=(3, 4))
+    _check(g, "g", dtype=torch.float32, ndim=2)
+    _check(beta, "beta", dtype=torch.float32, ndim=(2, 3))
+    _check(ssm_state, "ssm_state", dtype=torch.float32, ndim=4)
+    if batch_indices is not None:
+        _check(batch_indices, "batch_indices", dtype=torch.int32, ndim=1)
+    n = q.shape[0]
+    Hv, V = v.shape[-2], v.shape[-1]
+    if out is None:
+        od = v.dtype if out_dtype is None else out_dtype
+        out = torch.empty((n, Hv, V), dtype=od, device=q.device)
+    else:
+        _check(out, "out", ndim=3)
+    a = decode_args(q, k, v, g, beta, ssm_state, batch_indices=batch_indices, scale=scale,
+                    use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, out=out)
+    _raise(lib.gdr_ssm_decode(a, _stream(stream)), "gdr_ssm_decode")
+    return out
+
+
+def default_scale(head_k: int) -> float:
+    return 1.0 / math.sqrt(head_k)

@@ -1,0 +1,157 @@
+// Host side of the C ABI declared in include/gdr.h: argument checks (pure host
+// code, no HIP calls), launch-shape selection and kernel dispatch.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "gdr.h"
+#include "gdr_internal.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int32_t d) { return d == GDR_DTYPE_F32 || d == GDR_DTYPE_BF16; }
+bool head_ok(int32_t d) { return d == 64 || d == 128; }
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1024;
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_string(int status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+    default: return "GDR_ERR_UNKNOWN";
+  }
+}
+
+int gdr_validate_prefill(const gdr_prefill_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->seqlen < 0 || a->num_seqs < 0) return GDR_ERR_INVALID_ARG;
+  if (a->num_qk_heads <= 0 || a->num_v_heads <= 0) return GDR_ERR_INVALID_ARG;
+  if (a->num_v_heads % a->num_qk_heads != 0) return GDR_ERR_INVALID_ARG;
+  if (a->head_k <= 0 || a->head_v <= 0 || a->num_householder <= 0 || a->chunk_size <= 0)
+    return GDR_ERR_INVALID_ARG;
+  if (!dtype_ok(a->qkv_dtype) || !dtype_ok(a->out_dtype)) return GDR_ERR_INVALID_ARG;
+  if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
+  if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (a->cu_seqlens) {
+    if (a->batch != 1) return GDR_ERR_INVALID_ARG;
+  } else if (a->num_seqs != a->batch) {
+    return GDR_ERR_INVALID_ARG;
+  }
+  if (a->state_indices && a->num_slots <= 0) return GDR_ERR_INVALID_ARG;
+  const int64_t tokens = int64_t{a->batch} * a->seqlen;
+  if (tokens * a->num_householder > kMaxRows) return GDR_ERR_UNSUPPORTED;
+  if (!head_ok(a->head_k) || !head_ok(a->head_v)) return GDR_ERR_UNSUPPORTED;
+  if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
+  if (!pow2(a->chunk_size) || a->chunk_size < 16 || a->chunk_size > 256)
+    return GDR_ERR_UNSUPPORTED;
+  if (tokens > 0) {
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out) return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+      return GDR_ERR_INVALID_ARG;
+  }
+  if ((a->initial_state && !aligned16(a->initial_state)) ||
+      (a->final_state && !aligned16(a->final_state)))
+    return GDR_ERR_INVALID_ARG;
+  if (a->workspace_bytes < gdr_prefill_workspace_bytes(a)) return GDR_ERR_WORKSPACE;
+  return GDR_OK;
+}
+
+int gdr_validate_decode(const gdr_decode_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->num_qk_heads <= 0 || a->num_v_heads <= 0) return GDR_ERR_INVALID_ARG;
+  if (a->num_v_heads % a->num_qk_heads != 0) return GDR_ERR_INVALID_ARG;
+  if (a->head_k <= 0 || a->head_v <= 0 || a->num_householder <= 0) return GDR_ERR_INVALID_ARG;
+  if (!dtype_ok(a->qkv_dtype) || !dtype_ok(a->out_dtype)) return GDR_ERR_INVALID_ARG;
+  if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
+  if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (!head_ok(a->head_k) || !head_ok(a->head_v)) return GDR_ERR_UNSUPPORTED;
+  if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
+  if (a->batch > 0) {
+    if (a->num_slots <= 0) return GDR_ERR_INVALID_ARG;
+    if (!a->batch_indices && a->batch > a->num_slots) return GDR_ERR_INVALID_ARG;
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->out)
+      return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->state) || !aligned16(a->out)) return GDR_ERR_INVALID_ARG;
+    if (int64_t{a->batch} * a->num_v_heads > kMaxRows) return GDR_ERR_UNSUPPORTED;
+  }
+  return GDR_OK;
+}
+
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *a) {
+  (void)a;  // the chunked prefill keeps every intermediate on chip
+  return 0;
+}
+
+int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
+  const int st = gdr_validate_prefill(a);
+  if (st != GDR_OK) return st;
+  if (a->num_seqs == 0) return GDR_OK;
+  gdr::PrefillParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.cu_seqlens = a->cu_seqlens;
+  p.state_indices = a->state_indices;
+  p.initial_state = a->initial_state;
+  p.final_state = a->final_state;
+  p.out = a->out;
+  p.seqlen = a->seqlen;
+  p.num_seqs = a->num_seqs;
+  p.Hk = a->num_qk_heads;
+  p.Hv = a->num_v_heads;
+  p.DV = a->head_v;
+  const int waves = gdr::prefill_waves(a->head_v, a->num_seqs, a->num_v_heads);
+  p.num_vtiles = a->head_v / (16 * waves);
+  p.group_size = p.num_vtiles * (a->num_v_heads / a->num_qk_heads);
+  p.num_groups = a->num_seqs * a->num_qk_heads;
+  p.l2norm = a->use_qk_l2norm;
+  p.out_bf16 = a->out_dtype == GDR_DTYPE_BF16;
+  p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
+  const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
+  const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
+  const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, waves,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
+  const int st = gdr_validate_decode(a);
+  if (st != GDR_OK) return st;
+  if (a->batch == 0) return GDR_OK;
+  gdr::DecodeParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.state = a->state;
+  p.batch_indices = a->batch_indices;
+  p.out = a->out;
+  p.batch = a->batch;
+  p.Hk = a->num_qk_heads;
+  p.Hv = a->num_v_heads;
+  p.l2norm = a->use_qk_l2norm;
+  p.out_bf16 = a->out_dtype == GDR_DTYPE_BF16;
+  p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
+  const hipError_t e = gdr::launch_decode(p, a->qkv_dtype == GDR_DTYPE_F32, a->head_k,
+                                          a->head_v, a->num_householder,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // extern "C"

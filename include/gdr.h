@@ -1,0 +1,178 @@
+/*
+ * gdr.h — C ABI of the MI355X (gfx950) gated delta rule library (libgdr.so).
+ *
+ * The library computes the gated delta rule
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale S_t q_t,
+ *
+ * the recurrence of Megatron Core's Gated DeltaNet (API page
+ * "core.ssm.gated_delta_net.gdn", function torch_chunk_gated_delta_rule) and,
+ * with several Householder sub-steps per token, of its Gated Delta Product
+ * mixer (API page "core.ssm.gated_delta_product", class GatedDeltaProductMixer).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers to row-major arrays whose innermost
+ *    dimension is contiguous; base addresses must be 16-byte aligned.
+ *  - The state S of one (sequence, value head) is stored as a [K, V] float32
+ *    matrix holding S transposed: element [i][j] is S[j][i].
+ *  - Value head h reads query/key head floor(h * Hk / Hv) (Hv a multiple of Hk).
+ *  - q/k/v share one input dtype; g, beta and all states are float32.
+ *  - Calls only enqueue work on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream).  They never allocate, free or synchronise, keep no
+ *    mutable global state, and their launch shapes depend only on the sizes in
+ *    the argument struct, so they can be captured in a HIP graph.
+ *  - Errors: arguments are checked on the host before anything is launched; on
+ *    any error nothing is enqueued and no buffer is touched.  Preconditions on
+ *    device-resident data (monotone cu_seqlens, 0 <= index < num_slots, unique
+ *    non-negative indices, |q|,|k| entries below 65504 for bf16 inputs without the
+ *    L2 norm) are documented, not checked: checking them would need a device
+ *    synchronisation.  Violating them gives undefined results.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1, /* NULL where a pointer is required, bad size, misaligned */
+  GDR_ERR_UNSUPPORTED = 2, /* valid but not implemented (head size, dtype, n_h, ...) */
+  GDR_ERR_WORKSPACE = 3,   /* workspace smaller than gdr_prefill_workspace_bytes()   */
+  GDR_ERR_HIP = 4          /* the HIP runtime reported a launch error                 */
+} gdr_status;
+
+/* Element types of q/k/v and of the output. */
+typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
+
+/*
+ * Chunked prefill over packed or batched sequences.  Mirrors
+ * torch_chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64,
+ * initial_state=None, output_final_state=False, use_qk_l2norm_in_kernel=False,
+ * cu_seqlens=None) -> (o, final_state) (page "core.ssm.gated_delta_net.gdn"),
+ * with the slot-indexed state of ssm_prefill (page "core.ssm.gated_delta_product":
+ * each request enters with whatever its cache slot holds and writes the slot back;
+ * padding requests carry slot -1).
+ *
+ * Shapes (Tt = batch * seqlen tokens; with cu_seqlens, batch must be 1):
+ *   q    [Tt, Hk, K]            k    [Tt, n_h, Hk, K]     v [Tt, n_h, Hv, V]
+ *   g    [Tt, Hv]   float32     beta [Tt, n_h, Hv] float32
+ *   out  [Tt, Hv, V]  (out_dtype)
+ *   cu_seqlens    int32 [num_seqs + 1] or NULL.  NULL: num_seqs = batch and
+ *                 sequence n is tokens [n*seqlen, (n+1)*seqlen).
+ *   state_indices int32 [num_seqs] or NULL.
+ *     NULL:  sequence n starts from initial_state[n] ([num_seqs, Hv, K, V]; NULL
+ *            means zeros) and, if final_state != NULL, ends in final_state[n].
+ *     given: initial_state and final_state are slot caches [num_slots, Hv, K, V]
+ *            (usually the same pointer).  Sequence n reads slot max(idx, 0)
+ *            (zeros if initial_state is NULL) and writes slot idx only when
+ *            idx >= 0; -1 marks padding.  Slots no sequence writes are left
+ *            byte-identical.
+ *   final_state may equal initial_state (in place).
+ *
+ * scale: NaN selects the default 1/sqrt(K).
+ * use_qk_l2norm: nonzero divides each q and k row by sqrt(sum x^2 + 1e-6).
+ * num_householder: n_h (1 = gated delta rule; 2 = gated delta product with two
+ *   Householder sub-steps per token; the decay exp(g_t) is applied once per
+ *   token, before the first sub-step, and o_t is read after the last one).
+ * chunk_size: tokens per chunk, a power of two in [16, 256].  Chunking does not
+ *   change the result beyond rounding; the kernels evaluate chunks of
+ *   min(chunk_size * n_h, 64) rows (at most 32 rows for float32 inputs).
+ * Supported: K in {64, 128}, V in {64, 128}, n_h in {1, 2}, q/k/v F32 or BF16,
+ *   out F32 or BF16.
+ */
+typedef struct {
+  int32_t batch;            /* B; 1 when cu_seqlens is given                        */
+  int32_t seqlen;           /* tokens per batch row (total tokens with cu_seqlens)  */
+  int32_t num_seqs;         /* N; must equal batch when cu_seqlens is NULL          */
+  int32_t num_qk_heads;     /* Hk                                                   */
+  int32_t num_v_heads;      /* Hv                                                   */
+  int32_t head_k;           /* K                                                    */
+  int32_t head_v;           /* V                                                    */
+  int32_t num_householder;  /* n_h                                                  */
+  int32_t chunk_size;       /* tokens                                               */
+  int32_t qkv_dtype;        /* gdr_dtype                                            */
+  int32_t out_dtype;        /* gdr_dtype                                            */
+  int32_t use_qk_l2norm;    /* 0 or 1                                               */
+  float scale;              /* NaN => 1/sqrt(head_k)                                */
+  int32_t num_slots;        /* slot count when state_indices != NULL                */
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *g;
+  const float *beta;
+  const int32_t *cu_seqlens;
+  const int32_t *state_indices;
+  const float *initial_state;
+  float *final_state;
+  void *out;
+  void *workspace;          /* device memory of workspace_bytes (may be NULL if 0)  */
+  size_t workspace_bytes;
+} gdr_prefill_args;
+
+/*
+ * Single-token decode over a slot-indexed float32 state cache, updated in place.
+ * Mirrors ssm_decode (pages "core.ssm.gated_delta_net.gdn" and
+ * "core.ssm.gated_delta_product") and the padding rule of PR "Add GDN dynamic
+ * inference #6499" (review thread): batch_indices[i] = -1 marks padding; its
+ * read is clamped to slot 0 and its write is skipped, so its output is the
+ * step computed from slot 0 (meaningless if slot 0 is written in the same call).
+ * batch_indices NULL means static batching: request i uses slot i.
+ *
+ * Shapes: q [n, Hk, K]; k [n, n_h, Hk, K]; v [n, n_h, Hv, V]; g [n, Hv] float32;
+ *   beta [n, n_h, Hv] float32; state [num_slots, Hv, K, V] float32;
+ *   batch_indices int32 [n] or NULL; out [n, Hv, V] (out_dtype).
+ * Supported: K = 128 or 64, V = 128 or 64, n_h in {1, 2}.
+ */
+typedef struct {
+  int32_t batch;            /* n requests                                           */
+  int32_t num_qk_heads;
+  int32_t num_v_heads;
+  int32_t head_k;
+  int32_t head_v;
+  int32_t num_householder;
+  int32_t num_slots;
+  int32_t qkv_dtype;
+  int32_t out_dtype;
+  int32_t use_qk_l2norm;
+  float scale;              /* NaN => 1/sqrt(head_k)                                */
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *g;
+  const float *beta;
+  float *state;
+  const int32_t *batch_indices;
+  void *out;
+} gdr_decode_args;
+
+/* Version of this ABI (GDR_ABI_VERSION). */
+int gdr_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *gdr_status_string(int status);
+
+/* Host-only argument checks (no HIP calls; usable without a GPU). */
+int gdr_validate_prefill(const gdr_prefill_args *args);
+int gdr_validate_decode(const gdr_decode_args *args);
+
+/* Device workspace the prefill needs, in bytes (a host-only function of the sizes). */
+size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *args);
+
+/* Enqueue a prefill / a decode step on `stream` (hipStream_t). */
+int gdr_chunk_gated_delta_rule(const gdr_prefill_args *args, void *stream);
+int gdr_ssm_decode(const gdr_decode_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H */

@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point, and
+its host-side argument checks behave as include/gdr.h documents (no GPU calls)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_71_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdr_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == sorted(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"libgdr.so does not export {name}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdr_abi_version() == 1
+    for code, name in [(0, "GDR_OK"), (1, "GDR_ERR_INVALID_ARG"), (2, "GDR_ERR_UNSUPPORTED"),
+                       (3, "GDR_ERR_WORKSPACE"), (4, "GDR_ERR_HIP"), (99, "GDR_ERR_UNKNOWN")]:
+        assert lib.gdr_status_string(code).decode() == name
+
+
+FAKE = 0x100000  # 16-byte aligned dummy device address; never dereferenced on the host
+
+
+def _prefill(**kw):
+    a = _lib.PrefillArgs()
+    base = dict(batch=2, seqlen=100, num_seqs=2, num_qk_heads=2, num_v_heads=4, head_k=128,
+                head_v=128, num_householder=1, chunk_size=64, qkv_dtype=1, out_dtype=1,
+                use_qk_l2norm=0, scale=math.nan, num_slots=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+                beta=FAKE, out=FAKE)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+def _decode(**kw):
+    a = _lib.DecodeArgs()
+    base = dict(batch=8, num_qk_heads=2, num_v_heads=4, head_k=128, head_v=128,
+                num_householder=1, num_slots=16, qkv_dtype=1, out_dtype=1, use_qk_l2norm=0,
+                scale=math.nan, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE,
+                out=FAKE)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(num_seqs=3), 1),                           # batched: N must equal B
+    (dict(cu_seqlens=FAKE, batch=2), 1),             # packed: B must be 1
+    (dict(cu_seqlens=FAKE, batch=1, num_seqs=7), 0),
+    (dict(num_v_heads=3), 1),                        # Hv multiple of Hk
+    (dict(num_qk_heads=0), 1),
+    (dict(head_k=96), 2), (dict(head_v=256), 2),
+    (dict(num_householder=3), 2), (dict(num_householder=0), 1),
+    (dict(chunk_size=48), 2), (dict(chunk_size=8), 2), (dict(chunk_size=512), 2),
+    (dict(chunk_size=0), 1),
+    (dict(qkv_dtype=5), 1), (dict(out_dtype=-1), 1),
+    (dict(use_qk_l2norm=2), 1),
+    (dict(scale=math.inf), 1), (dict(scale=0.5), 0),
+    (dict(q=None), 1), (dict(beta=None), 1), (dict(out=None), 1),
+    (dict(q=FAKE + 2), 1),                           # misaligned
+    (dict(state_indices=FAKE), 1),                   # slots need num_slots
+    (dict(state_indices=FAKE, num_slots=4), 0),
+    (dict(initial_state=FAKE + 4), 1),
+    (dict(seqlen=0, q=None, k=None, v=None, g=None, beta=None, out=None), 0),  # empty
+    (dict(batch=-1), 1),
+    (dict(seqlen=1 << 30, batch=2, num_seqs=2), 2),  # beyond the row limit
+])
+def test_validate_prefill(lib, kw, code):
+    a = _prefill(**kw)
+    assert lib.gdr_validate_prefill(ctypes.byref(a)) == code
+    assert lib.gdr_prefill_workspace_bytes(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(num_v_heads=6, num_qk_heads=4), 1),
+    (dict(head_k=32), 2),
+    (dict(num_householder=4), 2),
+    (dict(num_slots=0), 1),
+    (dict(batch=20), 1),                             # static batching needs batch <= slots
+    (dict(batch=20, batch_indices=FAKE), 0),
+    (dict(state=None), 1), (dict(state=FAKE + 8), 1),
+    (dict(batch=0, q=None, k=None, v=None, g=None, beta=None, state=None, out=None,
+          num_slots=0), 0),
+    (dict(scale=-math.inf), 1),
+])
+def test_validate_decode(lib, kw, code):
+    a = _decode(**kw)
+    assert lib.gdr_validate_decode(ctypes.byref(a)) == code
+
+
+def test_null_args_rejected(lib):
+    assert lib.gdr_validate_prefill(None) == 1
+    assert lib.gdr_validate_decode(None) == 1
+
+
+def test_invalid_call_launches_nothing(lib):
+    """An invalid call returns before any HIP call, so it works without a GPU."""
+    a = _prefill(head_k=96)
+    assert lib.gdr_chunk_gated_delta_rule(ctypes.byref(a), None) == 2
+    d = _decode(num_slots=0)
+    assert lib.gdr_ssm_decode(ctypes.byref(d), None) == 1
+
+
+def test_python_binding_raises_without_fallback(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "nope.so"))

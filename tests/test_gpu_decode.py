@@ -1,0 +1,165 @@
+"""GPU decode vs the fp64 oracle, through the C ABI (marked gpu)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_71_amd import workloads as W
+from parity import check, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_decode(wl, cache_f64, *, num_householder=1, use_qk_l2norm=False, scale=None):
+    import oracle
+    n = wl.q.shape[0]
+    return oracle.decode(W.as_f64(wl.q), W.as_f64(wl.k), W.as_f64(wl.v),
+                         np.asarray(wl.g, np.float64), np.asarray(wl.beta, np.float64),
+                         cache_f64, batch_indices=wl.batch_indices, scale=scale,
+                         use_qk_l2norm=use_qk_l2norm, num_householder=num_householder)
+
+
+def _run_gpu(wl, *, out_dtype=None, use_qk_l2norm=False, scale=None, indices=True):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    cache = to_dev(wl.cache)
+    idx = to_dev(wl.batch_indices) if (indices and wl.batch_indices is not None) else None
+    od = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    o = gdr.ssm_decode(to_dev(wl.q), to_dev(wl.k), to_dev(wl.v), to_dev(wl.g), to_dev(wl.beta),
+                       cache, batch_indices=idx, scale=scale,
+                       use_qk_l2norm_in_kernel=use_qk_l2norm, out_dtype=od)
+    torch.cuda.synchronize()
+    return o, cache
+
+
+def _check_decode(wl, o, cache_after, *, out_bf16, f32_inputs, **okw):
+    before = wl.cache
+    ref_cache = W.as_f64(before).copy()
+    ref_o = _oracle_decode(wl, ref_cache, **okw)
+    idx = wl.batch_indices if wl.batch_indices is not None else np.arange(wl.q.shape[0])
+    written = set(int(s) for s in idx if s >= 0)
+    real = idx >= 0
+    # padding rows read slot 0; their output is defined only when slot 0 is not written
+    comparable = real | (0 not in written)
+    o_host = to_host(o)
+    check(o_host[comparable], ref_o[comparable], f32_inputs=f32_inputs, out_bf16=out_bf16,
+          what="decode outputs")
+    assert np.all(np.isfinite(o_host)), "padding outputs must be finite"
+    after = cache_after.cpu().numpy()
+    ws = sorted(written)
+    check(after[ws].astype(np.float64), ref_cache[ws], f32_inputs=f32_inputs, out_bf16=False,
+          what="decode states")
+    untouched = np.setdiff1d(np.arange(before.shape[0]), ws)
+    assert np.array_equal(after[untouched].view(np.uint32), before[untouched].view(np.uint32)), \
+        "slots not named by batch_indices must stay byte-identical"
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_decode_config3_full(out_dtype):
+    """128 requests (16 padding) over a [256,32,128,128] fp32 cache."""
+    wl = W.config3()
+    o, cache = _run_gpu(wl, out_dtype=out_dtype)
+    _check_decode(wl, o, cache, out_bf16=out_dtype == "bf16", f32_inputs=False)
+
+
+def _small_decode(seed, *, n=24, slots=40, Hk=2, Hv=4, K=128, V=128, n_h=1, dtype=W.BF16,
+                  pad=5, unit=True, slot0_written=False):
+    rng = np.random.default_rng(seed)
+    kshape = (n, Hk, K) if n_h == 1 else (n, n_h, Hk, K)
+    vshape = (n, Hv, V) if n_h == 1 else (n, n_h, Hv, V)
+    bshape = (n, Hv) if n_h == 1 else (n, n_h, Hv)
+    x = rng.standard_normal((n, Hk, K), dtype=np.float32)
+    kx = rng.standard_normal(kshape, dtype=np.float32)
+    if unit:
+        x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        kx /= np.linalg.norm(kx, axis=-1, keepdims=True)
+    else:
+        x *= rng.uniform(0.5, 3.0, x.shape[:-1] + (1,)).astype(np.float32)
+        kx *= rng.uniform(0.5, 3.0, kx.shape[:-1] + (1,)).astype(np.float32)
+    v = rng.standard_normal(vshape, dtype=np.float32)
+    g = (-rng.uniform(0, 2, (n, Hv))).astype(np.float32)
+    beta = rng.uniform(0, 1, bshape).astype(np.float32)
+    cache = (0.1 * rng.standard_normal((slots, Hv, K, V))).astype(np.float32)
+    if slot0_written:
+        idx = np.concatenate([[0], 1 + rng.permutation(slots - 1)[:n - 1]]).astype(np.int32)
+        idx = idx[rng.permutation(n)]
+    else:
+        idx = (1 + rng.permutation(slots - 1)[:n]).astype(np.int32)
+    pad_rows = rng.permutation(np.nonzero(idx != 0)[0])[:pad]
+    idx[pad_rows] = -1
+    return W.DecodeWorkload("small", dtype, W.store(x, dtype), W.store(kx, dtype),
+                            W.store(v, dtype), g, beta, cache, idx)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype=W.BF16), dict(dtype=W.F32), dict(dtype=W.BF16, n_h=2), dict(dtype=W.F32, n_h=2),
+    dict(dtype=W.BF16, K=64, V=64), dict(dtype=W.F32, K=128, V=64), dict(dtype=W.F32, K=64, V=128),
+    dict(dtype=W.BF16, Hk=4, Hv=4), dict(dtype=W.BF16, slot0_written=True),
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_decode_variants(case):
+    n_h = case.get("n_h", 1)
+    wl = _small_decode(11, **case)
+    f32 = wl.dtype == W.F32
+    o, cache = _run_gpu(wl, out_dtype="f32" if f32 else "bf16")
+    _check_decode(wl, o, cache, out_bf16=not f32, f32_inputs=f32, num_householder=n_h)
+
+
+def test_decode_l2norm_and_scale():
+    wl = _small_decode(12, unit=False, dtype=W.F32)
+    o, cache = _run_gpu(wl, out_dtype="f32", use_qk_l2norm=True, scale=0.37)
+    _check_decode(wl, o, cache, out_bf16=False, f32_inputs=True, use_qk_l2norm=True, scale=0.37)
+
+
+def test_decode_static_batching():
+    """batch_indices=None: request i reads and writes slot i."""
+    wl = _small_decode(13, n=16, slots=16, pad=0)
+    wl.batch_indices = None
+    o, cache = _run_gpu(wl, out_dtype="f32", indices=False)
+    _check_decode(wl, o, cache, out_bf16=False, f32_inputs=False)
+
+
+def test_decode_empty_batch():
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    cache = torch.zeros((4, 2, 128, 128), device="cuda")
+    e = torch.empty((0, 2, 128), device="cuda", dtype=torch.bfloat16)
+    o = gdr.ssm_decode(e, e, e, torch.empty((0, 2), device="cuda"),
+                       torch.empty((0, 2), device="cuda"), cache,
+                       batch_indices=torch.empty(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and float(cache.abs().sum()) == 0.0
+
+
+def test_decode_graph_replay():
+    """Captured in a HIP graph and replayed: every replay equals the eager call."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    wl = _small_decode(14)
+    args = [to_dev(x) for x in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+    idx = to_dev(wl.batch_indices)
+    cache0 = to_dev(wl.cache)
+    # eager reference: three consecutive steps
+    eager_c = cache0.clone()
+    eager = []
+    for _ in range(3):
+        eager.append(gdr.ssm_decode(*args, eager_c, batch_indices=idx).clone())
+        eager.append(eager_c.clone())
+    torch.cuda.synchronize()
+    graph_c = cache0.clone()
+    out = torch.empty((wl.q.shape[0], wl.v.shape[1], wl.v.shape[2]), dtype=torch.bfloat16,
+                      device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gdr.ssm_decode(*args, graph_c.clone(), batch_indices=idx, out=out)   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdr.ssm_decode(*args, graph_c, batch_indices=idx, out=out)
+    torch.cuda.synchronize()
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[2 * step]), f"replay {step}: outputs differ from eager"
+        assert torch.equal(graph_c, eager[2 * step + 1]), f"replay {step}: states differ"
+        _ = torch.ones(1, device="cuda").sum().item()   # eager work between replays

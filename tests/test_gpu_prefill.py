@@ -1,0 +1,260 @@
+"""GPU chunked prefill vs the fp64 oracle, through the C ABI (marked gpu).
+
+Small cases compare every output and state; the measured workloads run at their
+full size in the launch configuration the benchmark times and are compared on
+sampled (sequence, head) pairs that the oracle computes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_71_amd import workloads as W
+from parity import check, gpu_prefill, oracle_prefill_batch, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _spans(wl):
+    B, T = wl.q.shape[:2]
+    if wl.cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    return [(0, int(wl.cu_seqlens[i]), int(wl.cu_seqlens[i + 1])) for i in range(wl.num_seqs)]
+
+
+def _all_pairs(wl):
+    Hv = wl.v.shape[-2]
+    return [(n, h) for n in range(wl.num_seqs) for h in range(Hv)]
+
+
+def _compare(wl, o, states, pairs, *, out_bf16, use_qk_l2norm=False, scale=None, what=""):
+    ref = oracle_prefill_batch(wl, pairs, use_qk_l2norm=use_qk_l2norm, scale=scale)
+    spans = _spans(wl)
+    oh = to_host(o)
+    sh = states.cpu().numpy().astype(np.float64)
+    ox, orf, sx, srf = [], [], [], []
+    for (n, h) in pairs:
+        b, t0, t1 = spans[n]
+        ox.append(oh[b, t0:t1, h])
+        orf.append(ref[(n, h)][0])
+        slot = n if wl.state_indices is None else int(wl.state_indices[n])
+        if slot >= 0:
+            sx.append(sh[slot, h])
+            srf.append(ref[(n, h)][1])
+    f32 = wl.dtype == W.F32
+    e_o = check(np.concatenate(ox), np.concatenate(orf), f32_inputs=f32, out_bf16=out_bf16,
+                what=f"{what} outputs")
+    e_s = check(np.stack(sx), np.stack(srf), f32_inputs=f32, out_bf16=False,
+                what=f"{what} states")
+    print(f"{what}: output err {e_o:.3e}, state err {e_s:.3e}")
+    return e_o, e_s
+
+
+@pytest.mark.parametrize("decay", ["config", "slow", "zero"])
+def test_prefill_fp32_B1_T256_H2_D64(decay):
+    """float32 inputs and outputs, chunk 64, zero initial state (all pairs)."""
+    wl = W.config0(decay=decay)
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what=f"fp32 {decay}")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("decay", ["config", "slow", "zero"])
+def test_prefill_bf16_small(decay, out_dtype):
+    """bf16, B=2, T=333 (ragged last chunk), 16 heads, K=V=128, random initial state."""
+    wl = W.config1(decay=decay, T=333, B=2)
+    o, st, _ = gpu_prefill(wl, out_dtype=out_dtype)
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=out_dtype == "bf16", what=f"bf16 {decay}")
+
+
+@pytest.mark.parametrize("chunk_size", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_prefill_chunk_sizes(chunk_size, dtype):
+    """Any chunk size gives the per-token recurrence (slow decay keeps state alive)."""
+    wl = W.prefill_dense("cs", 21, 2, 200, 2, 4, 128, 128, dtype, chunk_size, decay="slow",
+                         initial_state="random")
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what=f"chunk {chunk_size} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 64), (64, 128)])
+def test_prefill_head_dims(dtype, dims):
+    K, V = dims
+    wl = W.prefill_dense("dims", 22, 2, 150, 2, 2, K, V, dtype, 64, decay="slow",
+                         initial_state="random")
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what=f"K{K} V{V} {dtype}")
+
+
+@pytest.mark.parametrize("decay", ["config", "slow"])
+def test_prefill_varlen_slots(decay):
+    """Packed sequences with ragged, tiny and empty lengths; slot cache with padding.
+
+    Sequence 3 is padding with tokens (reads slot 0, writes nothing) and sequence
+    5 zero-length padding; slots no sequence writes stay byte-identical.
+    """
+    lengths = [1, 63, 64, 65, 130, 0, 200, 17]
+    wl = W.prefill_packed("varlen", 23, lengths, 2, 4, 128, 128, W.BF16, 64, decay=decay,
+                          num_slots=12, slot_init="random")
+    wl.state_indices = wl.state_indices.copy()
+    wl.state_indices[3] = -1
+    wl.state_indices[5] = -1
+    before = wl.initial_state.copy()
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what=f"varlen {decay}")
+    written = [int(s) for s in wl.state_indices if s >= 0]
+    untouched = np.setdiff1d(np.arange(wl.initial_state.shape[0]), written)
+    after = st.cpu().numpy()
+    assert np.array_equal(after[untouched].view(np.uint32), before[untouched].view(np.uint32))
+
+
+@pytest.mark.parametrize("decay", ["config", "slow"])
+def test_prefill_product_two_householder(decay):
+    """Gated delta product, n_h = 2, chunk 128 tokens (evaluated as 64-row chunks)."""
+    wl = W.config4(decay=decay, T=300, H=4)
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what=f"gdp {decay}")
+
+
+def test_prefill_product_fp32():
+    wl = W.prefill_dense("gdp32", 24, 1, 150, 2, 2, 64, 64, W.F32, 32, decay="slow",
+                         initial_state="random", num_householder=2)
+    o, st, _ = gpu_prefill(wl, out_dtype="f32")
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, what="gdp fp32")
+
+
+def test_prefill_l2norm_and_scale():
+    """use_qk_l2norm_in_kernel on un-normalised q/k, non-default scale."""
+    wl = W.prefill_dense("l2", 25, 1, 160, 2, 2, 128, 128, W.F32, 64, decay="slow",
+                         initial_state="random")
+    rng = np.random.default_rng(5)
+    wl.q = (wl.q * rng.uniform(0.5, 3, wl.q.shape[:-1] + (1,))).astype(np.float32)
+    wl.k = (wl.k * rng.uniform(0.5, 3, wl.k.shape[:-1] + (1,))).astype(np.float32)
+    o, st, _ = gpu_prefill(wl, out_dtype="f32", use_qk_l2norm=True, scale=0.2)
+    _compare(wl, o, st, _all_pairs(wl), out_bf16=False, use_qk_l2norm=True, scale=0.2,
+             what="l2norm")
+
+
+def test_prefill_deterministic_and_packing_invariant():
+    """Bitwise: two runs agree; packed sequences equal the same sequences run alone."""
+    import torch
+    lengths = [70, 5, 129]
+    wl = W.prefill_packed("det", 26, lengths, 2, 4, 128, 128, W.BF16, 64, decay="slow",
+                          num_slots=6, slot_init="random")
+    o1, s1, _ = gpu_prefill(wl)
+    o2, s2, _ = gpu_prefill(wl)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2), "prefill is not deterministic"
+    cu = wl.cu_seqlens
+    for n in range(len(lengths)):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        one = W.PrefillWorkload("one", wl.dtype, wl.q[:, t0:t1], wl.k[:, t0:t1], wl.v[:, t0:t1],
+                                wl.g[:, t0:t1], wl.beta[:, t0:t1], 64,
+                                initial_state=wl.initial_state[[wl.state_indices[n]]])
+        oo, so, _ = gpu_prefill(one)
+        assert torch.equal(oo[0], o1[0, t0:t1]), f"sequence {n}: packed output differs"
+        assert torch.equal(so[0], s1[int(wl.state_indices[n])]), f"sequence {n}: state differs"
+
+
+def test_prefill_split_at_chunk_boundary_bitwise():
+    """Prefill of L tokens then of the rest equals one prefill when L is a multiple of 64."""
+    import torch
+    wl = W.prefill_dense("split", 27, 1, 320, 2, 2, 128, 128, W.BF16, 64, decay="slow",
+                         initial_state="random")
+    o, s, _ = gpu_prefill(wl)
+    L = 192
+    a = W.PrefillWorkload("a", wl.dtype, wl.q[:, :L], wl.k[:, :L], wl.v[:, :L], wl.g[:, :L],
+                          wl.beta[:, :L], 64, initial_state=wl.initial_state)
+    oa, sa, _ = gpu_prefill(a)
+    b = W.PrefillWorkload("b", wl.dtype, wl.q[:, L:], wl.k[:, L:], wl.v[:, L:], wl.g[:, L:],
+                          wl.beta[:, L:], 64, initial_state=sa.cpu().numpy())
+    ob, sb, _ = gpu_prefill(b)
+    assert torch.equal(torch.cat([oa, ob], dim=1), o)
+    assert torch.equal(sb, s)
+
+
+def test_prefill_empty_and_zero_length():
+    """No tokens: states pass through unchanged (dense) and padding touches nothing."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")  # noqa: E731
+    h0 = torch.randn((3, 2, 128, 128), device="cuda")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    o, fs = gdr.chunk_gated_delta_rule(z(1, 0, 2, 128), z(1, 0, 2, 128), z(1, 0, 2, 128),
+                                       z(1, 0, 2, dt=torch.float32),
+                                       z(1, 0, 2, dt=torch.float32), initial_state=h0,
+                                       output_final_state=True, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 128) and torch.equal(fs, h0)
+
+
+def test_prefill_graph_replay():
+    """The prefill captured in a HIP graph replays to the eager result every time."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    wl = W.prefill_packed("graph", 28, [100, 37, 64], 2, 4, 128, 128, W.BF16, 64,
+                          decay="slow", num_slots=6, slot_init="random")
+    dev = [to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")]
+    cu, idx = to_dev(wl.cu_seqlens), to_dev(wl.state_indices)
+    cache0 = to_dev(wl.initial_state)
+    eager_c = cache0.clone()
+    eager = []
+    for _ in range(3):
+        o, _ = gdr.chunk_gated_delta_rule(*dev, initial_state=eager_c, cu_seqlens=cu,
+                                          state_indices=idx)
+        eager.append((o.clone(), eager_c.clone()))
+    torch.cuda.synchronize()
+    graph_c = cache0.clone()
+    out = torch.empty_like(eager[0][0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gdr.chunk_gated_delta_rule(*dev, initial_state=graph_c.clone(), cu_seqlens=cu,
+                                   state_indices=idx, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdr.chunk_gated_delta_rule(*dev, initial_state=graph_c, cu_seqlens=cu,
+                                   state_indices=idx, out=out)
+    torch.cuda.synchronize()
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[step][0]), f"replay {step}: outputs differ"
+        assert torch.equal(graph_c, eager[step][1]), f"replay {step}: states differ"
+        _ = torch.ones(1, device="cuda").sum().item()
+
+
+# ---- measured workloads at full size, sampled pairs -------------------------------------
+
+def _sample_pairs(wl, per_seq, seed):
+    rng = np.random.default_rng(seed)
+    Hv = wl.v.shape[-2]
+    pairs = []
+    for n in range(wl.num_seqs):
+        for h in rng.permutation(Hv)[:per_seq]:
+            pairs.append((n, int(h)))
+    return pairs
+
+
+def test_prefill_full_B4_T4096_H16():
+    wl = W.config1()
+    o, st, _ = gpu_prefill(wl)
+    _compare(wl, o, st, _sample_pairs(wl, 2, 1), out_bf16=True, what="B4 T4096 H16")
+
+
+def test_prefill_full_varlen_Hk16_Hv32():
+    wl = W.config2()
+    before = wl.initial_state.copy()
+    o, st, _ = gpu_prefill(wl)
+    _compare(wl, o, st, _sample_pairs(wl, 2, 2), out_bf16=True, what="varlen 8 seqs")
+    written = [int(s) for s in wl.state_indices]
+    untouched = np.setdiff1d(np.arange(before.shape[0]), written)
+    after = st.cpu().numpy()
+    assert np.array_equal(after[untouched].view(np.uint32), before[untouched].view(np.uint32))
+
+
+def test_prefill_full_product_T65536_H32():
+    wl = W.config4()
+    o, st, _ = gpu_prefill(wl)
+    _compare(wl, o, st, [(0, 3), (0, 17)], out_bf16=True, what="gdp T65536 H32")
