@@ -9,7 +9,7 @@ Three legs, each timed over exactly K steps bracketed by torch.cuda.synchronize(
            the headline `value`.
   decode:  one token for each of 128 requests (16 padding) over a
            [256, 32, 128, 128] fp32 slot cache; reported as state GB/s.  The
-           256 MB last-level cache is flushed (1 GiB write) before every launch,
+           256 MB last-level cache is flushed (1 GiB read) before every launch,
            outside the timed launch.
   gdp:     gated delta product, 2 Householder sub-steps, B=1, T=65536, H=32,
            K = V = 128, bf16, chunk 128 tokens; tokens/s.
@@ -253,9 +253,9 @@ def profile_run():
     wl3 = W.config3()
     d = [up(x) for x in (wl3.q, wl3.k, wl3.v, wl3.g, wl3.beta)]
     cache, idx = up(wl3.cache), up(wl3.batch_indices)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     for _ in range(3):
-        flush.zero_()
+        flush.sum()
         gdr.ssm_decode(*d, cache, batch_indices=idx)
     src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -313,7 +313,9 @@ def main():
         idx = up(wl3.batch_indices)
         out = torch.empty((wl3.q.shape[0], wl3.v.shape[1], wl3.v.shape[2]),
                           dtype=torch.bfloat16, device="cuda")
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        # 1 GiB read before each launch evicts the 256 MB last-level cache without
+        # leaving dirty lines to be written back during the timed launch
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         gdr.ssm_decode(*d, cache, batch_indices=idx, out=out)
         dargs = gdr.decode_args(*d, cache, batch_indices=idx, out=out)
         lib = gdr.library()
@@ -324,7 +326,7 @@ def main():
             assert rc == 0, rc
 
         wall, kern = time_launches(launch_dec, args.steps, args.warmup,
-                                   before=lambda: flush.zero_())
+                                   before=lambda: flush.sum())
         n_real = int((wl3.batch_indices >= 0).sum())
         Hv, K, V = wl3.cache.shape[1:]
         state_bytes = 2 * n_real * Hv * K * V * 4

@@ -72,7 +72,7 @@ struct PrefillTraits {
   static constexpr int PAD = F32 ? 4 : 8;            // elements of row padding
   static constexpr int LDK = DK + PAD;               // K, Q leading dimension
   static constexpr int LDC = 32 + PAD;               // T, A10, P, KT leading dimension
-  static constexpr int LDA = 17;                     // AT (fp32 16x16 scratch) leading dim.
+  static constexpr int LDA = 20;                     // AT (fp32 16x16, column-major) leading dim.
   static constexpr int NT = 64 * NW;                 // threads
   static constexpr int KS = DK / 32;                 // 32-deep slices over keys
   static constexpr int KM = DK / 16;                 // 16-row blocks of H
@@ -111,7 +111,7 @@ template <class Tr>
 struct PrefillSmem {
   StageBuf<Tr> st[3];
   SolveBuf<Tr> sv[2];
-  float AT[2][16 * Tr::LDA];   // per diagonal block: A_bb, read by its inverting wave
+  float AT[2][16 * Tr::LDA];   // per diagonal block: A_bb column-major, for its inverting wave
 };
 
 // Inputs of one chunk held in registers between their fetch and their staging.
@@ -155,23 +155,35 @@ __device__ __forceinline__ void solve_chunk(const StageBuf<Tr> &s, SolveBuf<Tr> 
     const int bk = wave;
     float a[4];
     a_tile(bk, bk, a);
+    // column-major: column c of A_bb is 16 contiguous floats (one 16-byte store
+    // per lane here, four 16-byte loads per column below)
     float *Ab = AT[bk];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ab[(4 * g4 + i) * LDA + l16] = a[i];
+    *reinterpret_cast<float4 *>(Ab + l16 * LDA + 4 * g4) = make_float4(a[0], a[1], a[2], a[3]);
     // column substitution: lanes 0..15 keep column j of (I + A_bb)^-1 in registers;
-    // step i eliminates entry i from the rows below it
+    // step i eliminates entry i from the rows below it, with column i+1 already
+    // being loaded while step i computes
     if (lane < 16) {
       const int j = lane;
       float t[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.0f : 0.0f;
+      float4 cur[4], nxt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const float4 *>(Ab + 4 * q);
 #pragma unroll
       for (int i = 0; i < 15; ++i) {
-        float col[16];
+        if (i + 1 < 15) {
 #pragma unroll
-        for (int r = i + 1; r < 16; ++r) col[r] = Ab[r * LDA + i];
+          for (int q = 0; q < 4; ++q)
+            nxt[q] = *reinterpret_cast<const float4 *>(Ab + (i + 1) * LDA + 4 * q);
+        }
+        const float col[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
+                               cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                               cur[3].x, cur[3].y, cur[3].z, cur[3].w};
 #pragma unroll
         for (int r = i + 1; r < 16; ++r) t[r] -= col[r] * t[i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) v.T[(16 * bk + r) * LDC + 16 * bk + j] = M::cvt(t[r]);
@@ -246,7 +258,7 @@ prefill_kernel(const PrefillParams p) {
   if (w_item < 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -280,7 +292,7 @@ prefill_kernel(const PrefillParams p) {
   const TIn *__restrict__ vrow = static_cast<const TIn *>(p.v) + h * p.DV + vt * DVT;
   const float *__restrict__ gb = p.g + h;
   const float *__restrict__ bb = p.beta + h;
-  TOut *__restrict__ ob = static_cast<TOut *>(p.out) + h * p.DV + col0 + l16;
+  TOut *__restrict__ ob = static_cast<TOut *>(p.out) + h * p.DV + col0;   // + row, lane
   const uint32_t kstride = p.Hk * DK;        // elements between key rows (and query rows)
   const uint32_t vstride = p.Hv * p.DV;      // elements between value / output rows
   const size_t state_stride = static_cast<size_t>(DK) * p.DV;
@@ -351,7 +363,7 @@ prefill_kernel(const PrefillParams p) {
         const int idx = tid + j * NT, r = idx / SEG, sg = idx % SEG;
         float x[8];
         src[j].get(x);
-        if (r >= nvalid) {
+        if (nvalid < nrows && r >= nvalid) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = 0.0f;
         }
@@ -374,7 +386,7 @@ prefill_kernel(const PrefillParams p) {
     for (int j = 0; j < Tr::VPT; ++j) {
       const int idx = tid + j * NT, r = idx / Tr::VSEG, sg = idx % Tr::VSEG;
       Seg8<TIn> x = cr.v[j];
-      if (r >= nrow) x.zero();
+      if (nrow < CR && r >= nrow) x.zero();
       if (r < CR) x.store(s.V + r * Tr::LDV + sg * 8);
     }
     if (wave == 0) {
@@ -419,6 +431,7 @@ prefill_kernel(const PrefillParams p) {
   for (int ci = 0; ci < nchunks; ++ci) {
     const int c0 = row_begin + ci * CR;
     const int tq0 = c0 / NH;
+    const bool full = tq0 + CQ <= t1;   // every query row of the chunk is in the sequence
     const StageBuf<Tr> &s = sm.st[ci % 3];
     const SolveBuf<Tr> &v = sm.sv[ci & 1];
 
@@ -472,14 +485,14 @@ prefill_kernel(const PrefillParams p) {
           const int q = 16 * mq + 4 * g4 + i;
           o[i] = p.scale * (s.eG[NH * q + NH - 1] * xq[i] + pd[i]);
         }
-        TOut *dst = ob + static_cast<uint32_t>(tb) * vstride;
-        if (tb + 3 < t1) {
+        const uint32_t off = static_cast<uint32_t>(tb) * vstride + l16;
+        if (full) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i * vstride] = static_cast<TOut>(o[i]);
+          for (int i = 0; i < 4; ++i) ob[off + i * vstride] = static_cast<TOut>(o[i]);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (tb + i < t1) dst[i * vstride] = static_cast<TOut>(o[i]);
+            if (tb + i < t1) ob[off + i * vstride] = static_cast<TOut>(o[i]);
         }
       }
 
