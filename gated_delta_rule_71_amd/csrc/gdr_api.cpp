@@ -115,8 +115,8 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.Hk = a->num_qk_heads;
   p.Hv = a->num_v_heads;
   p.DV = a->head_v;
-  const int waves = gdr::prefill_waves(a->head_v, a->num_seqs, a->num_v_heads);
-  p.num_vtiles = a->head_v / (16 * waves);
+  const int state_waves = gdr::prefill_state_waves(a->head_v, a->num_seqs, a->num_v_heads);
+  p.num_vtiles = a->head_v / (32 * state_waves);
   p.group_size = p.num_vtiles * (a->num_v_heads / a->num_qk_heads);
   p.num_groups = a->num_seqs * a->num_qk_heads;
   p.l2norm = a->use_qk_l2norm;
@@ -124,7 +124,7 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
   const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
   const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
-  const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, waves,
+  const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, state_waves,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

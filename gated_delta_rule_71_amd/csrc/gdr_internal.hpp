@@ -49,11 +49,11 @@ struct DecodeParams {
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k);
-// Waves (16 value columns each) per prefill workgroup.
-int prefill_waves(int head_v, int num_seqs, int num_v_heads);
+// State waves (32 value columns each) per prefill workgroup.
+int prefill_state_waves(int head_v, int num_seqs, int num_v_heads);
 
 hipError_t launch_prefill(const PrefillParams &p, int qkv_f32, int head_k, int rows, int nh,
-                          int waves, hipStream_t stream);
+                          int state_waves, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int qkv_f32, int dk, int dv, int nh,
                          hipStream_t stream);
 
