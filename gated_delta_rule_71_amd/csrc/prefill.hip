@@ -43,6 +43,8 @@
 // exactly; T, P, H and D are rounded to fp16, 11 significant bits) and fp32
 // accumulation; fp32 inputs run every product with fp32 operands.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "gdr_internal.hpp"
 
@@ -141,7 +143,7 @@ struct PrefillTraits {
   static constexpr int NP = 4;                       // producer waves
   static constexpr int NW = NS + NP;                 // waves per workgroup
   static constexpr int NT = 64 * NW;                 // threads
-  static constexpr int PT = 64 * NP;                 // producer threads
+  static constexpr int ST = 64 * NP;                 // staging threads (all producer waves)
   static constexpr int CQ = CR / NH;                 // query rows per chunk
   static constexpr int NB = CR / 16;                 // 16-row blocks
   static constexpr int NQB = CQ / 16;                // 16-row query blocks
@@ -149,16 +151,17 @@ struct PrefillTraits {
   static constexpr int PAD = F32 ? 4 : 8;            // elements of row padding
   static constexpr int LDK = DK + PAD;               // K, Q leading dimension
   static constexpr int LDC = 32 + PAD;               // T, A10, P, KT leading dimension
-  static constexpr int LDA = 20;                     // AT (fp32 16x16, column-major) leading dim.
+  static constexpr int LDA = 20;                     // AR (fp32 16x16 blocks) leading dim.
   static constexpr int LDVT = CR + 4;                // VT (value column major) leading dim.
   static constexpr int KS = DK / 32;                 // 32-deep slices over keys
   static constexpr int KM = DK / 16;                 // 16-row blocks of H
   static constexpr int SEG = DK / 8;                 // 8-element segments per row
-  static constexpr int KPT = (CR * SEG + PT - 1) / PT;
-  static constexpr int QPT = (CQ * SEG + PT - 1) / PT;
+  static constexpr int KUNITS = (CR / 2) * SEG;      // (row pair, segment) units of K
+  static constexpr int KPT = (KUNITS + ST - 1) / ST;
+  static constexpr int QPT = (CQ * SEG + ST - 1) / ST;
   static constexpr int VSEG = DVT / 8;               // 8-element segments per V row
   static constexpr int VUNITS = (CR / 2) * VSEG;     // (row pair, segment) units of V
-  static constexpr int VPT = (VUNITS + PT - 1) / PT;
+  static constexpr int VPT = (VUNITS + ST - 1) / ST;
   static_assert(CR == 16 || CR == 32, "chunk rows");
   static_assert(CQ % 16 == 0, "query rows");
   static_assert(DK % 32 == 0, "head_k");
@@ -170,6 +173,7 @@ template <class Tr>
 struct alignas(16) StageBuf {
   typename Tr::elem K[Tr::CR * Tr::LDK];
   typename Tr::elem Q[Tr::CQ * Tr::LDK];
+  typename Tr::elem KT[Tr::DK * Tr::LDC];   // K^T (keys by rows)
   typename Tr::TIn VT[Tr::DVT * Tr::LDVT];   // the workgroup's value columns, transposed
   double G[Tr::CR];     // cumulative decay (fp64: differences of large sums stay exact)
   float eG[Tr::CR];     // exp(G_r)
@@ -182,13 +186,12 @@ struct alignas(16) SolveBuf {
   typename Tr::elem T[Tr::CR * Tr::LDC];    // diag(T_00, T_11), T_bb = (I + A_bb)^-1
   typename Tr::elem A10[16 * Tr::LDC];      // A_10 in columns 0..15 (32-row chunks)
   typename Tr::elem P[Tr::CQ * Tr::LDC];    // Q K^T * Gamma, causal
-  typename Tr::elem KT[Tr::DK * Tr::LDC];   // (diag(exp(G_last - G)) K)^T
 };
 template <class Tr>
 struct PrefillSmem {
   StageBuf<Tr> st[3];
   SolveBuf<Tr> sv[2];
-  float AT[2][16 * Tr::LDA];   // per diagonal block: A_bb column-major, for its inverting wave
+  float AR[2][16 * Tr::LDA];   // the diagonal blocks A_bb (fp32, row-major) for the inversion
 };
 
 // Inputs of one chunk held in a producer thread's registers between their fetch
@@ -197,121 +200,213 @@ struct PrefillSmem {
 // instruction waits on a load before the data is needed.
 template <class Tr>
 struct ChunkRegs {
-  Seg8<typename Tr::TIn> k[Tr::KPT], q[Tr::QPT], v[Tr::VPT][2];
+  Seg8<typename Tr::TIn> k[Tr::KPT][2], q[Tr::QPT], v[Tr::VPT][2];
   float g, b;   // producer wave 0: decay and write strength of row `lane`
   int c;        // first row of the chunk these registers hold
 };
 
-// ---- solve one chunk: T_bb, A_10, P and K~^T (producer waves) ------------------
-// producer wave b < NB: A_bb and its inverse; the other producer waves: A_10 and
-// the P tiles round-robin, then the decayed, transposed keys.
+// ---- solve one chunk (producer waves) ---------------------------------------------
+// Each task issues all of its LDS reads first, then its matrix-core products, then
+// its epilogue and stores, so that no read has to wait behind a store.
+//   producer wave 0: the diagonal blocks A_bb and their inverses T_bb;
+//   producer waves 1 and 2: A_10 and the P tiles on or below the causal boundary.
+// Every producer wave also stages and fetches; wave 3 runs the decay scan.
+
+// Tile j of the off-diagonal work: A_10 first (32-row chunks), then the nonzero P
+// tiles.  Encoded as 4*row_block + col_block, plus 16 for P tiles; -1 past the end.
+template <class Tr>
+__device__ __forceinline__ constexpr int tile_job(int j) {
+  if (Tr::NB == 2) {
+    if (j == 0) return 4;
+    --j;
+  }
+  for (int mq = 0; mq < Tr::NQB; ++mq)
+    for (int ni = 0; ni < Tr::NB; ++ni)
+      if (16 * ni <= Tr::NH * (16 * mq + 15) + Tr::NH - 1) {
+        if (j == 0) return 16 + 4 * mq + ni;
+        --j;
+      }
+  return -1;
+}
+template <class Tr>
+__device__ __forceinline__ constexpr int tile_job_count() {
+  int n = 0;
+  while (tile_job<Tr>(n) >= 0) ++n;
+  return n;
+}
+
+// four consecutive operand elements in LDS (8 bytes for fp16, 16 for fp32)
+__device__ __forceinline__ void store4e(_Float16 *p, const float (&x)[4]) {
+  f16x4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(x[i]);
+  *reinterpret_cast<f16x4 *>(p) = h;
+}
+__device__ __forceinline__ void store4e(float *p, const float (&x)[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// Off-diagonal tiles J0 .. J1-1: A_10 = strict_lower(diag(beta) K_1 K_0^T * Gamma) and
+// P tiles = (Q K^T * Gamma) on or below the causal boundary.  Each is formed
+// transposed (K_ni X^T), so that a lane holds four consecutive columns of one row
+// and writes them with one store.
+template <class Tr, int J0, int J1>
+__device__ __forceinline__ void run_tiles(const StageBuf<Tr> &s, SolveBuf<Tr> &v, int lane) {
+  constexpr int N = J1 - J0;
+  if constexpr (N > 0) {
+    using M = typename Tr::M;
+    using frag = typename M::frag;
+    constexpr int KS = Tr::KS, LDK = Tr::LDK, LDC = Tr::LDC, NH = Tr::NH;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    frag fk[N][KS], fx[N][KS];
+    double gr[N], gc[N][4];
+    float br[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int code = tile_job<Tr>(J0 + j);
+      const bool is_p = code >= 16;
+      const int mi = (code & 15) >> 2, ni = code & 3;
+      const typename Tr::elem *xrows = is_p ? s.Q : s.K;
+#pragma unroll
+      for (int sl = 0; sl < KS; ++sl) {
+        fk[j][sl] = M::load(s.K, LDK, 16 * ni + l16, 32 * sl, lane);
+        fx[j][sl] = M::load(xrows, LDK, 16 * mi + l16, 32 * sl, lane);
+      }
+      const int q = 16 * mi + l16;               // row of A_10 / P held by this lane
+      const int r = is_p ? NH * q + NH - 1 : q;  // its key row
+      gr[j] = s.G[r];
+      br[j] = is_p ? 1.0f : s.B[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gc[j][i] = s.G[16 * ni + 4 * g4 + i];
+    }
+    f32x4 acc[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      acc[j] = zero4();
+#pragma unroll
+      for (int sl = 0; sl < KS; ++sl) acc[j] = M::mma(fk[j][sl], fx[j][sl], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int code = tile_job<Tr>(J0 + j);
+      const bool is_p = code >= 16;
+      const int mi = (code & 15) >> 2, ni = code & 3;
+      const int q = 16 * mi + l16;
+      const int r = is_p ? NH * q + NH - 1 : q;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * ni + 4 * g4 + i;
+        // mask before the exponential: G_r - G_c may be large positive above
+        const bool keep = is_p ? c <= r : c < r;
+        const float d = keep ? static_cast<float>(gr[j] - gc[j][i]) : 0.0f;
+        x[i] = keep ? br[j] * acc[j][i] * fexp(d) : 0.0f;
+      }
+      if (is_p)
+        store4e(v.P + q * LDC + 16 * ni + 4 * g4, x);
+      else
+        store4e(v.A10 + l16 * LDC + 4 * g4, x);
+    }
+  }
+}
+
+// The diagonal blocks A_bb = strict_lower(diag(beta) K_b K_b^T * Gamma) and their
+// inverses T_bb = (I + A_bb)^-1.  K_b K_b^T is symmetric, so its accumulator tile
+// also gives lane (l16, g4) row l16, columns 4*g4 .. 4*g4+3 of A_bb, written to LDS
+// row-major with one store.  Row j of T_bb solves (I + A_bb)^T t = e_j, an upper
+// triangular system: lanes 16b .. 16b+15 solve it for block b by back
+// substitution (lane j keeps row j of T_bb in registers, step c subtracts row c of
+// A_bb times t_c) and write the row with two or four 16-byte stores.
+template <class Tr>
+__device__ __forceinline__ void diag_blocks(const StageBuf<Tr> &s, SolveBuf<Tr> &v,
+                                            float (*AR)[16 * Tr::LDA], int lane) {
+  using M = typename Tr::M;
+  using frag = typename M::frag;
+  constexpr int NB = Tr::NB, KS = Tr::KS, LDK = Tr::LDK, LDC = Tr::LDC, LDA = Tr::LDA;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  frag f[NB][KS];
+  double gr[NB], gc[NB][4];
+  float br[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int sl = 0; sl < KS; ++sl) f[b][sl] = M::load(s.K, LDK, 16 * b + l16, 32 * sl, lane);
+    gr[b] = s.G[16 * b + l16];
+    br[b] = s.B[16 * b + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gc[b][i] = s.G[16 * b + 4 * g4 + i];
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    acc[b] = zero4();
+#pragma unroll
+    for (int sl = 0; sl < KS; ++sl) acc[b] = M::mma(f[b][sl], f[b][sl], acc[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * g4 + i;   // column within the block; the row is l16
+      const bool keep = c < l16;
+      const float d = keep ? static_cast<float>(gr[b] - gc[b][i]) : 0.0f;
+      a[i] = keep ? br[b] * acc[b][i] * fexp(d) : 0.0f;
+    }
+    *reinterpret_cast<float4 *>(AR[b] + l16 * LDA + 4 * g4) = make_float4(a[0], a[1], a[2], a[3]);
+  }
+  if (lane < 16 * NB) {
+    const int bk = lane >> 4, j = lane & 15;
+    const float *Ab = AR[bk];
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.0f : 0.0f;
+    // step c needs row c of A_bb left of its diagonal (quads 0 .. (c-1)/4); the rows
+    // are read in three batches, each ahead of its steps
+    auto steps = [&](auto first, auto count) {
+      constexpr int C0 = decltype(first)::value, NC = decltype(count)::value;
+      float4 row[NC][4];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int qd = 0; qd <= (C0 - cc - 1) / 4; ++qd)
+          row[cc][qd] = *reinterpret_cast<const float4 *>(Ab + (C0 - cc) * LDA + 4 * qd);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int c = C0 - cc;
+#pragma unroll
+        for (int r = 0; r < c; ++r) {
+          const float4 q = row[cc][r / 4];
+          const float acr = (r & 3) == 0 ? q.x : (r & 3) == 1 ? q.y : (r & 3) == 2 ? q.z : q.w;
+          t[r] -= acr * t[c];
+        }
+      }
+    };
+    steps(std::integral_constant<int, 15>(), std::integral_constant<int, 5>());
+    steps(std::integral_constant<int, 10>(), std::integral_constant<int, 5>());
+    steps(std::integral_constant<int, 5>(), std::integral_constant<int, 5>());
+    typename Tr::elem *trow = v.T + (16 * bk + j) * LDC + 16 * bk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x[4] = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+      store4e(trow + 4 * q, x);
+    }
+  }
+}
+
 template <class Tr>
 __device__ __forceinline__ void solve_chunk(const StageBuf<Tr> &s, SolveBuf<Tr> &v,
-                                            float (*AT)[16 * Tr::LDA], int pw, int lane) {
-  using M = typename Tr::M;
-  constexpr int NB = Tr::NB, NH = Tr::NH, LDK = Tr::LDK, LDC = Tr::LDC, LDA = Tr::LDA;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  // one 16x16 tile of diag(beta) K K^T * Gamma (rows mi, columns ni), strict lower
-  auto a_tile = [&](int mi, int ni, float (&out)[4]) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int sl = 0; sl < Tr::KS; ++sl)
-      acc = M::mma(M::load(s.K, LDK, 16 * mi + l16, 32 * sl, lane),
-                   M::load(s.K, LDK, 16 * ni + l16, 32 * sl, lane), acc);
-    const int c = 16 * ni + l16;
-    const double gc = s.G[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mi + 4 * g4 + i;
-      // mask before the exponential: G_r - G_c may be large positive above
-      const float d = c < r ? static_cast<float>(s.G[r] - gc) : 0.0f;
-      out[i] = c < r ? s.B[r] * acc[i] * fexp(d) : 0.0f;
-    }
-  };
-  if (pw < NB) {
-    const int bk = pw;
-    float a[4];
-    a_tile(bk, bk, a);
-    // column-major: column c of A_bb is 16 contiguous floats (one 16-byte store
-    // per lane here, four 16-byte loads per column below)
-    float *Ab = AT[bk];
-    *reinterpret_cast<float4 *>(Ab + l16 * LDA + 4 * g4) = make_float4(a[0], a[1], a[2], a[3]);
-    // column substitution: lanes 0..15 keep column j of (I + A_bb)^-1 in registers;
-    // step i eliminates entry i from the rows below it, with column i+1 already
-    // being loaded while step i computes
-    if (lane < 16) {
-      const int j = lane;
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = (r == j) ? 1.0f : 0.0f;
-      float4 cur[4], nxt[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cur[q] = *reinterpret_cast<const float4 *>(Ab + 4 * q);
-#pragma unroll
-      for (int i = 0; i < 15; ++i) {
-        if (i + 1 < 15) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            nxt[q] = *reinterpret_cast<const float4 *>(Ab + (i + 1) * LDA + 4 * q);
-        }
-        const float col[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
-                               cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
-                               cur[3].x, cur[3].y, cur[3].z, cur[3].w};
-#pragma unroll
-        for (int r = i + 1; r < 16; ++r) t[r] -= col[r] * t[i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v.T[(16 * bk + r) * LDC + 16 * bk + j] = M::cvt(t[r]);
-    }
-    return;
-  }
-  // tiles: A_10 (32-row chunks), then the P tiles on or below the causal boundary
-  constexpr int nwk = Tr::NP - NB;
-  constexpr int NA = NB == 2 ? 1 : 0;
-  constexpr int NPT = Tr::NQB * NB;
-  for (int ti = pw - NB; ti < NA + NPT; ti += nwk) {
-    if (NA == 1 && ti == 0) {
-      float a[4];
-      a_tile(1, 0, a);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v.A10[(4 * g4 + i) * LDC + l16] = M::cvt(a[i]);
-      continue;
-    }
-    const int pt = ti - NA;
-    const int mq = pt / NB, ni = pt % NB;
-    if (16 * ni > NH * (16 * mq + 15) + NH - 1) continue;   // above the boundary: zero
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int sl = 0; sl < Tr::KS; ++sl)
-      acc = M::mma(M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane),
-                   M::load(s.K, LDK, 16 * ni + l16, 32 * sl, lane), acc);
-    const int c = 16 * ni + l16;
-    const double gc = s.G[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = 16 * mq + 4 * g4 + i;
-      const int r = NH * q + NH - 1;
-      const float d = c <= r ? static_cast<float>(s.G[r] - gc) : 0.0f;
-      v.P[q * LDC + c] = M::cvt(c <= r ? acc[i] * fexp(d) : 0.0f);
-    }
-  }
-  // K~^T[d][r] = exp(G_last - G_r) K[r][d]: a lane takes two rows and 8 keys and
-  // writes 8 row pairs (one 32-bit store each for fp16 operands)
-  {
-    constexpr int UNITS = (Tr::CR / 2) * Tr::SEG;  // (row pair, segment) units
-    for (int u = (pw - NB) * 64 + lane; u < UNITS; u += nwk * 64) {
-      const int rp = u % (Tr::CR / 2), sg = u / (Tr::CR / 2);
-      const int r0 = 2 * rp;
-      const float d0 = s.eGl[r0], d1 = s.eGl[r0 + 1];
-      float x0[8], x1[8];
-      load8(s.K + r0 * LDK + 8 * sg, x0);
-      load8(s.K + (r0 + 1) * LDK + 8 * sg, x1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) store2(v.KT + (8 * sg + e) * LDC + r0, x0[e] * d0, x1[e] * d1);
-    }
-  }
+                                            float (*AR)[16 * Tr::LDA], int pw, int lane) {
+  static_assert(Tr::NP == 4, "four producer waves");
+  constexpr int NJ = tile_job_count<Tr>();
+  constexpr int H1 = (NJ + 1) / 2;
+  if (pw == 0)
+    diag_blocks<Tr>(s, v, AR, lane);
+  else if (pw == 1)
+    run_tiles<Tr, 0, H1>(s, v, lane);
+  else if (pw == 2)
+    run_tiles<Tr, H1, NJ>(s, v, lane);
 }
 
 template <typename TIn, typename TOut, int DK, int CR, int NH, int NS, bool F32>
@@ -322,7 +417,7 @@ prefill_kernel(const PrefillParams p) {
   using elem = typename Tr::elem;
   using frag = typename M::frag;
   constexpr int CQ = Tr::CQ, NB = Tr::NB, NQB = Tr::NQB, DVT = Tr::DVT, SEG = Tr::SEG;
-  constexpr int LDK = Tr::LDK, LDC = Tr::LDC, LDVT = Tr::LDVT, NT = Tr::NT, PT = Tr::PT;
+  constexpr int LDK = Tr::LDK, LDC = Tr::LDC, LDVT = Tr::LDVT, NT = Tr::NT, ST = Tr::ST;
   constexpr int KS = Tr::KS, KM = Tr::KM, KPT = Tr::KPT, QPT = Tr::QPT;
 
   __shared__ PrefillSmem<Tr> sm;
@@ -334,7 +429,7 @@ prefill_kernel(const PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const bool is_state = wave < NS;
   const int pw = wave - NS;            // producer wave index (state waves: negative)
-  const int ptid = tid - 64 * NS;      // producer thread index
+  const int stid = tid - 64 * NS;      // staging thread index
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -373,11 +468,18 @@ prefill_kernel(const PrefillParams p) {
   const uint32_t vstride = p.Hv * p.DV;      // elements between value / output rows
   const size_t state_stride = static_cast<size_t>(DK) * p.DV;
 
-  // parts of the solve buffers no chunk writes must read as zero
+  // parts of the solve buffers and of K^T (columns past a 16-row chunk) that no
+  // chunk writes must read as zero
   {
     elem *z = reinterpret_cast<elem *>(&sm.sv[0]);
     constexpr int nz = static_cast<int>(sizeof(sm.sv) / (sizeof(elem)));
     for (int i = tid; i < nz; i += NT) z[i] = M::cvt(0.0f);
+    if constexpr (CR < 32) {
+      constexpr int nkt = Tr::DK * LDC;
+#pragma unroll
+      for (int b = 0; b < 3; ++b)
+        for (int i = tid; i < nkt; i += NT) sm.st[b].KT[i] = M::cvt(0.0f);
+    }
   }
 
   // ---- initial state -> registers of the state waves --------------------------
@@ -403,6 +505,20 @@ prefill_kernel(const PrefillParams p) {
 
   ChunkRegs<Tr> cra, crb;   // producer registers: two chunks' inputs
 
+  // K unit u -> (row pair, segment).  With L2 normalisation the SEG units of a row
+  // pair sit in consecutive lanes (the norm is a reduction over them); without it
+  // consecutive lanes take consecutive row pairs, so that the transposed stores
+  // of a wave fall in distinct banks.
+  auto k_unit = [&](int u, int &rp, int &sg) {
+    if (p.l2norm) {
+      rp = u / SEG;
+      sg = u % SEG;
+    } else {
+      rp = u % (CR / 2);
+      sg = u / (CR / 2);
+    }
+  };
+
   // inputs of the chunk starting at row c -> producer registers (addresses clamped
   // to the sequence and the column tile, also for chunks past the end; validity is
   // applied where the values are consumed)
@@ -412,25 +528,29 @@ prefill_kernel(const PrefillParams p) {
     cr.c = c;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int idx = ptid + j * PT, r = idx / SEG, sg = idx % SEG;
-      const int row = min(c + r, last);
-      cr.k[j].load(kb + (static_cast<uint32_t>(row) * kstride + sg * 8));
+      int rp, sg;
+      k_unit(stid + j * ST, rp, sg);
+      rp = min(rp, CR / 2 - 1);
+      sg = min(sg, SEG - 1);
+      const int ra = min(c + 2 * rp, last), rb = min(c + 2 * rp + 1, last);
+      cr.k[j][0].load(kb + (static_cast<uint32_t>(ra) * kstride + sg * 8));
+      cr.k[j][1].load(kb + (static_cast<uint32_t>(rb) * kstride + sg * 8));
     }
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
-      const int idx = ptid + j * PT, r = idx / SEG, sg = idx % SEG;
+      const int idx = stid + j * ST, r = idx / SEG, sg = idx % SEG;
       const int t = min(tq + r, tlast);
       cr.q[j].load(qb + (static_cast<uint32_t>(t) * kstride + sg * 8));
     }
 #pragma unroll
     for (int j = 0; j < Tr::VPT; ++j) {
-      const int u = ptid + j * PT;
+      const int u = stid + j * ST;
       const int rp = u % (CR / 2), sg = min(u / (CR / 2), Tr::VSEG - 1);
       const int ra = min(c + 2 * rp, last), rb = min(c + 2 * rp + 1, last);
       cr.v[j][0].load(vrow + (static_cast<uint32_t>(ra) * vstride + sg * 8));
       cr.v[j][1].load(vrow + (static_cast<uint32_t>(rb) * vstride + sg * 8));
     }
-    if (pw == 0) {
+    if (pw == 3) {
       const int row = min(c + lane, last);
       cr.g = gb[static_cast<uint32_t>(row / NH) * p.Hv];
       cr.b = bb[static_cast<uint32_t>(row) * p.Hv];
@@ -440,34 +560,50 @@ prefill_kernel(const PrefillParams p) {
   auto stage = [&](const ChunkRegs<Tr> &cr, StageBuf<Tr> &s) {
     const int nrow = min(CR, row_end - cr.c);              // valid key rows
     const int nq = min(CQ, t1 - cr.c / NH);                // valid query rows
-    auto rows = [&](const Seg8<TIn> *srcr, int count, int nrows, int nvalid, elem *dstm) {
+    // one 8-element segment of a row: zero past the valid rows, optionally divided
+    // by the row's L2 norm (the SEG lanes holding a row are consecutive)
+    auto segment = [&](const Seg8<TIn> &src, bool valid, float (&x)[8]) {
+      src.get(x);
+      if (!valid) {
 #pragma unroll
-      for (int j = 0; j < count; ++j) {
-        const int idx = ptid + j * PT, r = idx / SEG, sg = idx % SEG;
-        float x[8];
-        srcr[j].get(x);
-        if (nvalid < nrows && r >= nvalid) {
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+      }
+      if (p.l2norm) {
+        float ss = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-        }
-        if (p.l2norm) {
-          float ss = 0.0f;
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        for (int o = SEG / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        const float rn = 1.0f / sqrtf(ss + 1e-6f);
 #pragma unroll
-          for (int o = SEG / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-          const float rn = 1.0f / sqrtf(ss + 1e-6f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= rn;
-        }
-        if (r < nrows) store8(dstm + r * LDK + sg * 8, x);
+        for (int e = 0; e < 8; ++e) x[e] *= rn;
       }
     };
-    rows(cr.k, KPT, CR, nrow, s.K);
-    rows(cr.q, QPT, CQ, nq, s.Q);
+    // K rows 2rp, 2rp+1: row-major, and transposed as row pairs
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      int rp, sg;
+      k_unit(stid + j * ST, rp, sg);
+      float x0[8], x1[8];
+      segment(cr.k[j][0], nrow == CR || 2 * rp < nrow, x0);
+      segment(cr.k[j][1], nrow == CR || 2 * rp + 1 < nrow, x1);
+      if (Tr::KUNITS % ST == 0 || (rp < CR / 2 && sg < SEG)) {
+        store8(s.K + (2 * rp) * LDK + sg * 8, x0);
+        store8(s.K + (2 * rp + 1) * LDK + sg * 8, x1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store2(s.KT + (8 * sg + e) * LDC + 2 * rp, x0[e], x1[e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int idx = stid + j * ST, r = idx / SEG, sg = idx % SEG;
+      float x[8];
+      segment(cr.q[j], nq == CQ || r < nq, x);
+      if (r < CQ) store8(s.Q + r * LDK + sg * 8, x);
+    }
 #pragma unroll
     for (int j = 0; j < Tr::VPT; ++j) {
-      const int u = ptid + j * PT;
+      const int u = stid + j * ST;
       const int rp = u % (CR / 2), sg = u / (CR / 2);
       Seg8<TIn> a = cr.v[j][0], b = cr.v[j][1];
       if (nrow < CR) {
@@ -476,7 +612,7 @@ prefill_kernel(const PrefillParams p) {
       }
       if (sg < Tr::VSEG) store_vt_pairs(s.VT + (8 * sg) * LDVT + 2 * rp, LDVT, a, b);
     }
-    if (pw == 0) {
+    if (pw == 3) {
       // inclusive prefix sum of the per-row decay, in fp64, and per-row factors
       const bool ok = lane < nrow;
       const double gr = prefix_sum32((ok && (cr.c + lane) % NH == 0) ? cr.g : 0.0);
@@ -496,14 +632,15 @@ prefill_kernel(const PrefillParams p) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- prologue ---------------------------------------------------------------------
-  if (!is_state && nchunks > 0) {
+  const bool stager = !is_state;   // producer waves that stage and fetch
+  if (stager && nchunks > 0) {
     fetch(cra, row_begin);
     stage(cra, sm.st[0]);
     fetch(crb, row_begin + CR);
   }
   __syncthreads();
-  if (!is_state && nchunks > 0) {
-    solve_chunk<Tr>(sm.st[0], sm.sv[0], sm.AT, pw, lane);
+  if (stager && nchunks > 0) {
+    solve_chunk<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, lane);
     if (nchunks > 1) stage(crb, sm.st[1]);
     fetch(cra, row_begin + 2 * CR);
   }
@@ -514,6 +651,28 @@ prefill_kernel(const PrefillParams p) {
   // chunk ci's state products (state waves) overlap the solve of chunk ci+1, the
   // staging of chunk ci+2 and the fetch of chunk ci+3 (producer waves).
   if (is_state) {
+    // Software pipeline of the state waves: the operands of R for chunk ci+1 (its
+    // K fragments, V columns, beta and exp(G) rows; staged an interval earlier) are
+    // read at the end of interval ci, so they arrive while the wave waits at the
+    // barrier; the solved operands and Q are read behind the products of R, the
+    // decayed keys behind those of Q H0.
+    frag kf[NB][KS];
+    float vr[2][NB][4], br[NB][4], er[NB][4];
+    auto load_r = [&](const StageBuf<Tr> &s) {
+#pragma unroll
+      for (int mk = 0; mk < NB; ++mk) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) kf[mk][sl] = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
+        const int r0 = 16 * mk + 4 * g4;
+        const float4 b4 = *reinterpret_cast<const float4 *>(s.B + r0);
+        const float4 e4 = *reinterpret_cast<const float4 *>(s.eG + r0);
+        br[mk][0] = b4.x; br[mk][1] = b4.y; br[mk][2] = b4.z; br[mk][3] = b4.w;
+        er[mk][0] = e4.x; er[mk][1] = e4.y; er[mk][2] = e4.z; er[mk][3] = e4.w;
+        load4(s.VT + (32 * wave + l16) * LDVT + r0, vr[0][mk]);
+        load4(s.VT + (32 * wave + 16 + l16) * LDVT + r0, vr[1][mk]);
+      }
+    };
+    if (nchunks > 0) load_r(sm.st[0]);
     for (int ci = 0; ci < nchunks; ++ci) {
       const int c0 = row_begin + ci * CR;
       // ---- state-dependent products of chunk ci (this wave's 32 columns) ----
@@ -528,42 +687,52 @@ prefill_kernel(const PrefillParams p) {
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) hb[ct][sl] = M::from_acc(H[ct][2 * sl], H[ct][2 * sl + 1]);
 
-      // R = diag(beta) (V - diag(exp G) K H0)
-      f32x4 R[2][2];
+      // X = K H0 (both column tiles)
+      f32x4 X[2][2];
 #pragma unroll
       for (int mk = 0; mk < NB; ++mk) {
-        f32x4 a0 = zero4(), a1 = zero4();
+        X[0][mk] = zero4();
+        X[1][mk] = zero4();
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) {
-          const frag kf = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
-          a0 = M::mma(kf, hb[0][sl], a0);
-          a1 = M::mma(kf, hb[1][sl], a1);
-        }
-        const int r0 = 16 * mk + 4 * g4;
-        const float4 b4 = *reinterpret_cast<const float4 *>(s.B + r0);
-        const float4 e4 = *reinterpret_cast<const float4 *>(s.eG + r0);
-        const float bq[4] = {b4.x, b4.y, b4.z, b4.w}, eq[4] = {e4.x, e4.y, e4.z, e4.w};
-        float v0[4], v1[4];
-        load4(s.VT + (32 * wave + l16) * LDVT + r0, v0);
-        load4(s.VT + (32 * wave + 16 + l16) * LDVT + r0, v1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          R[0][mk][i] = bq[i] * (v0[i] - eq[i] * a0[i]);
-          R[1][mk][i] = bq[i] * (v1[i] - eq[i] * a1[i]);
+          X[0][mk] = M::mma(kf[mk][sl], hb[0][sl], X[0][mk]);
+          X[1][mk] = M::mma(kf[mk][sl], hb[1][sl], X[1][mk]);
         }
       }
+      // the operands of D and O, read while those products run
+      const frag tf0 = M::load(v.T, LDC, l16, 0, lane);
+      frag af, tf1;
+      if constexpr (NB == 2) {
+        af = M::load(v.A10, LDC, l16, 0, lane);
+        tf1 = M::load(v.T, LDC, 16 + l16, 0, lane);
+      }
+      frag qf[NQB][KS], pf[NQB];
+      float sx[NQB];
+#pragma unroll
+      for (int mq = 0; mq < NQB; ++mq) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) qf[mq][sl] = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
+        pf[mq] = M::load(v.P, LDC, 16 * mq + l16, 0, lane);
+        sx[mq] = p.scale * s.eG[NH * (16 * mq + l16) + NH - 1];
+      }
+      const float dl = s.eG[CR - 1];
+
+      // R = diag(beta) (V - diag(exp G) X)
+      f32x4 R[2][2];
+#pragma unroll
+      for (int mk = 0; mk < NB; ++mk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          R[0][mk][i] = br[mk][i] * (vr[0][mk][i] - er[mk][i] * X[0][mk][i]);
+          R[1][mk][i] = br[mk][i] * (vr[1][mk][i] - er[mk][i] * X[1][mk][i]);
+        }
       if constexpr (NB == 1) R[0][1] = R[1][1] = zero4();
 
       // D_0 = T_00 R_0;  D_1 = T_11 (R_1 - A_10 D_0)   (T rows hold diag(T_00, T_11))
       f32x4 D[2][2];
-      {
-        const frag tf0 = M::load(v.T, LDC, l16, 0, lane);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) D[ct][0] = M::mma(tf0, M::from_acc(R[ct][0], zero4()), zero4());
-      }
+      for (int ct = 0; ct < 2; ++ct) D[ct][0] = M::mma(tf0, M::from_acc(R[ct][0], zero4()), zero4());
       if constexpr (NB == 2) {
-        const frag af = M::load(v.A10, LDC, l16, 0, lane);
-        const frag tf1 = M::load(v.T, LDC, 16 + l16, 0, lane);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const f32x4 z = M::mma(af, M::from_acc(D[ct][0], zero4()), zero4());
@@ -576,43 +745,65 @@ prefill_kernel(const PrefillParams p) {
       const frag db[2] = {M::from_acc(D[0][0], D[0][1]), M::from_acc(D[1][0], D[1][1])};
 
       // O^T = scale (H0^T Q^T diag(exp G) + D^T P^T): lane holds output columns
-      // 4*g4 .. 4*g4+3 of token l16 of the query block
+      // 4*g4 .. 4*g4+3 of token l16 of each query block
+      f32x4 xo[NQB][2], yo[NQB][2];
 #pragma unroll
       for (int mq = 0; mq < NQB; ++mq) {
-        f32x4 x0 = zero4(), x1 = zero4();
+        xo[mq][0] = zero4();
+        xo[mq][1] = zero4();
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) {
-          const frag qf = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
-          x0 = M::mma(hb[0][sl], qf, x0);
-          x1 = M::mma(hb[1][sl], qf, x1);
+          xo[mq][0] = M::mma(hb[0][sl], qf[mq][sl], xo[mq][0]);
+          xo[mq][1] = M::mma(hb[1][sl], qf[mq][sl], xo[mq][1]);
         }
-        const frag pf = M::load(v.P, LDC, 16 * mq + l16, 0, lane);
-        const f32x4 y0 = M::mma(db[0], pf, zero4());
-        const f32x4 y1 = M::mma(db[1], pf, zero4());
-        const int q = 16 * mq + l16;
-        const float sx = p.scale * s.eG[NH * q + NH - 1];
+      }
+      // the keys of the update, read while those products run
+      frag kt[KM];
+#pragma unroll
+      for (int m = 0; m < KM; ++m) kt[m] = M::load(s.KT, LDC, 16 * m + l16, 0, lane);
+      // D~ = diag(exp(G_last - G)) D: the decay of the update, on its B operand
+      frag dk[2];
+      {
+        const float4 l0 = *reinterpret_cast<const float4 *>(s.eGl + 4 * g4);
+        f32x4 e0 = {l0.x, l0.y, l0.z, l0.w}, e1 = zero4();
+        if constexpr (NB == 2) {
+          const float4 l1 = *reinterpret_cast<const float4 *>(s.eGl + 16 + 4 * g4);
+          e1 = f32x4{l1.x, l1.y, l1.z, l1.w};
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) dk[ct] = M::from_acc(D[ct][0] * e0, D[ct][1] * e1);
+      }
+#pragma unroll
+      for (int mq = 0; mq < NQB; ++mq) {
+        yo[mq][0] = M::mma(db[0], pf[mq], zero4());
+        yo[mq][1] = M::mma(db[1], pf[mq], zero4());
+      }
+
+      // H <- exp(G_last) H0 + K^T D~
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        H[0][m] = M::mma(kt[m], dk[0], H[0][m] * dl);
+        H[1][m] = M::mma(kt[m], dk[1], H[1][m] * dl);
+      }
+
+#pragma unroll
+      for (int mq = 0; mq < NQB; ++mq) {
         float o0[4], o1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          o0[i] = sx * x0[i] + p.scale * y0[i];
-          o1[i] = sx * x1[i] + p.scale * y1[i];
+          o0[i] = sx[mq] * xo[mq][0][i] + p.scale * yo[mq][0][i];
+          o1[i] = sx[mq] * xo[mq][1][i] + p.scale * yo[mq][1][i];
         }
-        const int tok = tq0 + q;
+        const int tok = tq0 + 16 * mq + l16;
         if (full || tok < t1) {
           TOut *o = ob + (static_cast<uint32_t>(tok) * vstride + 4 * g4);
           store4(o, o0);
           store4(o + 16, o1);
         }
       }
-
-      // H <- exp(G_last) H0 + K~^T D
-      const float dl = s.eG[CR - 1];
-#pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        const frag kt = M::load(v.KT, LDC, 16 * m + l16, 0, lane);
-        H[0][m] = M::mma(kt, db[0], H[0][m] * dl);
-        H[1][m] = M::mma(kt, db[1], H[1][m] * dl);
-      }
+      // the R operands of the next chunk (staged an interval ago; read past the end
+      // of the sequence they are never used)
+      load_r(sm.st[(ci + 1) % 3]);
       __syncthreads();
     }
   } else if (nchunks > 0) {
@@ -621,9 +812,11 @@ prefill_kernel(const PrefillParams p) {
     // carried around the loop stays in place
     auto produce = [&](int ci, const ChunkRegs<Tr> &from, ChunkRegs<Tr> &into) {
       if (ci + 1 < nchunks)
-        solve_chunk<Tr>(sm.st[(ci + 1) % 3], sm.sv[(ci + 1) & 1], sm.AT, pw, lane);
-      if (ci + 2 < nchunks) stage(from, sm.st[(ci + 2) % 3]);
-      fetch(into, row_begin + (ci + 3) * CR);
+        solve_chunk<Tr>(sm.st[(ci + 1) % 3], sm.sv[(ci + 1) & 1], sm.AR, pw, lane);
+      if (stager) {
+        if (ci + 2 < nchunks) stage(from, sm.st[(ci + 2) % 3]);
+        fetch(into, row_begin + (ci + 3) * CR);
+      }
       __syncthreads();
     };
     for (int ci = 0;; ci += 2) {
