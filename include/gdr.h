@@ -86,7 +86,7 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
  *   token, before the first sub-step, and o_t is read after the last one).
  * chunk_size: tokens per chunk, a power of two in [16, 256].  Chunking does not
  *   change the result beyond rounding; the kernels evaluate chunks of
- *   min(chunk_size * n_h, 64) rows (at most 32 rows for float32 inputs).
+ *   min(chunk_size * n_h, 32) rows (16 rows for float32 inputs with K = 128).
  * Supported: K in {64, 128}, V in {64, 128}, n_h in {1, 2}, q/k/v F32 or BF16,
  *   out F32 or BF16.
  */
