@@ -53,6 +53,14 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
   if (a->state_indices && a->num_slots <= 0) return GDR_ERR_INVALID_ARG;
   const int64_t tokens = int64_t{a->batch} * a->seqlen;
   if (tokens * a->num_householder > kMaxRows) return GDR_ERR_UNSUPPORTED;
+  // the prefill kernels form element offsets within q, k, v and out as 32-bit
+  // unsigned values: rows * (heads * head size) must stay below 2^32
+  {
+    const int64_t kw = int64_t{a->num_qk_heads} * a->head_k;
+    const int64_t vw = int64_t{a->num_v_heads} * a->head_v;
+    if (tokens * a->num_householder * (kw > vw ? kw : vw) >= (int64_t{1} << 32))
+      return GDR_ERR_UNSUPPORTED;
+  }
   if (!head_ok(a->head_k) || !head_ok(a->head_v)) return GDR_ERR_UNSUPPORTED;
   if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
   if (!pow2(a->chunk_size) || a->chunk_size < 16 || a->chunk_size > 256)

@@ -88,7 +88,9 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
  *   change the result beyond rounding; the kernels evaluate chunks of
  *   min(chunk_size * n_h, 32) rows (16 rows for float32 inputs with K = 128).
  * Supported: K in {64, 128}, V in {64, 128}, n_h in {1, 2}, q/k/v F32 or BF16,
- *   out F32 or BF16.
+ *   out F32 or BF16, Tt * n_h < 2^31 - 1024 rows and
+ *   Tt * n_h * max(Hk * K, Hv * V) < 2^32 (element offsets within q, k, v and out
+ *   are 32-bit); larger inputs return GDR_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t batch;            /* B; 1 when cu_seqlens is given                        */

@@ -88,6 +88,8 @@ def _decode(**kw):
     (dict(seqlen=0, q=None, k=None, v=None, g=None, beta=None, out=None), 0),  # empty
     (dict(batch=-1), 1),
     (dict(seqlen=1 << 30, batch=2, num_seqs=2), 2),  # beyond the row limit
+    (dict(seqlen=1 << 23, batch=1, num_seqs=1), 2),  # offsets past 2^32 elements
+    (dict(seqlen=(1 << 23) - 64, batch=1, num_seqs=1, num_v_heads=2), 0),
 ])
 def test_validate_prefill(lib, kw, code):
     a = _prefill(**kw)
