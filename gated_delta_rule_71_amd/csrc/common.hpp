@@ -127,8 +127,14 @@ template <> struct Mma<false> {
                                               int lane) {
     const int g = lane >> 4;
     const elem *p = base + row * ld + k0 + 4 * g;
+    // Two separate 8-byte reads.  The compiler would otherwise pair them into one
+    // ds_read2_b64, whose two addresses 32 bytes apart collide in the LDS banks
+    // (about four times the cycles of two single reads at these row strides); the
+    // empty asm with a memory clobber keeps them apart.
     const f16x4 lo = *reinterpret_cast<const f16x4 *>(p);
+    asm volatile("" ::: "memory");
     const f16x4 hi = *reinterpret_cast<const f16x4 *>(p + 16);
+    asm volatile("" ::: "memory");
     frag f;
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return f;
