@@ -152,7 +152,13 @@ struct PrefillTraits {
   static constexpr int LDK = DK + PAD;               // K, Q leading dimension
   static constexpr int LDC = 32 + PAD;               // T, A10, P, KT leading dimension
   static constexpr int LDA = 20;                     // AR (fp32 16x16 blocks) leading dim.
-  static constexpr int LDVT = CR + 4;                // VT (value column major) leading dim.
+  // VT (value column major) leading dimension: with 8 elements of padding the
+  // bf16 rows sit 20 LDS words apart, where a wave's 8-byte reads of them do not
+  // collide in the banks (fp32 keeps 4: its largest tile would not fit otherwise)
+  static constexpr int LDVT = CR + (F32 ? 4 : 8);
+  // AR block stride: four words past 16 rows, so that the two blocks' rows read
+  // together during the inversion fall in different banks
+  static constexpr int ARB = 16 * LDA + 4;
   static constexpr int KS = DK / 32;                 // 32-deep slices over keys
   static constexpr int KM = DK / 16;                 // 16-row blocks of H
   static constexpr int SEG = DK / 8;                 // 8-element segments per row
@@ -191,7 +197,7 @@ template <class Tr>
 struct PrefillSmem {
   StageBuf<Tr> st[3];
   SolveBuf<Tr> sv[2];
-  float AR[2][16 * Tr::LDA];   // the diagonal blocks A_bb (fp32, row-major) for the inversion
+  float AR[2][Tr::ARB];   // the diagonal blocks A_bb (fp32, row-major) for the inversion
 };
 
 // Inputs of one chunk held in a producer thread's registers between their fetch
@@ -319,7 +325,7 @@ __device__ __forceinline__ void run_tiles(const StageBuf<Tr> &s, SolveBuf<Tr> &v
 // A_bb times t_c) and write the row with two or four 16-byte stores.
 template <class Tr>
 __device__ __forceinline__ void diag_blocks(const StageBuf<Tr> &s, SolveBuf<Tr> &v,
-                                            float (*AR)[16 * Tr::LDA], int lane) {
+                                            float (*AR)[Tr::ARB], int lane) {
   using M = typename Tr::M;
   using frag = typename M::frag;
   constexpr int NB = Tr::NB, KS = Tr::KS, LDK = Tr::LDK, LDC = Tr::LDC, LDA = Tr::LDA;
@@ -397,7 +403,7 @@ __device__ __forceinline__ void diag_blocks(const StageBuf<Tr> &s, SolveBuf<Tr> 
 
 template <class Tr>
 __device__ __forceinline__ void solve_chunk(const StageBuf<Tr> &s, SolveBuf<Tr> &v,
-                                            float (*AR)[16 * Tr::LDA], int pw, int lane) {
+                                            float (*AR)[Tr::ARB], int pw, int lane) {
   static_assert(Tr::NP == 4, "four producer waves");
   constexpr int NJ = tile_job_count<Tr>();
   constexpr int H1 = (NJ + 1) / 2;
