@@ -25,11 +25,11 @@
 //     which puts four consecutive output columns of one token in each lane.
 //   * NP producer waves prepare the chunks ahead of them: they solve chunk i+1
 //     (the 16x16 diagonal blocks of A on the matrix cores and the inverses of
-//     I + A_bb by column substitution, one block per wave; the off-diagonal block
-//     A_10; P = Q K^T * Gamma; and the decayed, transposed keys K~^T of the state
-//     update), stage chunk i+2 (K, Q, optionally L2-normalised, the workgroup's V
-//     columns transposed, the cumulative decay and per-row factors) from registers
-//     into LDS, and fetch the inputs of chunk i+3 into registers.
+//     I + A_bb by back substitution, both blocks on one wave; the off-diagonal
+//     block A_10; P = scale (Q K^T * Gamma)), stage chunk i+2 (K and K^T, Q,
+//     optionally L2-normalised, the workgroup's V columns transposed, the
+//     cumulative decay and per-row factors) from registers into LDS, and fetch the
+//     inputs of chunk i+3 into registers.
 // Both kinds work at once and meet at one workgroup barrier per chunk, so a chunk
 // interval costs the longer of the two instead of their sum.  With the diagonal
 // inverses T_bb the chunk's delta follows by block forward substitution,
@@ -191,7 +191,7 @@ template <class Tr>
 struct alignas(16) SolveBuf {
   typename Tr::elem T[Tr::CR * Tr::LDC];    // diag(T_00, T_11), T_bb = (I + A_bb)^-1
   typename Tr::elem A10[16 * Tr::LDC];      // A_10 in columns 0..15 (32-row chunks)
-  typename Tr::elem P[Tr::CQ * Tr::LDC];    // Q K^T * Gamma, causal
+  typename Tr::elem P[Tr::CQ * Tr::LDC];    // scale (Q K^T * Gamma), causal
 };
 template <class Tr>
 struct PrefillSmem {
@@ -253,11 +253,12 @@ __device__ __forceinline__ void store4e(float *p, const float (&x)[4]) {
 }
 
 // Off-diagonal tiles J0 .. J1-1: A_10 = strict_lower(diag(beta) K_1 K_0^T * Gamma) and
-// P tiles = (Q K^T * Gamma) on or below the causal boundary.  Each is formed
+// P tiles = scale (Q K^T * Gamma) on or below the causal boundary.  Each is formed
 // transposed (K_ni X^T), so that a lane holds four consecutive columns of one row
 // and writes them with one store.
 template <class Tr, int J0, int J1>
-__device__ __forceinline__ void run_tiles(const StageBuf<Tr> &s, SolveBuf<Tr> &v, int lane) {
+__device__ __forceinline__ void run_tiles(const StageBuf<Tr> &s, SolveBuf<Tr> &v, float scale,
+                                          int lane) {
   constexpr int N = J1 - J0;
   if constexpr (N > 0) {
     using M = typename Tr::M;
@@ -281,7 +282,7 @@ __device__ __forceinline__ void run_tiles(const StageBuf<Tr> &s, SolveBuf<Tr> &v
       const int q = 16 * mi + l16;               // row of A_10 / P held by this lane
       const int r = is_p ? NH * q + NH - 1 : q;  // its key row
       gr[j] = s.G[r];
-      br[j] = is_p ? 1.0f : s.B[r];
+      br[j] = is_p ? scale : s.B[r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) gc[j][i] = s.G[16 * ni + 4 * g4 + i];
     }
@@ -403,16 +404,17 @@ __device__ __forceinline__ void diag_blocks(const StageBuf<Tr> &s, SolveBuf<Tr> 
 
 template <class Tr>
 __device__ __forceinline__ void solve_chunk(const StageBuf<Tr> &s, SolveBuf<Tr> &v,
-                                            float (*AR)[Tr::ARB], int pw, int lane) {
+                                            float (*AR)[Tr::ARB], int pw, float scale,
+                                            int lane) {
   static_assert(Tr::NP == 4, "four producer waves");
   constexpr int NJ = tile_job_count<Tr>();
   constexpr int H1 = (NJ + 1) / 2;
   if (pw == 0)
     diag_blocks<Tr>(s, v, AR, lane);
   else if (pw == 1)
-    run_tiles<Tr, 0, H1>(s, v, lane);
+    run_tiles<Tr, 0, H1>(s, v, scale, lane);
   else if (pw == 2)
-    run_tiles<Tr, H1, NJ>(s, v, lane);
+    run_tiles<Tr, H1, NJ>(s, v, scale, lane);
 }
 
 template <typename TIn, typename TOut, int DK, int CR, int NH, int NS, bool F32>
@@ -646,7 +648,7 @@ prefill_kernel(const PrefillParams p) {
   }
   __syncthreads();
   if (stager && nchunks > 0) {
-    solve_chunk<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, lane);
+    solve_chunk<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, p.scale, lane);
     if (nchunks > 1) stage(crb, sm.st[1]);
     fetch(cra, row_begin + 2 * CR);
   }
@@ -750,8 +752,8 @@ prefill_kernel(const PrefillParams p) {
       }
       const frag db[2] = {M::from_acc(D[0][0], D[0][1]), M::from_acc(D[1][0], D[1][1])};
 
-      // O^T = scale (H0^T Q^T diag(exp G) + D^T P^T): lane holds output columns
-      // 4*g4 .. 4*g4+3 of token l16 of each query block
+      // O^T = scale H0^T Q^T diag(exp G) + D^T P^T (P carries the scale): lane holds
+      // output columns 4*g4 .. 4*g4+3 of token l16 of each query block
       f32x4 xo[NQB][2], yo[NQB][2];
 #pragma unroll
       for (int mq = 0; mq < NQB; ++mq) {
@@ -797,8 +799,8 @@ prefill_kernel(const PrefillParams p) {
         float o0[4], o1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          o0[i] = sx[mq] * xo[mq][0][i] + p.scale * yo[mq][0][i];
-          o1[i] = sx[mq] * xo[mq][1][i] + p.scale * yo[mq][1][i];
+          o0[i] = sx[mq] * xo[mq][0][i] + yo[mq][0][i];   // P carries the scale
+          o1[i] = sx[mq] * xo[mq][1][i] + yo[mq][1][i];
         }
         const int tok = tq0 + 16 * mq + l16;
         if (full || tok < t1) {
@@ -818,7 +820,7 @@ prefill_kernel(const PrefillParams p) {
     // carried around the loop stays in place
     auto produce = [&](int ci, const ChunkRegs<Tr> &from, ChunkRegs<Tr> &into) {
       if (ci + 1 < nchunks)
-        solve_chunk<Tr>(sm.st[(ci + 1) % 3], sm.sv[(ci + 1) & 1], sm.AR, pw, lane);
+        solve_chunk<Tr>(sm.st[(ci + 1) % 3], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
       if (stager) {
         if (ci + 2 < nchunks) stage(from, sm.st[(ci + 2) % 3]);
         fetch(into, row_begin + (ci + 3) * CR);
