@@ -1,8 +1,8 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,gdp]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,gdp,gates]
 
-Three legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Four legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
@@ -13,6 +13,9 @@ Three legs, each timed over exactly K steps bracketed by torch.cuda.synchronize(
            outside the timed launch.
   gdp:     gated delta product, 2 Householder sub-steps, B=1, T=65536, H=32,
            K = V = 128, bf16, chunk 128 tokens; tokens/s.
+  gates:   the prefill and decode workloads again with g and beta given as raw
+           projections and formed inside the kernels (A_log, dt_bias); kernel
+           times and their ratio to the legs above.
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -42,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,gdp")
+    ap.add_argument("--legs", default="prefill,decode,gdp,gates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -223,15 +226,16 @@ def run_prefill_leg(wl, steps, warmup):
     out = torch.empty((wl.q.shape[0], wl.q.shape[1], wl.v.shape[-2], wl.v.shape[-1]),
                       dtype=torch.bfloat16, device="cuda")
     fs = torch.empty_like(h0) if idx is None else h0
+    gate = dict(A_log=up(wl.A_log), dt_bias=up(wl.dt_bias))   # None unless raw gates
     # one checked call through the Python binding, then the same C call with the
     # argument struct built once, so the timed launches carry no Python marshalling
     gdr.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                chunk_size=wl.chunk_size, initial_state=h0,
                                output_final_state=True, cu_seqlens=cu, state_indices=idx,
-                               out=out, final_state=fs)
+                               out=out, final_state=fs, **gate)
     args = gdr.prefill_args(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=wl.chunk_size,
                             initial_state=h0, final_state=fs, cu_seqlens=cu,
-                            state_indices=idx, out=out)
+                            state_indices=idx, out=out, **gate)
     lib = gdr.library()
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -240,6 +244,32 @@ def run_prefill_leg(wl, steps, warmup):
         assert rc == 0, rc
 
     wall, kern = time_launches(launch, steps, warmup)
+    return wall, kern
+
+
+def run_decode_leg(wl3, steps, warmup):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    d = [up(x) for x in (wl3.q, wl3.k, wl3.v, wl3.g, wl3.beta)]
+    cache = up(wl3.cache)
+    idx = up(wl3.batch_indices)
+    gate = dict(A_log=up(wl3.A_log), dt_bias=up(wl3.dt_bias))   # None unless raw gates
+    out = torch.empty((wl3.q.shape[0], wl3.v.shape[1], wl3.v.shape[2]),
+                      dtype=torch.bfloat16, device="cuda")
+    # 1 GiB read before each launch evicts the 256 MB last-level cache without
+    # leaving dirty lines to be written back during the timed launch
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    gdr.ssm_decode(*d, cache, batch_indices=idx, out=out, **gate)
+    dargs = gdr.decode_args(*d, cache, batch_indices=idx, out=out, **gate)
+    lib = gdr.library()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch_dec():
+        rc = lib.gdr_ssm_decode(dargs, stream)
+        assert rc == 0, rc
+
+    wall, kern = time_launches(launch_dec, steps, warmup, before=lambda: flush.sum())
+    del cache, flush
     return wall, kern
 
 
@@ -310,32 +340,13 @@ def main():
     # ---- decode ------------------------------------------------------------------------
     if "decode" in legs:
         wl3 = W.config3()
-        d = [up(x) for x in (wl3.q, wl3.k, wl3.v, wl3.g, wl3.beta)]
-        cache = up(wl3.cache)
-        idx = up(wl3.batch_indices)
-        out = torch.empty((wl3.q.shape[0], wl3.v.shape[1], wl3.v.shape[2]),
-                          dtype=torch.bfloat16, device="cuda")
-        # 1 GiB read before each launch evicts the 256 MB last-level cache without
-        # leaving dirty lines to be written back during the timed launch
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        gdr.ssm_decode(*d, cache, batch_indices=idx, out=out)
-        dargs = gdr.decode_args(*d, cache, batch_indices=idx, out=out)
-        lib = gdr.library()
-        stream = torch.cuda.current_stream().cuda_stream
-
-        def launch_dec():
-            rc = lib.gdr_ssm_decode(dargs, stream)
-            assert rc == 0, rc
-
-        wall, kern = time_launches(launch_dec, args.steps, args.warmup,
-                                   before=lambda: flush.sum())
+        wall, kern = run_decode_leg(wl3, args.steps, args.warmup)
         n_real = int((wl3.batch_indices >= 0).sum())
         Hv, K, V = wl3.cache.shape[1:]
         state_bytes = 2 * n_real * Hv * K * V * 4
         res["decode"] = dict(wall_ms=wall, kernel_ms=kern, state_bytes=state_bytes,
                              workload=wl3.name, n_real=n_real)
         print(f"[bench] decode: kernel {kern:.4f} ms", file=sys.stderr, flush=True)
-        del cache, flush
 
     # ---- gated delta product, long context ----------------------------------------------
     if "gdp" in legs:
@@ -347,6 +358,23 @@ def main():
                           flops=F * wl4.tokens, flops_per_token=F, workload=wl4.name)
         print(f"[bench] gdp: kernel {kern:.3f} ms", file=sys.stderr, flush=True)
         del wl4
+
+    # ---- gates formed in the kernels from raw projections (same workloads) --------------
+    if "gates" in legs:
+        gw2 = W.with_raw_gates(wl2, 2)
+        _, kp = run_prefill_leg(gw2, args.steps, args.warmup)
+        gw3 = W.with_raw_gates(W.config3(), 3)
+        _, kd = run_decode_leg(gw3, args.steps, args.warmup)
+        res["gates"] = {"prefill_kernel_ms": kp, "decode_kernel_ms": kd,
+                        "note": "packed prefill and decode workloads with g, beta formed in "
+                                "the kernels from raw projections (A_log, dt_bias)"}
+        if "prefill" in res:
+            res["gates"]["prefill_vs_formed"] = kp / res["prefill"]["kernel_ms"]
+        if "decode" in res:
+            res["gates"]["decode_vs_formed"] = kd / res["decode"]["kernel_ms"]
+        print(f"[bench] fused gates: prefill {kp:.3f} ms, decode {kd:.4f} ms", file=sys.stderr,
+              flush=True)
+        del gw2, gw3
 
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ------------
     cpu = None
@@ -429,6 +457,8 @@ def main():
                                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
                        "mfma": {"flops_per_token": gg["flops_per_token"],
                                 "achieved_tflops": tf, "frac": tf / MFMA_PEAK_TFLOPS}}
+    if "gates" in res:
+        line["fused_gates"] = res["gates"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["bench_wall_s"] = time.perf_counter() - t_start

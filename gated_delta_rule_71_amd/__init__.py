@@ -13,6 +13,12 @@ The signature of chunk_gated_delta_rule follows torch_chunk_gated_delta_rule on
 the Megatron Core API page "core.ssm.gated_delta_net.gdn" (extra keyword
 arguments are accepted and ignored there too); ssm_decode follows ssm_decode on
 the pages "core.ssm.gated_delta_net.gdn" / "core.ssm.gated_delta_product".
+
+Both take the gates either formed (g, beta) or, with ``A_log`` and ``dt_bias``
+([Hv] float32) given, as the raw per-token projections (g holds alpha, beta holds
+the logits b); the kernels then form g = -exp(A_log) softplus(alpha + dt_bias)
+and beta = sigmoid(b) themselves (GatedDeltaNet._compute_gates, page
+"core.ssm.gated_delta_net.gdn").
 """
 from __future__ import annotations
 
@@ -79,9 +85,22 @@ def _raise(code, what):
         raise RuntimeError(f"{what} failed: {_lib.status_string(code)}")
 
 
+def _gate_params(A_log, dt_bias, Hv, torch):
+    """gate_mode and the [Hv] parameter tensors (both or neither must be given)."""
+    if A_log is None and dt_bias is None:
+        return 0, None, None
+    if A_log is None or dt_bias is None:
+        raise ValueError("A_log and dt_bias go together (raw gate projections)")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _check(t, name, dtype=torch.float32, ndim=1)
+        if t.numel() != Hv:
+            raise ValueError(f"{name} needs one entry per value head ({Hv})")
+    return 1, A_log, dt_bias
+
+
 def prefill_args(q, k, v, g, beta, *, scale=None, chunk_size=64, initial_state=None,
                  final_state=None, use_qk_l2norm_in_kernel=False, cu_seqlens=None,
-                 state_indices=None, out=None):
+                 state_indices=None, out=None, A_log=None, dt_bias=None):
     """Fill a gdr_prefill_args struct from tensors (no checks beyond shapes)."""
     B, T, Hk, K = q.shape
     n_h = k.shape[2] if k.dim() == 5 else 1
@@ -107,13 +126,16 @@ def prefill_args(q, k, v, g, beta, *, scale=None, chunk_size=64, initial_state=N
     a.out = _ptr(out)
     a.workspace = None
     a.workspace_bytes = 0
+    a.gate_mode = 0 if A_log is None else 1
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     return a
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None,
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            cu_seqlens=None, *, state_indices=None, out_dtype=None, out=None,
-                           final_state=None, stream=None, **kwargs):
+                           final_state=None, stream=None, A_log=None, dt_bias=None,
+                           **kwargs):
     """Chunked prefill of the gated delta rule (packed or batched sequences).
 
     q [B,T,Hk,K]; k [B,T,Hk,K] or [B,T,n_h,Hk,K]; v [B,T,Hv,V] or [B,T,n_h,Hv,V]
@@ -122,6 +144,8 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     initial_state float32 [N,Hv,K,V]; with ``state_indices`` (int32 [N]) it is a
     slot cache [slots,Hv,K,V], read at max(idx, 0) and written back in place at
     idx >= 0 (or into ``final_state`` if given).
+    With ``A_log`` and ``dt_bias`` ([Hv] float32), g and beta are the raw gate
+    projections alpha and b, and the kernel forms the gates.
     Returns (o [B,T,Hv,V], final_state or None).
     """
     torch = _torch()
@@ -134,6 +158,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     B, T, Hk, K = q.shape
     n_h = k.shape[2] if k.dim() == 5 else 1
     Hv, V = v.shape[-2], v.shape[-1]
+    _gate_params(A_log, dt_bias, Hv, torch)
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
@@ -158,14 +183,14 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     a = prefill_args(q, k, v, g, beta, scale=scale, chunk_size=chunk_size,
                      initial_state=initial_state, final_state=final_state,
                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
-                     state_indices=state_indices, out=out)
+                     state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias)
     _raise(lib.gdr_chunk_gated_delta_rule(a, _stream(stream)), "gdr_chunk_gated_delta_rule")
     ret_state = final_state if (output_final_state or state_indices is not None) else None
     return out, ret_state
 
 
 def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,
-                use_qk_l2norm_in_kernel=False, out=None):
+                use_qk_l2norm_in_kernel=False, out=None, A_log=None, dt_bias=None):
     n, Hk, K = q.shape
     n_h = k.shape[1] if k.dim() == 4 else 1
     Hv, V = v.shape[-2], v.shape[-1]
@@ -181,16 +206,21 @@ def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,
     a.state = _ptr(ssm_state)
     a.batch_indices = _ptr(batch_indices)
     a.out = _ptr(out)
+    a.gate_mode = 0 if A_log is None else 1
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     return a
 
 
 def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
-               use_qk_l2norm_in_kernel=False, *, out_dtype=None, out=None, stream=None):
+               use_qk_l2norm_in_kernel=False, *, out_dtype=None, out=None, stream=None,
+               A_log=None, dt_bias=None):
     """One decode token per request, updating ``ssm_state`` [slots,Hv,K,V] in place.
 
     q [n,Hk,K]; k [n,Hk,K] or [n,n_h,Hk,K]; v [n,Hv,V] or [n,n_h,Hv,V];
     g [n,Hv]; beta [n,Hv] or [n,n_h,Hv] (float32); batch_indices int32 [n]
     (-1: padding, reads slot 0, writes nothing) or None (request i <-> slot i).
+    With ``A_log`` and ``dt_bias`` ([Hv] float32), g and beta are the raw gate
+    projections alpha and b, and the kernel forms the gates.
     Returns o [n,Hv,V].
     """
     torch = _torch()
@@ -205,13 +235,15 @@ def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
         _check(batch_indices, "batch_indices", dtype=torch.int32, ndim=1)
     n = q.shape[0]
     Hv, V = v.shape[-2], v.shape[-1]
+    _gate_params(A_log, dt_bias, Hv, torch)
     if out is None:
         od = v.dtype if out_dtype is None else out_dtype
         out = torch.empty((n, Hv, V), dtype=od, device=q.device)
     else:
         _check(out, "out", ndim=3)
     a = decode_args(q, k, v, g, beta, ssm_state, batch_indices=batch_indices, scale=scale,
-                    use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, out=out)
+                    use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, out=out, A_log=A_log,
+                    dt_bias=dt_bias)
     _raise(lib.gdr_ssm_decode(a, _stream(stream)), "gdr_ssm_decode")
     return out
 

@@ -18,6 +18,7 @@ GDR_ERR_WORKSPACE = 3
 GDR_ERR_HIP = 4
 GDR_DTYPE_F32 = 0
 GDR_DTYPE_BF16 = 1
+ABI_VERSION = 2   # GDR_ABI_VERSION the structures below are laid out for
 
 # Every symbol include/gdr.h declares.
 EXPORTS = (
@@ -60,6 +61,9 @@ class PrefillArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("gate_mode", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -85,6 +89,9 @@ class DecodeArgs(ctypes.Structure):
         ("state", ctypes.c_void_p),
         ("batch_indices", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
+        ("gate_mode", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -117,6 +124,9 @@ def load(path: str = LIB_PATH):
         lib.gdr_chunk_gated_delta_rule.restype = ctypes.c_int
         lib.gdr_ssm_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
         lib.gdr_ssm_decode.restype = ctypes.c_int
+        if lib.gdr_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{path} has ABI version {lib.gdr_abi_version()}, the bindings "
+                               f"expect {ABI_VERSION}: rebuild it")
         if path == LIB_PATH:
             _lib = lib
         return lib

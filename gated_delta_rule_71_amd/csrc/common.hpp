@@ -196,6 +196,23 @@ template <> struct Mma<true> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// ---- gates from raw projections ----------------------------------------------
+// GatedDeltaNet._compute_gates (page "core.ssm.gated_delta_net.gdn") turns the
+// per-token projections alpha and b into the gates with the per-head parameters
+// A_log and dt_bias; read as the softplus time-step parametrisation those names
+// denote:  g = -exp(A_log) softplus(alpha + dt_bias),  beta = sigmoid(b).
+// Evaluated in float32 with the library's correctly rounded-to-1-ulp expf and
+// log1pf (softplus split at 0, so that exp never overflows); a float32 g carries
+// the same information as a float32 g given as input.
+__device__ __forceinline__ float softplus_f32(float x) {
+  return x > 0.0f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+// g from the raw decay projection; A = exp(A_log[h]) is passed precomputed
+__device__ __forceinline__ float gate_decay(float alpha, float A, float dt_bias) {
+  return -A * softplus_f32(alpha + dt_bias);
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
 // element e of a fragment, from a float
 __device__ __forceinline__ void set_frag(Mma<false>::frag &f, int e, float x) {
   f.v[e] = static_cast<_Float16>(x);

@@ -131,7 +131,21 @@ decode_kernel(const DecodeParams p) {
   __syncthreads();
 
   // per-column step (every thread, for its own 4 columns)
-  const float alpha = expf(p.g[static_cast<size_t>(i) * p.Hv + h]);
+  // the gates (formed here from the raw projections when gate_mode is set)
+  float alpha, bet[NH];
+  {
+    const float gin = p.g[static_cast<size_t>(i) * p.Hv + h];
+    if (p.gate_mode) {
+      alpha = expf(gate_decay(gin, expf(p.A_log[h]), p.dt_bias[h]));
+    } else {
+      alpha = expf(gin);
+    }
+#pragma unroll
+    for (int s = 0; s < NH; ++s) {
+      const float b = p.beta[(static_cast<size_t>(i) * NH + s) * p.Hv + h];
+      bet[s] = p.gate_mode ? gate_beta(b) : b;
+    }
+  }
   const TIn *vg = static_cast<const TIn *>(p.v);
   float dlt[NH][4];
   float out[4];
@@ -154,7 +168,7 @@ decode_kernel(const DecodeParams p) {
       for (int s2 = 0; s2 < s; ++s2) u += dots[s2 * NV + s] * dlt[s2][c];
       const size_t row = static_cast<size_t>(i) * NH + s;
       const float vv = load_f32(vg + (row * p.Hv + h) * DV + col);
-      dlt[s][c] = p.beta[row * p.Hv + h] * (vv - u);
+      dlt[s][c] = bet[s] * (vv - u);
       o += dots[s * NV + NH] * dlt[s][c];
     }
     out[c] = p.scale * o;

@@ -45,6 +45,7 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
   if (!dtype_ok(a->qkv_dtype) || !dtype_ok(a->out_dtype)) return GDR_ERR_INVALID_ARG;
   if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
   if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (a->gate_mode != 0 && a->gate_mode != 1) return GDR_ERR_INVALID_ARG;
   if (a->cu_seqlens) {
     if (a->batch != 1) return GDR_ERR_INVALID_ARG;
   } else if (a->num_seqs != a->batch) {
@@ -67,6 +68,7 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
     return GDR_ERR_UNSUPPORTED;
   if (tokens > 0) {
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out) return GDR_ERR_INVALID_ARG;
+    if (a->gate_mode == 1 && (!a->A_log || !a->dt_bias)) return GDR_ERR_INVALID_ARG;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
       return GDR_ERR_INVALID_ARG;
   }
@@ -85,9 +87,11 @@ int gdr_validate_decode(const gdr_decode_args *a) {
   if (!dtype_ok(a->qkv_dtype) || !dtype_ok(a->out_dtype)) return GDR_ERR_INVALID_ARG;
   if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
   if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (a->gate_mode != 0 && a->gate_mode != 1) return GDR_ERR_INVALID_ARG;
   if (!head_ok(a->head_k) || !head_ok(a->head_v)) return GDR_ERR_UNSUPPORTED;
   if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
   if (a->batch > 0) {
+    if (a->gate_mode == 1 && (!a->A_log || !a->dt_bias)) return GDR_ERR_INVALID_ARG;
     if (a->num_slots <= 0) return GDR_ERR_INVALID_ARG;
     if (!a->batch_indices && a->batch > a->num_slots) return GDR_ERR_INVALID_ARG;
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->state || !a->out)
@@ -130,6 +134,9 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.l2norm = a->use_qk_l2norm;
   p.out_bf16 = a->out_dtype == GDR_DTYPE_BF16;
   p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
+  p.gate_mode = a->gate_mode;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
   const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
   const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
   const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, state_waves,
@@ -156,6 +163,9 @@ int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
   p.l2norm = a->use_qk_l2norm;
   p.out_bf16 = a->out_dtype == GDR_DTYPE_BF16;
   p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
+  p.gate_mode = a->gate_mode;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
   const hipError_t e = gdr::launch_decode(p, a->qkv_dtype == GDR_DTYPE_F32, a->head_k,
                                           a->head_v, a->num_householder,
                                           static_cast<hipStream_t>(stream));

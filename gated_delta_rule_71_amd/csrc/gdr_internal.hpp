@@ -28,6 +28,9 @@ struct PrefillParams {
   int l2norm;
   int out_bf16;
   float scale;
+  int gate_mode;                 // 1: g, beta hold raw projections (gates computed here)
+  const float *A_log;            // [Hv] (gate_mode 1)
+  const float *dt_bias;          // [Hv] (gate_mode 1)
 };
 
 struct DecodeParams {
@@ -45,6 +48,9 @@ struct DecodeParams {
   int l2norm;
   int out_bf16;
   float scale;
+  int gate_mode;
+  const float *A_log;
+  const float *dt_bias;
 };
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).

@@ -471,6 +471,12 @@ prefill_kernel(const PrefillParams p) {
   const TIn *__restrict__ vrow = static_cast<const TIn *>(p.v) + h * p.DV + vt * DVT;
   const float *__restrict__ gb = p.g + h;
   const float *__restrict__ bb = p.beta + h;
+  // gate parameters of this value head when g and beta hold raw projections
+  float gate_A = 0.0f, gate_dt = 0.0f;
+  if (p.gate_mode) {
+    gate_A = expf(p.A_log[h]);
+    gate_dt = p.dt_bias[h];
+  }
   TOut *__restrict__ ob = static_cast<TOut *>(p.out) + h * p.DV + col0;   // + token, lane
   const uint32_t kstride = p.Hk * DK;        // elements between key rows (and query rows)
   const uint32_t vstride = p.Hv * p.DV;      // elements between value / output rows
@@ -622,9 +628,16 @@ prefill_kernel(const PrefillParams p) {
     }
     if (pw == 3) {
       // inclusive prefix sum of the per-row decay, in fp64, and per-row factors
+      // (the gates are formed here first when g and beta hold raw projections)
       const bool ok = lane < nrow;
-      const double gr = prefix_sum32((ok && (cr.c + lane) % NH == 0) ? cr.g : 0.0);
-      const float bv = ok ? cr.b : 0.0f;
+      float gv = cr.g;
+      float bv = cr.b;
+      if (p.gate_mode) {
+        gv = gate_decay(cr.g, gate_A, gate_dt);
+        bv = gate_beta(cr.b);
+      }
+      const double gr = prefix_sum32((ok && (cr.c + lane) % NH == 0) ? gv : 0.0);
+      bv = ok ? bv : 0.0f;
       const double glast = readlane_f64(gr, CR - 1);
       if (lane < CR) {
         s.G[lane] = gr;

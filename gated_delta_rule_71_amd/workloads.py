@@ -18,7 +18,12 @@ given per workload, draw order fixed as written below):
     "core.ssm.gated_delta_net.gdn" and "core.ssm.gated_delta_product");
     decay variants "slow" (g ~ -U(0, 0.05)) and "zero" (g = 0) exist so that
     state carried across chunks is not forgotten within one chunk;
-  * states ~ N(0, 0.1) in float32 where a workload asks for a random state.
+  * states ~ N(0, 0.1) in float32 where a workload asks for a random state;
+  * raw gate inputs (:func:`with_raw_gates`, for kernels that form the gates):
+    alpha, b ~ N(0, 1) per (token, [sub-step,] head) in place of g and beta,
+    A_log_h = log(A_h) with A_h ~ U(1, 16) and dt_bias_h = log(expm1(dt_h)) with
+    dt_h ~ U(0.001, 0.1) (the inverse softplus of the time step), so that the
+    gates they define follow the distribution above.
 bf16 tensors are rounded from float32 with round-to-nearest-even and stored as
 uint16 bit patterns; :func:`as_f64` gives the exact values both sides compute on.
 """
@@ -115,6 +120,8 @@ class PrefillWorkload:
     state_indices: Optional[np.ndarray] = None   # int32 [N]
     output_final_state: bool = True
     meta: dict = field(default_factory=dict)
+    A_log: Optional[np.ndarray] = None           # float32 [Hv]: g, beta are raw projections
+    dt_bias: Optional[np.ndarray] = None         # float32 [Hv]
 
     @property
     def shape(self):
@@ -142,6 +149,22 @@ class DecodeWorkload:
     cache: np.ndarray               # [slots,Hv,K,V] float32
     batch_indices: Optional[np.ndarray]  # int32 [n] (-1 = padding)
     meta: dict = field(default_factory=dict)
+    A_log: Optional[np.ndarray] = None           # float32 [Hv]: g, beta are raw projections
+    dt_bias: Optional[np.ndarray] = None         # float32 [Hv]
+
+
+def with_raw_gates(wl, seed):
+    """A copy of a prefill or decode workload whose g and beta are replaced by raw
+    gate projections (alpha, b) and per-head A_log, dt_bias (see the recipe above)."""
+    from dataclasses import replace
+    rng = np.random.default_rng([seed, 0x6A7E])
+    Hv = wl.g.shape[-1]
+    A_log = np.log(rng.uniform(1.0, 16.0, size=Hv)).astype(np.float32)
+    dt_bias = np.log(np.expm1(rng.uniform(0.001, 0.1, size=Hv))).astype(np.float32)
+    alpha = rng.standard_normal(wl.g.shape, dtype=np.float32)
+    b = rng.standard_normal(wl.beta.shape, dtype=np.float32)
+    return replace(wl, name=wl.name + "_rawgates", g=alpha, beta=b, A_log=A_log,
+                   dt_bias=dt_bias)
 
 
 # ---- the measured workloads ---------------------------------------------------------

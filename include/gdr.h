@@ -19,6 +19,21 @@
  *    matrix holding S transposed: element [i][j] is S[j][i].
  *  - Value head h reads query/key head floor(h * Hk / Hv) (Hv a multiple of Hk).
  *  - q/k/v share one input dtype; g, beta and all states are float32.
+ *  - Gates (gate_mode): with gate_mode 0 the g and beta arguments hold the gates
+ *    themselves, the per-token log-decay g_t and the write strength beta_t.  With
+ *    gate_mode 1 they hold the raw per-token projections the gates are computed
+ *    from inside the kernels (the "alpha" and "beta" outputs of the fused input
+ *    projection, GatedDeltaNet.forward_pre_attn_and_core_attn and
+ *    _prepare_inference_inputs on page "core.ssm.gated_delta_net.gdn", which leave
+ *    the gates to the kernel), together with the per-value-head parameters A_log
+ *    and dt_bias of GatedDeltaNet._compute_gates:
+ *        g_t    = -exp(A_log[h]) * softplus(alpha_t + dt_bias[h]),
+ *        beta_t = sigmoid(b_t),      softplus(x) = log(1 + exp(x)).
+ *    The pages name the parameters (A_log, dt_bias; A_init_range, dt_min, dt_max
+ *    on page "core.ssm.gated_delta_product") but print no formula; this is the
+ *    decay parametrisation those names denote (A = exp(A_log) > 0 times a
+ *    softplus time step).  The gates are evaluated in float32 (the library's
+ *    expf / log1pf; softplus split at 0 so that exp never overflows).
  *  - Calls only enqueue work on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream).  They never allocate, free or synchronise, keep no
  *    mutable global state, and their launch shapes depend only on the sizes in
@@ -40,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 typedef enum {
@@ -119,6 +134,9 @@ typedef struct {
   void *out;
   void *workspace;          /* device memory of workspace_bytes (may be NULL if 0)  */
   size_t workspace_bytes;
+  int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections (above) */
+  const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
+  const float *dt_bias;     /* [Hv] float32, gate_mode 1 only (else ignored)        */
 } gdr_prefill_args;
 
 /*
@@ -155,6 +173,9 @@ typedef struct {
   float *state;
   const int32_t *batch_indices;
   void *out;
+  int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections (above) */
+  const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
+  const float *dt_bias;     /* [Hv] float32, gate_mode 1 only (else ignored)        */
 } gdr_decode_args;
 
 /* Version of this ABI (GDR_ABI_VERSION). */

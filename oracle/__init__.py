@@ -12,6 +12,8 @@ Two independent CPU evaluations of the recurrence, both in fp64:
 * :func:`oracle.chunked.chunked_prefill` — the chunked (WY / UT transform)
   evaluation written with NumPy, used to check that chunking leaves the result
   unchanged for any chunk size.
+* :func:`gates` (``oracle/gating.py``) — the gates g and beta from the raw
+  per-token projections and the per-head parameters A_log and dt_bias.
 
 The recurrence is the gated delta rule named on the Megatron Core API page
 "core.ssm.gated_delta_net.gdn" (function torch_chunk_gated_delta_rule) and, with
@@ -26,6 +28,8 @@ import subprocess
 import threading
 
 import numpy as np
+
+from .gating import gates  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr_oracle.c")

@@ -77,6 +77,15 @@ def to_host(t):
 
 # ---- oracle on a workload -------------------------------------------------------------
 
+def gate_values(wl):
+    """(g, beta) float64 the oracle runs on: the workload's own, or the oracle's gates
+    of its raw projections when it carries A_log / dt_bias."""
+    if getattr(wl, "A_log", None) is None:
+        return np.asarray(wl.g, dtype=np.float64), np.asarray(wl.beta, dtype=np.float64)
+    import oracle
+    return oracle.gates(wl.g, wl.beta, wl.A_log, wl.dt_bias)
+
+
 def oracle_prefill(wl: W.PrefillWorkload, *, seqs=None, heads=None, use_qk_l2norm=False,
                    scale=None, threads=0):
     """fp64 oracle on (a sample of) a prefill workload.
@@ -98,7 +107,8 @@ def oracle_prefill(wl: W.PrefillWorkload, *, seqs=None, heads=None, use_qk_l2nor
     qf = wl.q
     kf = wl.k.reshape(B, T, n_h, Hk, K)
     vf = wl.v.reshape(B, T, n_h, Hv, V)
-    bf = wl.beta.reshape(B, T, n_h, Hv)
+    gv, bv = gate_values(wl)
+    bf = bv.reshape(B, T, n_h, Hv)
     res = {}
     jobs = []
     for n in seqs:
@@ -117,7 +127,7 @@ def oracle_prefill(wl: W.PrefillWorkload, *, seqs=None, heads=None, use_qk_l2nor
         q = W.as_f64(qf[b:b + 1, t0:t1, hk:hk + 1])
         k = W.as_f64(kf[b:b + 1, t0:t1, :, hk:hk + 1])
         v = W.as_f64(vf[b:b + 1, t0:t1, :, h:h + 1])
-        g = np.asarray(wl.g[b:b + 1, t0:t1, h:h + 1], dtype=np.float64)
+        g = gv[b:b + 1, t0:t1, h:h + 1]
         be = np.asarray(bf[b:b + 1, t0:t1, :, h:h + 1], dtype=np.float64)
         o, fs = oracle.prefill(q, k, v, g, be, scale=scale, initial_state=s0,
                                output_final_state=True, use_qk_l2norm=use_qk_l2norm,
@@ -144,7 +154,8 @@ def oracle_prefill_batch(wl: W.PrefillWorkload, pairs, *, use_qk_l2norm=False, s
         spans = [(0, int(wl.cu_seqlens[i]), int(wl.cu_seqlens[i + 1])) for i in range(N)]
     kf = wl.k.reshape(B, T, n_h, Hk, K)
     vf = wl.v.reshape(B, T, n_h, Hv, V)
-    bf = wl.beta.reshape(B, T, n_h, Hv)
+    gv, bv = gate_values(wl)
+    bf = bv.reshape(B, T, n_h, Hv)
     qs, ks, vs, gs, bs, s0s, lens = [], [], [], [], [], [], []
     for (n, h) in pairs:
         b, t0, t1 = spans[n]
@@ -152,7 +163,7 @@ def oracle_prefill_batch(wl: W.PrefillWorkload, pairs, *, use_qk_l2norm=False, s
         qs.append(W.as_f64(wl.q[b, t0:t1, hk:hk + 1]))
         ks.append(W.as_f64(kf[b, t0:t1, :, hk:hk + 1]))
         vs.append(W.as_f64(vf[b, t0:t1, :, h:h + 1]))
-        gs.append(np.asarray(wl.g[b, t0:t1, h:h + 1], dtype=np.float64))
+        gs.append(gv[b, t0:t1, h:h + 1])
         bs.append(np.asarray(bf[b, t0:t1, :, h:h + 1], dtype=np.float64))
         if wl.initial_state is None:
             s0s.append(np.zeros((1, K, V)))
@@ -189,10 +200,12 @@ def gpu_prefill(wl: W.PrefillWorkload, *, out_dtype=None, chunk_size=None, use_q
     idx = None if wl.state_indices is None else to_dev(wl.state_indices)
     h0 = None if wl.initial_state is None else to_dev(wl.initial_state)
     od = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    A_log = to_dev(getattr(wl, "A_log", None))
+    dt_bias = to_dev(getattr(wl, "dt_bias", None))
     o, fs = gdr.chunk_gated_delta_rule(
         dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], scale=scale,
         chunk_size=chunk_size or wl.chunk_size, initial_state=h0, output_final_state=True,
         use_qk_l2norm_in_kernel=use_qk_l2norm, cu_seqlens=cu, state_indices=idx,
-        out_dtype=od)
+        out_dtype=od, A_log=A_log, dt_bias=dt_bias)
     torch.cuda.synchronize()
     return o, fs, dev

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == _lib.ABI_VERSION == 2
     for code, name in [(0, "GDR_OK"), (1, "GDR_ERR_INVALID_ARG"), (2, "GDR_ERR_UNSUPPORTED"),
                        (3, "GDR_ERR_WORKSPACE"), (4, "GDR_ERR_HIP"), (99, "GDR_ERR_UNKNOWN")]:
         assert lib.gdr_status_string(code).decode() == name
@@ -90,6 +90,11 @@ def _decode(**kw):
     (dict(seqlen=1 << 30, batch=2, num_seqs=2), 2),  # beyond the row limit
     (dict(seqlen=1 << 23, batch=1, num_seqs=1), 2),  # offsets past 2^32 elements
     (dict(seqlen=(1 << 23) - 64, batch=1, num_seqs=1, num_v_heads=2), 0),
+    (dict(gate_mode=2), 1),                          # gate modes are 0 and 1
+    (dict(gate_mode=1), 1),                          # raw gates need A_log and dt_bias
+    (dict(gate_mode=1, A_log=FAKE), 1),
+    (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE), 0),
+    (dict(gate_mode=0, A_log=FAKE), 0),              # ignored without gate_mode
 ])
 def test_validate_prefill(lib, kw, code):
     a = _prefill(**kw)
@@ -109,6 +114,9 @@ def test_validate_prefill(lib, kw, code):
     (dict(batch=0, q=None, k=None, v=None, g=None, beta=None, state=None, out=None,
           num_slots=0), 0),
     (dict(scale=-math.inf), 1),
+    (dict(gate_mode=-1), 1),
+    (dict(gate_mode=1, dt_bias=FAKE), 1),
+    (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE), 0),
 ])
 def test_validate_decode(lib, kw, code):
     a = _decode(**kw)
