@@ -1,8 +1,9 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,gdp,gates]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--legs prefill,decode,gdp,gates,boundary]
 
-Four legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Five legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
@@ -16,6 +17,8 @@ Four legs, each timed over exactly K steps bracketed by torch.cuda.synchronize()
   gates:   the prefill and decode workloads again with g and beta given as raw
            projections and formed inside the kernels (A_log, dt_bias); kernel
            times and their ratio to the legs above.
+  boundary: the prefill again, also writing boundary states every 1024 and every
+           64 tokens (prefix caching); kernel times and bytes written.
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -45,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,gdp,gates")
+    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -216,7 +219,7 @@ def prefill_flops_per_token(wl, chunk_tokens):
     return Hv * ((4 * n_h + 2) * K * V + 2 * n_h * n_h * C * (2 * K + V) + 2 * n_h * C * (K + V))
 
 
-def run_prefill_leg(wl, steps, warmup):
+def run_prefill_leg(wl, steps, warmup, boundary_interval=None):
     import torch
     import gated_delta_rule_71_amd as gdr
     d = {n: up(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")}
@@ -227,6 +230,13 @@ def run_prefill_leg(wl, steps, warmup):
                       dtype=torch.bfloat16, device="cuda")
     fs = torch.empty_like(h0) if idx is None else h0
     gate = dict(A_log=up(wl.A_log), dt_bias=up(wl.dt_bias))   # None unless raw gates
+    if boundary_interval:
+        lens = np.diff(wl.cu_seqlens) if wl.cu_seqlens is not None else [wl.q.shape[1]] * \
+            wl.q.shape[0]
+        E = gdr.boundary_count(lens, boundary_interval)
+        gate.update(boundary_states=torch.empty((E,) + tuple(h0.shape[1:]), dtype=torch.float32,
+                                                device="cuda"),
+                    boundary_interval=boundary_interval)
     # one checked call through the Python binding, then the same C call with the
     # argument struct built once, so the timed launches carry no Python marshalling
     gdr.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
@@ -376,6 +386,21 @@ def main():
               flush=True)
         del gw2, gw3
 
+    # ---- boundary states (prefix caching) on the packed prefill ------------------------
+    if "boundary" in legs:
+        res["boundary"] = {"note": "packed prefill also writing each sequence's state every "
+                                   "`interval` tokens; bytes = entries x Hv x K x V x 4"}
+        for iv in (1024, 64):
+            _, kb = run_prefill_leg(wl2, args.steps, args.warmup, boundary_interval=iv)
+            E = sum(int(L) // iv for L in np.diff(wl2.cu_seqlens))
+            nbytes_b = E * int(np.prod(wl2.initial_state.shape[1:])) * 4
+            entry = {"kernel_ms": kb, "entries": E, "bytes": nbytes_b}
+            if "prefill" in res:
+                entry["vs_without"] = kb / res["prefill"]["kernel_ms"]
+            res["boundary"][f"interval_{iv}"] = entry
+            print(f"[bench] boundary states every {iv}: {kb:.3f} ms ({E} entries)",
+                  file=sys.stderr, flush=True)
+
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -459,6 +484,8 @@ def main():
                                 "achieved_tflops": tf, "frac": tf / MFMA_PEAK_TFLOPS}}
     if "gates" in res:
         line["fused_gates"] = res["gates"]
+    if "boundary" in res:
+        line["boundary_states"] = res["boundary"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["bench_wall_s"] = time.perf_counter() - t_start

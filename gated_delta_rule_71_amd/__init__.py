@@ -100,7 +100,8 @@ def _gate_params(A_log, dt_bias, Hv, torch):
 
 def prefill_args(q, k, v, g, beta, *, scale=None, chunk_size=64, initial_state=None,
                  final_state=None, use_qk_l2norm_in_kernel=False, cu_seqlens=None,
-                 state_indices=None, out=None, A_log=None, dt_bias=None):
+                 state_indices=None, out=None, A_log=None, dt_bias=None,
+                 boundary_states=None, boundary_interval=0):
     """Fill a gdr_prefill_args struct from tensors (no checks beyond shapes)."""
     B, T, Hk, K = q.shape
     n_h = k.shape[2] if k.dim() == 5 else 1
@@ -128,14 +129,21 @@ def prefill_args(q, k, v, g, beta, *, scale=None, chunk_size=64, initial_state=N
     a.workspace_bytes = 0
     a.gate_mode = 0 if A_log is None else 1
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.boundary_states = _ptr(boundary_states)
+    a.boundary_interval = int(boundary_interval or 0)
     return a
+
+
+def boundary_count(lengths, interval):
+    """Entries a prefill writes to ``boundary_states``: sum of floor(L_n / interval)."""
+    return int(sum(int(L) // int(interval) for L in lengths))
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None,
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            cu_seqlens=None, *, state_indices=None, out_dtype=None, out=None,
                            final_state=None, stream=None, A_log=None, dt_bias=None,
-                           **kwargs):
+                           boundary_states=None, boundary_interval=None, **kwargs):
     """Chunked prefill of the gated delta rule (packed or batched sequences).
 
     q [B,T,Hk,K]; k [B,T,Hk,K] or [B,T,n_h,Hk,K]; v [B,T,Hv,V] or [B,T,n_h,Hv,V]
@@ -146,6 +154,9 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     idx >= 0 (or into ``final_state`` if given).
     With ``A_log`` and ``dt_bias`` ([Hv] float32), g and beta are the raw gate
     projections alpha and b, and the kernel forms the gates.
+    ``boundary_states`` float32 [E,Hv,K,V] with ``boundary_interval`` (tokens, a
+    multiple of 64) receives each sequence's state after every whole multiple of
+    the interval, sequences in order (E = boundary_count(lengths, interval)).
     Returns (o [B,T,Hv,V], final_state or None).
     """
     torch = _torch()
@@ -172,9 +183,12 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
             final_state = initial_state
     elif output_final_state and final_state is None:
         final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=q.device)
-    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+    for name, st in (("initial_state", initial_state), ("final_state", final_state),
+                     ("boundary_states", boundary_states)):
         if st is not None:
             _check(st, name, dtype=torch.float32, ndim=4)
+    if (boundary_states is None) != (boundary_interval is None):
+        raise ValueError("boundary_states and boundary_interval go together")
     if out is None:
         od = v.dtype if out_dtype is None else out_dtype
         out = torch.empty((B, T, Hv, V), dtype=od, device=q.device)
@@ -183,7 +197,8 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     a = prefill_args(q, k, v, g, beta, scale=scale, chunk_size=chunk_size,
                      initial_state=initial_state, final_state=final_state,
                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
-                     state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias)
+                     state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias,
+                     boundary_states=boundary_states, boundary_interval=boundary_interval)
     _raise(lib.gdr_chunk_gated_delta_rule(a, _stream(stream)), "gdr_chunk_gated_delta_rule")
     ret_state = final_state if (output_final_state or state_indices is not None) else None
     return out, ret_state

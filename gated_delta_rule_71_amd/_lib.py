@@ -64,6 +64,8 @@ class PrefillArgs(ctypes.Structure):
         ("gate_mode", ctypes.c_int32),
         ("A_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p),
+        ("boundary_states", ctypes.c_void_p),
+        ("boundary_interval", ctypes.c_int32),
     ]
 
 

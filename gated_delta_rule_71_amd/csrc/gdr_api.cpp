@@ -75,6 +75,9 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
   if ((a->initial_state && !aligned16(a->initial_state)) ||
       (a->final_state && !aligned16(a->final_state)))
     return GDR_ERR_INVALID_ARG;
+  if (a->boundary_states && (!aligned16(a->boundary_states) || a->boundary_interval <= 0 ||
+                             a->boundary_interval % 64 != 0))
+    return GDR_ERR_INVALID_ARG;
   if (a->workspace_bytes < gdr_prefill_workspace_bytes(a)) return GDR_ERR_WORKSPACE;
   return GDR_OK;
 }
@@ -137,6 +140,8 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.gate_mode = a->gate_mode;
   p.A_log = a->A_log;
   p.dt_bias = a->dt_bias;
+  p.boundary_states = a->boundary_states;
+  p.boundary_interval = a->boundary_interval;
   const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
   const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
   const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, state_waves,

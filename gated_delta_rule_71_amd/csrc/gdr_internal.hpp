@@ -31,6 +31,8 @@ struct PrefillParams {
   int gate_mode;                 // 1: g, beta hold raw projections (gates computed here)
   const float *A_log;            // [Hv] (gate_mode 1)
   const float *dt_bias;          // [Hv] (gate_mode 1)
+  float *boundary_states;        // NULL, or [entries, Hv, K, V]
+  int boundary_interval;         // tokens between boundary states
 };
 
 struct DecodeParams {

@@ -458,6 +458,17 @@ prefill_kernel(const PrefillParams p) {
     t0 = n * p.seqlen;
     t1 = t0 + p.seqlen;
   }
+  // boundary states: rows between entries, and the first entry of this sequence
+  int bnd_rows = 0, bnd_base = 0;
+  if (p.boundary_states) {
+    const int iv = p.boundary_interval;
+    bnd_rows = iv * NH;
+    if (p.cu_seqlens) {
+      for (int m = 0; m < n; ++m) bnd_base += (p.cu_seqlens[m + 1] - p.cu_seqlens[m]) / iv;
+    } else {
+      bnd_base = n * (p.seqlen / iv);
+    }
+  }
   int src = n, dst = n;
   if (p.state_indices) {
     const int idx = p.state_indices[n];
@@ -513,6 +524,23 @@ prefill_kernel(const PrefillParams p) {
         for (int i = 0; i < 4; ++i)
           H[ct][m][i] = s0[static_cast<size_t>(16 * m + 4 * g4 + i) * p.DV + col0 + 16 * ct + l16];
   }
+
+  // this state wave's 32 columns of H -> a [K, V] state at s1 (uniform): each store
+  // is a uniform row pointer plus one per-lane offset, kept opaque so that the
+  // compiler does not precompute (and hold) 64 separate lane addresses
+  auto store_state = [&](float *s1) {
+    uint32_t lane_off = static_cast<uint32_t>(4 * g4 * p.DV + col0 + l16);
+    asm volatile("" : "+v"(lane_off));
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float *row = s1 + static_cast<size_t>(16 * m + i) * p.DV + 16 * ct;
+          row[lane_off] = H[ct][m][i];
+        }
+  };
 
   const int row_begin = t0 * NH, row_end = t1 * NH;
   const int nchunks = (row_end - row_begin + CR - 1) / CR;
@@ -822,6 +850,11 @@ prefill_kernel(const PrefillParams p) {
           store4(o + 16, o1);
         }
       }
+      // a boundary state after every bnd_rows rows (boundaries fall on chunk ends)
+      if (bnd_rows && ((ci + 1) * CR) % bnd_rows == 0 && (ci + 1) * CR <= row_end - row_begin) {
+        const int e = bnd_base + (ci + 1) * CR / bnd_rows - 1;
+        store_state(p.boundary_states + (static_cast<size_t>(e) * p.Hv + h) * state_stride);
+      }
       // the R operands of the next chunk (staged an interval ago; read past the end
       // of the sequence they are never used)
       load_r(sm.st[(ci + 1) % 3]);
@@ -849,16 +882,8 @@ prefill_kernel(const PrefillParams p) {
   }
 
   // ---- final state ---------------------------------------------------------------
-  if (is_state && p.final_state && dst >= 0) {
-    float *s1 = p.final_state + (static_cast<size_t>(dst) * p.Hv + h) * state_stride;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int m = 0; m < KM; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s1[static_cast<size_t>(16 * m + 4 * g4 + i) * p.DV + col0 + 16 * ct + l16] = H[ct][m][i];
-  }
+  if (is_state && p.final_state && dst >= 0)
+    store_state(p.final_state + (static_cast<size_t>(dst) * p.Hv + h) * state_stride);
 }
 
 // ---- dispatch --------------------------------------------------------------------

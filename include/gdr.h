@@ -102,6 +102,14 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
  * chunk_size: tokens per chunk, a power of two in [16, 256].  Chunking does not
  *   change the result beyond rounding; the kernels evaluate chunks of
  *   min(chunk_size * n_h, 32) rows (16 rows for float32 inputs with K = 128).
+ * boundary_states (optional, for prefix caching; the per-chunk states of page
+ *   "core.ssm.gated_delta_product", ssm_prefill): the state of every sequence
+ *   after each whole multiple of boundary_interval tokens from its start.
+ *   Sequence n of L_n tokens writes floor(L_n / boundary_interval) entries, at
+ *   rows off_n + j, off_n = sum over m < n of floor(L_m / boundary_interval);
+ *   entry j holds the state after the sequence's first (j + 1) * boundary_interval
+ *   tokens, in the [K, V] layout of final states.  E = sum of the counts.  Every
+ *   sequence writes its entries, padding sequences (state index -1) included.
  * Supported: K in {64, 128}, V in {64, 128}, n_h in {1, 2}, q/k/v F32 or BF16,
  *   out F32 or BF16, Tt * n_h < 2^31 - 1024 rows and
  *   Tt * n_h * max(Hk * K, Hv * V) < 2^32 (element offsets within q, k, v and out
@@ -137,6 +145,8 @@ typedef struct {
   int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections (above) */
   const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
   const float *dt_bias;     /* [Hv] float32, gate_mode 1 only (else ignored)        */
+  float *boundary_states;   /* [E, Hv, K, V] float32 or NULL (below)                */
+  int32_t boundary_interval; /* tokens, a positive multiple of 64 (boundary_states) */
 } gdr_prefill_args;
 
 /*

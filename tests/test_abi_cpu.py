@@ -95,6 +95,12 @@ def _decode(**kw):
     (dict(gate_mode=1, A_log=FAKE), 1),
     (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE), 0),
     (dict(gate_mode=0, A_log=FAKE), 0),              # ignored without gate_mode
+    (dict(boundary_states=FAKE, boundary_interval=64), 0),
+    (dict(boundary_states=FAKE, boundary_interval=1024), 0),
+    (dict(boundary_states=FAKE, boundary_interval=0), 1),
+    (dict(boundary_states=FAKE, boundary_interval=96), 1),   # multiples of 64 only
+    (dict(boundary_states=FAKE + 8, boundary_interval=64), 1),
+    (dict(boundary_interval=100), 0),                # ignored without boundary_states
 ])
 def test_validate_prefill(lib, kw, code):
     a = _prefill(**kw)
