@@ -205,9 +205,12 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
 
 
 def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,
-                use_qk_l2norm_in_kernel=False, out=None, A_log=None, dt_bias=None):
-    n, Hk, K = q.shape
-    n_h = k.shape[1] if k.dim() == 4 else 1
+                use_qk_l2norm_in_kernel=False, out=None, A_log=None, dt_bias=None,
+                intermediate_ssm_state=None):
+    multi = q.dim() == 4                     # [n, T, Hk, K]: several tokens per request
+    n, Hk, K = q.shape[0], q.shape[-2], q.shape[-1]
+    T = q.shape[1] if multi else 1
+    n_h = k.shape[-3] if k.dim() == (5 if multi else 4) else 1
     Hv, V = v.shape[-2], v.shape[-1]
     a = _lib.DecodeArgs()
     a.batch, a.num_qk_heads, a.num_v_heads, a.head_k, a.head_v = n, Hk, Hv, K, V
@@ -223,12 +226,14 @@ def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,
     a.out = _ptr(out)
     a.gate_mode = 0 if A_log is None else 1
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.num_tokens = T
+    a.intermediate_state = _ptr(intermediate_ssm_state)
     return a
 
 
 def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
                use_qk_l2norm_in_kernel=False, *, out_dtype=None, out=None, stream=None,
-               A_log=None, dt_bias=None):
+               A_log=None, dt_bias=None, intermediate_ssm_state=None):
     """One decode token per request, updating ``ssm_state`` [slots,Hv,K,V] in place.
 
     q [n,Hk,K]; k [n,Hk,K] or [n,n_h,Hk,K]; v [n,Hv,V] or [n,n_h,Hv,V];
@@ -236,29 +241,40 @@ def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
     (-1: padding, reads slot 0, writes nothing) or None (request i <-> slot i).
     With ``A_log`` and ``dt_bias`` ([Hv] float32), g and beta are the raw gate
     projections alpha and b, and the kernel forms the gates.
-    Returns o [n,Hv,V].
+    Several tokens per request: every tensor gains a token axis after the request
+    axis (q [n,T,Hk,K], k [n,T,(n_h,)Hk,K], v [n,T,(n_h,)Hv,V], g [n,T,Hv], beta
+    [n,T,(n_h,)Hv]); the state advances token by token and ``intermediate_ssm_state``
+    (float32 [n,T,Hv,K,V]) receives the state after each token.  Returns o
+    [n,Hv,V] ([n,T,Hv,V] for several tokens).
     """
     torch = _torch()
     lib = library()
-    _check(q, "q", ndim=3)
-    _check(k, "k", dtype=q.dtype, ndim=(3, 4))
-    _check(v, "v", dtype=q.dtype, ndim=(3, 4))
-    _check(g, "g", dtype=torch.float32, ndim=2)
-    _check(beta, "beta", dtype=torch.float32, ndim=(2, 3))
+    _check(q, "q", ndim=(3, 4))
+    t = 1 if q.dim() == 4 else 0            # extra token axis
+    _check(k, "k", dtype=q.dtype, ndim=(3 + t, 4 + t))
+    _check(v, "v", dtype=q.dtype, ndim=(3 + t, 4 + t))
+    _check(g, "g", dtype=torch.float32, ndim=2 + t)
+    _check(beta, "beta", dtype=torch.float32, ndim=(2 + t, 3 + t))
     _check(ssm_state, "ssm_state", dtype=torch.float32, ndim=4)
     if batch_indices is not None:
         _check(batch_indices, "batch_indices", dtype=torch.int32, ndim=1)
     n = q.shape[0]
     Hv, V = v.shape[-2], v.shape[-1]
     _gate_params(A_log, dt_bias, Hv, torch)
+    lead = (n, q.shape[1]) if t else (n,)
+    if intermediate_ssm_state is not None:
+        _check(intermediate_ssm_state, "intermediate_ssm_state", dtype=torch.float32, ndim=5)
+        if tuple(intermediate_ssm_state.shape) != (n, lead[-1] if t else 1, Hv,
+                                                   ssm_state.shape[2], V):
+            raise ValueError("intermediate_ssm_state must be [n, T, Hv, K, V]")
     if out is None:
         od = v.dtype if out_dtype is None else out_dtype
-        out = torch.empty((n, Hv, V), dtype=od, device=q.device)
+        out = torch.empty(lead + (Hv, V), dtype=od, device=q.device)
     else:
-        _check(out, "out", ndim=3)
+        _check(out, "out", ndim=3 + t)
     a = decode_args(q, k, v, g, beta, ssm_state, batch_indices=batch_indices, scale=scale,
                     use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, out=out, A_log=A_log,
-                    dt_bias=dt_bias)
+                    dt_bias=dt_bias, intermediate_ssm_state=intermediate_ssm_state)
     _raise(lib.gdr_ssm_decode(a, _stream(stream)), "gdr_ssm_decode")
     return out
 

@@ -94,6 +94,8 @@ class DecodeArgs(ctypes.Structure):
         ("gate_mode", ctypes.c_int32),
         ("A_log", ctypes.c_void_p),
         ("dt_bias", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32),
+        ("intermediate_state", ctypes.c_void_p),
     ]
 
 

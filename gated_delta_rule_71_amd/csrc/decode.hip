@@ -14,6 +14,8 @@
 //   u_s = alpha a_s + sum_{s'<s} (k_s'.k_s) d_s',  d_s = beta_s (v_s - u_s)
 //   o   = scale (alpha y + sum_s (k_s.q) d_s)
 //   H'  = alpha H + sum_s k_s d_s^T                        (same registers)
+// Several tokens per request repeat the step with H in registers; the slot is
+// read once and written once.
 //
 // Layout: one 256-thread workgroup per (request, value head).  Thread t owns four
 // adjacent value columns (16-byte accesses; a 128-column row is read by 32
@@ -52,7 +54,8 @@ decode_kernel(const DecodeParams p) {
 
   const int r = p.batch_indices ? p.batch_indices[i] : i;
   const int slot = r < 0 ? 0 : r;
-  float *st = p.state + (static_cast<size_t>(slot) * p.Hv + h) * (static_cast<size_t>(DK) * DV);
+  const size_t state_size = static_cast<size_t>(DK) * DV;
+  float *st = p.state + (static_cast<size_t>(slot) * p.Hv + h) * state_size;
 
   // issue the state reads first: they are the bulk of the traffic
   float4 Hr[RPT];
@@ -60,153 +63,166 @@ decode_kernel(const DecodeParams p) {
   for (int m = 0; m < RPT; ++m)
     Hr[m] = *reinterpret_cast<const float4 *>(st + static_cast<size_t>(rg + RG * m) * DV + 4 * cg);
 
-  // q and k rows (optionally L2-normalised) -> LDS
   const TIn *qg = static_cast<const TIn *>(p.q);
   const TIn *kg = static_cast<const TIn *>(p.k);
-  if (wave <= NH) {
-    const TIn *src = (wave < NH)
-        ? kg + ((static_cast<size_t>(i) * NH + wave) * p.Hk + hk) * DK
-        : qg + (static_cast<size_t>(i) * p.Hk + hk) * DK;
-    float x[DK / 64];
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DK / 64; ++e) {
-      x[e] = load_f32(src + lane + 64 * e);
-      ss += x[e] * x[e];
-    }
-    if (p.l2norm) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-      const float rn = 1.0f / sqrtf(ss + 1e-6f);
-#pragma unroll
-      for (int e = 0; e < DK / 64; ++e) x[e] *= rn;
-    }
-    float *dstv = (wave < NH) ? ks[wave] : qs;
-#pragma unroll
-    for (int e = 0; e < DK / 64; ++e) dstv[lane + 64 * e] = x[e];
-  }
-  __syncthreads();
-  // dot products among the sub-step keys and the query (one wave per product)
-  for (int d = wave; d < NV * NH; d += WAVES) {
-    const int s = d / NV, o = d % NV;   // k_s . (k_o or q when o == NH)
-    const float *b = (o < NH) ? ks[o] : qs;
-    float acc = 0.0f;
-    for (int e = lane; e < DK; e += 64) acc += ks[s][e] * b[e];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) dots[d] = acc;
-  }
-
-  // partial H^T x for x in {k_0.., q}: this thread's rows, its 4 columns
-  float part[NV][4];
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) part[v][c] = 0.0f;
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int row = rg + RG * m;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const float xv = (v < NH) ? ks[v][row] : qs[row];
-      part[v][0] += Hr[m].x * xv;
-      part[v][1] += Hr[m].y * xv;
-      part[v][2] += Hr[m].z * xv;
-      part[v][3] += Hr[m].w * xv;
-    }
-  }
-  // reduce over the row groups inside the wave (lanes CG apart)
-#pragma unroll
-  for (int off = CG; off < 64; off <<= 1)
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) part[v][c] += __shfl_xor(part[v][c], off);
-  if (lane < CG) {
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave][v][4 * cg + c] = part[v][c];
-  }
-  __syncthreads();
-
-  // per-column step (every thread, for its own 4 columns)
-  // the gates (formed here from the raw projections when gate_mode is set)
-  float alpha, bet[NH];
-  {
-    const float gin = p.g[static_cast<size_t>(i) * p.Hv + h];
-    if (p.gate_mode) {
-      alpha = expf(gate_decay(gin, expf(p.A_log[h]), p.dt_bias[h]));
-    } else {
-      alpha = expf(gin);
-    }
-#pragma unroll
-    for (int s = 0; s < NH; ++s) {
-      const float b = p.beta[(static_cast<size_t>(i) * NH + s) * p.Hv + h];
-      bet[s] = p.gate_mode ? gate_beta(b) : b;
-    }
-  }
   const TIn *vg = static_cast<const TIn *>(p.v);
-  float dlt[NH][4];
-  float out[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int col = 4 * cg + c;
-    float a[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) s += red[w][v][col];
-      a[v] = s;
-    }
-    float o = alpha * a[NH];
-#pragma unroll
-    for (int s = 0; s < NH; ++s) {
-      float u = alpha * a[s];
-#pragma unroll
-      for (int s2 = 0; s2 < s; ++s2) u += dots[s2 * NV + s] * dlt[s2][c];
-      const size_t row = static_cast<size_t>(i) * NH + s;
-      const float vv = load_f32(vg + (row * p.Hv + h) * DV + col);
-      dlt[s][c] = bet[s] * (vv - u);
-      o += dots[s * NV + NH] * dlt[s][c];
-    }
-    out[c] = p.scale * o;
-  }
-  if (rg == 0) {
-    const size_t off = (static_cast<size_t>(i) * p.Hv + h) * DV + 4 * cg;
-    if (p.out_bf16) {
-      uint16_t *op = static_cast<uint16_t *>(p.out) + off;
-      const uint2 pk = {static_cast<uint32_t>(f32_to_bf16(out[0])) |
-                            (static_cast<uint32_t>(f32_to_bf16(out[1])) << 16),
-                        static_cast<uint32_t>(f32_to_bf16(out[2])) |
-                            (static_cast<uint32_t>(f32_to_bf16(out[3])) << 16)};
-      *reinterpret_cast<uint2 *>(op) = pk;
-    } else {
-      *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + off) =
-          make_float4(out[0], out[1], out[2], out[3]);
-    }
-  }
-  if (r < 0) return;   // padding: no state write
+  const float gate_A = p.gate_mode ? expf(p.A_log[h]) : 0.0f;
 
+  // this thread's rows of H -> a [K, V] state at dst
+  auto store_state = [&](float *dst) {
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int row = rg + RG * m;
-    float4 hn;
-    hn.x = alpha * Hr[m].x;
-    hn.y = alpha * Hr[m].y;
-    hn.z = alpha * Hr[m].z;
-    hn.w = alpha * Hr[m].w;
+    for (int m = 0; m < RPT; ++m)
+      *reinterpret_cast<float4 *>(dst + static_cast<size_t>(rg + RG * m) * DV + 4 * cg) = Hr[m];
+  };
+
+  // the request's tokens one after another; the state stays in registers
+  for (int t = 0; t < p.num_tokens; ++t) {
+    const size_t tok = static_cast<size_t>(i) * p.num_tokens + t;   // token row
+    // q and k rows (optionally L2-normalised) -> LDS
+    if (wave <= NH) {
+      const TIn *src = (wave < NH) ? kg + ((tok * NH + wave) * p.Hk + hk) * DK
+                                   : qg + (tok * p.Hk + hk) * DK;
+      float x[DK / 64];
+      float ss = 0.0f;
 #pragma unroll
-    for (int s = 0; s < NH; ++s) {
-      const float kv = ks[s][row];
-      hn.x += kv * dlt[s][0];
-      hn.y += kv * dlt[s][1];
-      hn.z += kv * dlt[s][2];
-      hn.w += kv * dlt[s][3];
+      for (int e = 0; e < DK / 64; ++e) {
+        x[e] = load_f32(src + lane + 64 * e);
+        ss += x[e] * x[e];
+      }
+      if (p.l2norm) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        const float rn = 1.0f / sqrtf(ss + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < DK / 64; ++e) x[e] *= rn;
+      }
+      float *dstv = (wave < NH) ? ks[wave] : qs;
+#pragma unroll
+      for (int e = 0; e < DK / 64; ++e) dstv[lane + 64 * e] = x[e];
     }
-    *reinterpret_cast<float4 *>(st + static_cast<size_t>(row) * DV + 4 * cg) = hn;
+    __syncthreads();
+    // dot products among the sub-step keys and the query (one wave per product)
+    for (int d = wave; d < NV * NH; d += WAVES) {
+      const int s = d / NV, o = d % NV;   // k_s . (k_o or q when o == NH)
+      const float *b = (o < NH) ? ks[o] : qs;
+      float acc = 0.0f;
+      for (int e = lane; e < DK; e += 64) acc += ks[s][e] * b[e];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) dots[d] = acc;
+    }
+
+    // partial H^T x for x in {k_0.., q}: this thread's rows, its 4 columns
+    float part[NV][4];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) part[v][c] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int row = rg + RG * m;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float xv = (v < NH) ? ks[v][row] : qs[row];
+        part[v][0] += Hr[m].x * xv;
+        part[v][1] += Hr[m].y * xv;
+        part[v][2] += Hr[m].z * xv;
+        part[v][3] += Hr[m].w * xv;
+      }
+    }
+    // reduce over the row groups inside the wave (lanes CG apart)
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[v][c] += __shfl_xor(part[v][c], off);
+    if (lane < CG) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[wave][v][4 * cg + c] = part[v][c];
+    }
+    __syncthreads();
+
+    // the gates (formed here from the raw projections when gate_mode is set)
+    float alpha, bet[NH];
+    {
+      const float gin = p.g[tok * p.Hv + h];
+      alpha = p.gate_mode ? expf(gate_decay(gin, gate_A, p.dt_bias[h])) : expf(gin);
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        const float b = p.beta[(tok * NH + s) * p.Hv + h];
+        bet[s] = p.gate_mode ? gate_beta(b) : b;
+      }
+    }
+    // per-column step (every thread, for its own 4 columns)
+    float dlt[NH][4];
+    float out[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = 4 * cg + c;
+      float a[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][v][col];
+        a[v] = s;
+      }
+      float o = alpha * a[NH];
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        float u = alpha * a[s];
+#pragma unroll
+        for (int s2 = 0; s2 < s; ++s2) u += dots[s2 * NV + s] * dlt[s2][c];
+        const size_t row = tok * NH + s;
+        const float vv = load_f32(vg + (row * p.Hv + h) * DV + col);
+        dlt[s][c] = bet[s] * (vv - u);
+        o += dots[s * NV + NH] * dlt[s][c];
+      }
+      out[c] = p.scale * o;
+    }
+    if (rg == 0) {
+      const size_t off = (tok * p.Hv + h) * DV + 4 * cg;
+      if (p.out_bf16) {
+        uint16_t *op = static_cast<uint16_t *>(p.out) + off;
+        const uint2 pk = {static_cast<uint32_t>(f32_to_bf16(out[0])) |
+                              (static_cast<uint32_t>(f32_to_bf16(out[1])) << 16),
+                          static_cast<uint32_t>(f32_to_bf16(out[2])) |
+                              (static_cast<uint32_t>(f32_to_bf16(out[3])) << 16)};
+        *reinterpret_cast<uint2 *>(op) = pk;
+      } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + off) =
+            make_float4(out[0], out[1], out[2], out[3]);
+      }
+    }
+
+    // H' = alpha H + sum_s k_s d_s^T, in registers
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int row = rg + RG * m;
+      float4 hn;
+      hn.x = alpha * Hr[m].x;
+      hn.y = alpha * Hr[m].y;
+      hn.z = alpha * Hr[m].z;
+      hn.w = alpha * Hr[m].w;
+#pragma unroll
+      for (int s = 0; s < NH; ++s) {
+        const float kv = ks[s][row];
+        hn.x += kv * dlt[s][0];
+        hn.y += kv * dlt[s][1];
+        hn.z += kv * dlt[s][2];
+        hn.w += kv * dlt[s][3];
+      }
+      Hr[m] = hn;
+    }
+    if (p.intermediate_state && r >= 0)
+      store_state(p.intermediate_state + (tok * p.Hv + h) * state_size);
+    // the next token rewrites qs, ks, dots and red
+    if (t + 1 < p.num_tokens) __syncthreads();
   }
+  if (r >= 0) store_state(st);   // padding: no state write
 }
 
 namespace {

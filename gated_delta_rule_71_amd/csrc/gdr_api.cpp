@@ -91,9 +91,12 @@ int gdr_validate_decode(const gdr_decode_args *a) {
   if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
   if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
   if (a->gate_mode != 0 && a->gate_mode != 1) return GDR_ERR_INVALID_ARG;
+  if (a->num_tokens < 1) return GDR_ERR_INVALID_ARG;
   if (!head_ok(a->head_k) || !head_ok(a->head_v)) return GDR_ERR_UNSUPPORTED;
   if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
+  if (a->num_tokens > (1 << 16)) return GDR_ERR_UNSUPPORTED;
   if (a->batch > 0) {
+    if (a->intermediate_state && !aligned16(a->intermediate_state)) return GDR_ERR_INVALID_ARG;
     if (a->gate_mode == 1 && (!a->A_log || !a->dt_bias)) return GDR_ERR_INVALID_ARG;
     if (a->num_slots <= 0) return GDR_ERR_INVALID_ARG;
     if (!a->batch_indices && a->batch > a->num_slots) return GDR_ERR_INVALID_ARG;
@@ -101,6 +104,10 @@ int gdr_validate_decode(const gdr_decode_args *a) {
       return GDR_ERR_INVALID_ARG;
     if (!aligned16(a->state) || !aligned16(a->out)) return GDR_ERR_INVALID_ARG;
     if (int64_t{a->batch} * a->num_v_heads > kMaxRows) return GDR_ERR_UNSUPPORTED;
+    // token-row offsets (request * T + t) times heads x head size stay 64-bit in the
+    // kernel; the row count itself must fit an int
+    if (int64_t{a->batch} * a->num_tokens * a->num_householder > kMaxRows)
+      return GDR_ERR_UNSUPPORTED;
   }
   return GDR_OK;
 }
@@ -171,6 +178,8 @@ int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
   p.gate_mode = a->gate_mode;
   p.A_log = a->A_log;
   p.dt_bias = a->dt_bias;
+  p.num_tokens = a->num_tokens;
+  p.intermediate_state = a->intermediate_state;
   const hipError_t e = gdr::launch_decode(p, a->qkv_dtype == GDR_DTYPE_F32, a->head_k,
                                           a->head_v, a->num_householder,
                                           static_cast<hipStream_t>(stream));

@@ -53,6 +53,8 @@ struct DecodeParams {
   int gate_mode;
   const float *A_log;
   const float *dt_bias;
+  int num_tokens;                // tokens per request (>= 1)
+  float *intermediate_state;     // NULL, or [batch, num_tokens, Hv, K, V]
 };
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).

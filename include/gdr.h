@@ -158,10 +158,18 @@ typedef struct {
  * step computed from slot 0 (meaningless if slot 0 is written in the same call).
  * batch_indices NULL means static batching: request i uses slot i.
  *
- * Shapes: q [n, Hk, K]; k [n, n_h, Hk, K]; v [n, n_h, Hv, V]; g [n, Hv] float32;
- *   beta [n, n_h, Hv] float32; state [num_slots, Hv, K, V] float32;
- *   batch_indices int32 [n] or NULL; out [n, Hv, V] (out_dtype).
- * Supported: K = 128 or 64, V = 128 or 64, n_h in {1, 2}.
+ * Shapes (T = num_tokens tokens per request, 1 for the single-token step):
+ *   q [n, T, Hk, K]; k [n, T, n_h, Hk, K]; v [n, T, n_h, Hv, V]; g [n, T, Hv]
+ *   float32; beta [n, T, n_h, Hv] float32; state [num_slots, Hv, K, V] float32;
+ *   batch_indices int32 [n] or NULL; out [n, T, Hv, V] (out_dtype).
+ * Several tokens per request (the [n, seq_len, ...] form of ssm_decode on page
+ *   "core.ssm.gated_delta_product", e.g. speculative tokens) advance the state
+ *   token by token: the slot is read once, the T steps run in registers, and the
+ *   slot is written once at the end.  intermediate_state ([n, T, Hv, K, V]
+ *   float32, or NULL; the intermediate_ssm_state argument of ssm_decode) then
+ *   receives the state after each token.  A padding request evolves its copy of
+ *   slot 0 privately and writes neither the slot nor intermediate states.
+ * Supported: K = 128 or 64, V = 128 or 64, n_h in {1, 2}, 1 <= T <= 2^16.
  */
 typedef struct {
   int32_t batch;            /* n requests                                           */
@@ -186,6 +194,8 @@ typedef struct {
   int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections (above) */
   const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
   const float *dt_bias;     /* [Hv] float32, gate_mode 1 only (else ignored)        */
+  int32_t num_tokens;       /* T >= 1 tokens per request                            */
+  float *intermediate_state; /* [n, T, Hv, K, V] float32 or NULL                    */
 } gdr_decode_args;
 
 /* Version of this ABI (GDR_ABI_VERSION). */

@@ -170,3 +170,28 @@ def decode(q, k, v, g, beta, cache, *, batch_indices=None, scale=None, use_qk_l2
     if rc != 0:
         raise RuntimeError(f"gdr_oracle_decode failed with code {rc}")
     return out
+
+
+def decode_tokens(q, k, v, g, beta, cache, *, batch_indices=None, scale=None,
+                  use_qk_l2norm=False, num_householder=1, threads=0, lib=None):
+    """Several decode tokens per request (token axis 1, ssm_decode's [n, seq_len, ...]
+    form on page "core.ssm.gated_delta_product"): the single-token step of
+    :func:`decode` applied token after token to a private copy of each request's
+    slot state; the slot in ``cache`` (fp64, in place) is written at the end unless
+    the request is padding (index -1, whose copy starts from slot 0).
+
+    Returns (o [n,T,Hv,V], states [n,T,Hv,K,V]: the state after each token).
+    """
+    n, T = q.shape[0], q.shape[1]
+    idx = np.arange(n) if batch_indices is None else np.asarray(batch_indices)
+    work = np.ascontiguousarray(np.stack([cache[max(int(r), 0)] for r in idx]))
+    outs, states = [], []
+    for t in range(T):
+        outs.append(decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], work, scale=scale,
+                           use_qk_l2norm=use_qk_l2norm, num_householder=num_householder,
+                           threads=threads, lib=lib))
+        states.append(work.copy())
+    for i, r in enumerate(idx):
+        if r >= 0:
+            cache[int(r)] = work[i]
+    return np.stack(outs, axis=1), np.stack(states, axis=1)

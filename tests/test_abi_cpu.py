@@ -59,7 +59,7 @@ def _decode(**kw):
     base = dict(batch=8, num_qk_heads=2, num_v_heads=4, head_k=128, head_v=128,
                 num_householder=1, num_slots=16, qkv_dtype=1, out_dtype=1, use_qk_l2norm=0,
                 scale=math.nan, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE,
-                out=FAKE)
+                out=FAKE, num_tokens=1)
     base.update(kw)
     for k, v in base.items():
         setattr(a, k, v)
@@ -123,6 +123,9 @@ def test_validate_prefill(lib, kw, code):
     (dict(gate_mode=-1), 1),
     (dict(gate_mode=1, dt_bias=FAKE), 1),
     (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE), 0),
+    (dict(num_tokens=0), 1), (dict(num_tokens=4), 0), (dict(num_tokens=(1 << 16) + 1), 2),
+    (dict(num_tokens=4, intermediate_state=FAKE), 0),
+    (dict(num_tokens=4, intermediate_state=FAKE + 4), 1),
 ])
 def test_validate_decode(lib, kw, code):
     a = _decode(**kw)
