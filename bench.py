@@ -1,9 +1,9 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs prefill,decode,gdp,gates,boundary]
+                    [--legs prefill,decode,gdp,gates,boundary,conv_norm]
 
-Five legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Six legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
@@ -19,6 +19,9 @@ Five legs, each timed over exactly K steps bracketed by torch.cuda.synchronize()
            times and their ratio to the legs above.
   boundary: the prefill again, also writing boundary states every 1024 and every
            64 tokens (prefix caching); kernel times and bytes written.
+  conv_norm: the short causal conv over the workload's V/K/Q projection (prefill
+           and a 128-request decode step) and the gated RMS norm of its output;
+           kernel times and achieved bandwidth.
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary")
+    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary,conv_norm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -283,6 +286,65 @@ def run_decode_leg(wl3, steps, warmup):
     return wall, kern
 
 
+def run_conv_norm_leg(wl2, steps, warmup):
+    """The conv over the packed V/K/Q projection of the prefill workload (C = 2 Hk K
+    + Hv V channels, W = 4, SiLU, slot-indexed conv state), the cached conv decode
+    of 128 requests, and the gated RMS norm of the prefill output; kernel times and
+    bytes (read + written once) against the HBM peak."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    rng = np.random.default_rng(9)
+    T = wl2.tokens
+    Hk, K = wl2.q.shape[2], wl2.q.shape[3]
+    Hv, V = wl2.v.shape[-2], wl2.v.shape[-1]
+    C, Wd = 2 * Hk * K + Hv * V, 4
+    N = wl2.num_seqs
+    x = torch.randn((T, C), device="cuda", dtype=torch.bfloat16)
+    w = torch.randn((C, Wd), device="cuda") * 0.5
+    b = torch.randn(C, device="cuda") * 0.1
+    cu = up(wl2.cu_seqlens)
+    state = torch.zeros((2 * N, C, Wd - 1), device="cuda")
+    idx = torch.from_numpy(rng.permutation(2 * N)[:N].astype(np.int32)).cuda()
+    y = torch.empty_like(x)
+    lib = gdr.library()
+    stream = torch.cuda.current_stream().cuda_stream
+    a = gdr.conv_prefill_args(x, w, b, cu, conv_state=state, state_indices=idx, out=y)
+    assert lib.gdr_causal_conv1d_prefill(a, stream) == 0
+    _, kc = time_launches(lambda: lib.gdr_causal_conv1d_prefill(a, stream), steps, warmup)
+    conv_bytes = 2 * x.numel() * 2
+    n = 128
+    xd = torch.randn((n, 1, C), device="cuda", dtype=torch.bfloat16)
+    sd = torch.zeros((256, C, Wd - 1), device="cuda")
+    bi = torch.from_numpy(rng.permutation(256)[:n].astype(np.int32)).cuda()
+    yd = torch.empty_like(xd)
+    ad = gdr.conv_decode_args(xd, w, b, sd, batch_indices=bi, out=yd)
+    assert lib.gdr_causal_conv1d_decode(ad, stream) == 0
+    _, kd = time_launches(lambda: lib.gdr_causal_conv1d_decode(ad, stream), steps, warmup)
+    dec_bytes = 2 * xd.numel() * 2 + 2 * n * C * (Wd - 1) * 4
+    o = torch.randn((T, Hv, V), device="cuda", dtype=torch.bfloat16)
+    z = torch.randn((T, Hv, V), device="cuda", dtype=torch.bfloat16)
+    wn = torch.ones(Hv * V, device="cuda")
+    yn = torch.empty_like(o)
+    gdr.gated_rmsnorm(o, z, wn, out=yn)
+
+    def norm_launch():
+        gdr.gated_rmsnorm(o, z, wn, out=yn)
+
+    _, kn = time_launches(norm_launch, steps, warmup)
+    norm_bytes = 3 * o.numel() * 2
+    gbs = lambda byt, ms: byt / (ms * 1e-3) / 1e9
+    return {
+        "conv_prefill": {"kernel_ms": kc, "channels": C, "tokens": T, "bytes": conv_bytes,
+                         "achieved_gbs": gbs(conv_bytes, kc),
+                         "hbm_frac": gbs(conv_bytes, kc) / HBM_PEAK_GBS},
+        "conv_decode": {"kernel_ms": kd, "requests": n, "bytes": dec_bytes,
+                        "achieved_gbs": gbs(dec_bytes, kd)},
+        "gated_rmsnorm": {"kernel_ms": kn, "rows": T * Hv, "group": V, "bytes": norm_bytes,
+                          "achieved_gbs": gbs(norm_bytes, kn),
+                          "hbm_frac": gbs(norm_bytes, kn) / HBM_PEAK_GBS},
+    }
+
+
 def profile_run():
     """3 prefill launches, 3 decode launches (cache flushed before each) and a copy probe."""
     import torch
@@ -386,6 +448,11 @@ def main():
               flush=True)
         del gw2, gw3
 
+    # ---- short causal conv and gated RMS norm around the recurrence -------------------
+    if "conv_norm" in legs:
+        res["conv_norm"] = run_conv_norm_leg(wl2, args.steps, args.warmup)
+        print(f"[bench] conv/norm: {res['conv_norm']}", file=sys.stderr, flush=True)
+
     # ---- boundary states (prefix caching) on the packed prefill ------------------------
     if "boundary" in legs:
         res["boundary"] = {"note": "packed prefill also writing each sequence's state every "
@@ -486,6 +553,8 @@ def main():
         line["fused_gates"] = res["gates"]
     if "boundary" in res:
         line["boundary_states"] = res["boundary"]
+    if "conv_norm" in res:
+        line["conv_norm"] = res["conv_norm"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["bench_wall_s"] = time.perf_counter() - t_start

@@ -26,7 +26,8 @@ import math
 
 from . import _lib
 
-__all__ = ["chunk_gated_delta_rule", "ssm_decode", "library", "abi_version"]
+__all__ = ["chunk_gated_delta_rule", "ssm_decode", "causal_conv1d", "causal_conv1d_update",
+           "gated_rmsnorm", "library", "abi_version"]
 
 
 def library():
@@ -281,3 +282,113 @@ def ssm_decode(q, k, v, g, beta, ssm_state, batch_indices=None, scale=None,
 
 def default_scale(head_k: int) -> float:
     return 1.0 / math.sqrt(head_k)
+
+
+# ---- the steps around the recurrence: short causal conv, gated RMS norm -----------------
+
+def conv_prefill_args(x, weight, bias, cu_seqlens, *, conv_state=None, state_indices=None,
+                      activation="silu", out=None):
+    a = _lib.ConvPrefillArgs()
+    a.tokens, a.channels = x.shape[0], x.shape[1]
+    a.num_seqs = cu_seqlens.numel() - 1
+    a.width = weight.shape[1]
+    a.dtype = _dtype_code(x.dtype)
+    a.activation = {"silu": 1, None: 0, "none": 0}[activation]
+    a.num_slots = conv_state.shape[0] if (conv_state is not None and
+                                          state_indices is not None) else 0
+    a.x, a.weight, a.bias = _ptr(x), _ptr(weight), _ptr(bias)
+    a.cu_seqlens, a.state_indices = _ptr(cu_seqlens), _ptr(state_indices)
+    a.conv_state, a.out = _ptr(conv_state), _ptr(out)
+    return a
+
+
+def causal_conv1d(x, weight, bias=None, *, cu_seqlens=None, conv_state=None,
+                  state_indices=None, activation="silu", out=None, stream=None):
+    """Depthwise causal conv over packed sequences: x [tokens, C] (float32 or
+    bfloat16), weight float32 [C, W], bias float32 [C] or None, cu_seqlens int32
+    [N+1] (None: one sequence).  conv_state float32 [rows, C, W-1] (rows addressed
+    by state_indices, -1 = padding) supplies the inputs before each sequence and
+    receives its last W-1 inputs, in place.  Returns y [tokens, C]."""
+    torch = _torch()
+    lib = library()
+    _check(x, "x", ndim=2)
+    _check(weight, "weight", dtype=torch.float32, ndim=2)
+    if bias is not None:
+        _check(bias, "bias", dtype=torch.float32, ndim=1)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=x.device)
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+    if conv_state is not None:
+        _check(conv_state, "conv_state", dtype=torch.float32, ndim=3)
+    if state_indices is not None:
+        _check(state_indices, "state_indices", dtype=torch.int32, ndim=1)
+    if out is None:
+        out = torch.empty_like(x)
+    a = conv_prefill_args(x, weight, bias, cu_seqlens, conv_state=conv_state,
+                          state_indices=state_indices, activation=activation, out=out)
+    _raise(lib.gdr_causal_conv1d_prefill(a, _stream(stream)), "gdr_causal_conv1d_prefill")
+    return out
+
+
+def conv_decode_args(x, weight, bias, conv_state, *, batch_indices=None, activation="silu",
+                     intermediate_state=None, out=None):
+    a = _lib.ConvDecodeArgs()
+    a.batch = x.shape[0]
+    a.num_tokens = x.shape[1] if x.dim() == 3 else 1
+    a.channels = x.shape[-1]
+    a.width = weight.shape[1]
+    a.dtype = _dtype_code(x.dtype)
+    a.activation = {"silu": 1, None: 0, "none": 0}[activation]
+    a.num_slots = conv_state.shape[0]
+    a.x, a.weight, a.bias = _ptr(x), _ptr(weight), _ptr(bias)
+    a.batch_indices, a.conv_state = _ptr(batch_indices), _ptr(conv_state)
+    a.intermediate_state, a.out = _ptr(intermediate_state), _ptr(out)
+    return a
+
+
+def causal_conv1d_update(x, conv_state, weight, bias=None, *, batch_indices=None,
+                         activation="silu", intermediate_state=None, out=None, stream=None):
+    """The cached conv step: x [n, C] or [n, T, C]; conv_state float32 [slots, C, W-1]
+    updated in place at batch_indices (None: request i <-> row i; -1: padding
+    reads row 0, writes nothing); intermediate_state float32 [n, T, C, W-1] or
+    None receives the window after each token.  Returns y shaped like x."""
+    torch = _torch()
+    lib = library()
+    _check(x, "x", ndim=(2, 3))
+    _check(conv_state, "conv_state", dtype=torch.float32, ndim=3)
+    _check(weight, "weight", dtype=torch.float32, ndim=2)
+    if bias is not None:
+        _check(bias, "bias", dtype=torch.float32, ndim=1)
+    if batch_indices is not None:
+        _check(batch_indices, "batch_indices", dtype=torch.int32, ndim=1)
+    if intermediate_state is not None:
+        _check(intermediate_state, "intermediate_state", dtype=torch.float32, ndim=4)
+    if out is None:
+        out = torch.empty_like(x)
+    a = conv_decode_args(x, weight, bias, conv_state, batch_indices=batch_indices,
+                         activation=activation, intermediate_state=intermediate_state, out=out)
+    _raise(lib.gdr_causal_conv1d_decode(a, _stream(stream)), "gdr_causal_conv1d_decode")
+    return out
+
+
+def gated_rmsnorm(x, z, weight, *, eps=1e-5, norm_before_gate=False, out=None, stream=None):
+    """Gated RMS norm per (token, head) group: x, z [tokens, heads, group] (one
+    dtype); weight float32 [heads * group].  norm_before_gate False: norm(x *
+    silu(z)) * w; True: norm(x) * w * silu(z).  Returns y like x."""
+    torch = _torch()
+    lib = library()
+    _check(x, "x", ndim=3)
+    _check(z, "z", dtype=x.dtype, ndim=3)
+    _check(weight, "weight", dtype=torch.float32, ndim=1)
+    if tuple(z.shape) != tuple(x.shape) or weight.numel() != x.shape[1] * x.shape[2]:
+        raise ValueError("z must match x and weight must have heads * group entries")
+    if out is None:
+        out = torch.empty_like(x)
+    a = _lib.GatedRMSNormArgs()
+    a.tokens, a.heads, a.group = x.shape
+    a.dtype = _dtype_code(x.dtype)
+    a.norm_before_gate = int(bool(norm_before_gate))
+    a.eps = float(eps)
+    a.x, a.z, a.weight, a.out = _ptr(x), _ptr(z), _ptr(weight), _ptr(out)
+    _raise(lib.gdr_gated_rmsnorm(a, _stream(stream)), "gdr_gated_rmsnorm")
+    return out

@@ -29,6 +29,12 @@ EXPORTS = (
     "gdr_prefill_workspace_bytes",
     "gdr_chunk_gated_delta_rule",
     "gdr_ssm_decode",
+    "gdr_validate_conv_prefill",
+    "gdr_validate_conv_decode",
+    "gdr_validate_gated_rmsnorm",
+    "gdr_causal_conv1d_prefill",
+    "gdr_causal_conv1d_decode",
+    "gdr_gated_rmsnorm",
 )
 
 
@@ -99,6 +105,40 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class ConvPrefillArgs(ctypes.Structure):
+    """gdr_conv_prefill_args."""
+    _fields_ = [
+        ("tokens", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("channels", ctypes.c_int32),
+        ("width", ctypes.c_int32), ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("x", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p), ("conv_state", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
+class ConvDecodeArgs(ctypes.Structure):
+    """gdr_conv_decode_args."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("channels", ctypes.c_int32),
+        ("width", ctypes.c_int32), ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("x", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p), ("batch_indices", ctypes.c_void_p),
+        ("conv_state", ctypes.c_void_p), ("intermediate_state", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
+class GatedRMSNormArgs(ctypes.Structure):
+    """gdr_gated_rmsnorm_args."""
+    _fields_ = [
+        ("tokens", ctypes.c_int32), ("heads", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("norm_before_gate", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("x", ctypes.c_void_p), ("z", ctypes.c_void_p), ("weight", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -128,6 +168,17 @@ def load(path: str = LIB_PATH):
         lib.gdr_chunk_gated_delta_rule.restype = ctypes.c_int
         lib.gdr_ssm_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
         lib.gdr_ssm_decode.restype = ctypes.c_int
+        for name, typ in (("conv_prefill", ConvPrefillArgs), ("conv_decode", ConvDecodeArgs),
+                          ("gated_rmsnorm", GatedRMSNormArgs)):
+            v = getattr(lib, f"gdr_validate_{name}")
+            v.argtypes = [ctypes.POINTER(typ)]
+            v.restype = ctypes.c_int
+        for name, typ in (("causal_conv1d_prefill", ConvPrefillArgs),
+                          ("causal_conv1d_decode", ConvDecodeArgs),
+                          ("gated_rmsnorm", GatedRMSNormArgs)):
+            f = getattr(lib, f"gdr_{name}")
+            f.argtypes = [ctypes.POINTER(typ), ctypes.c_void_p]
+            f.restype = ctypes.c_int
         if lib.gdr_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{path} has ABI version {lib.gdr_abi_version()}, the bindings "
                                f"expect {ABI_VERSION}: rebuild it")

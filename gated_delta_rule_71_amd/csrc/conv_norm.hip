@@ -1,0 +1,321 @@
+// The steps on either side of the recurrence in a Gated DeltaNet / Gated Delta
+// Product layer (Megatron Core API pages "core.ssm.gated_delta_net.gdn" and
+// "core.ssm.gated_delta_product"):
+//   * the short depthwise causal convolution over the packed V/K/Q projection
+//     (GatedDeltaProductMixer d_conv = 4, _prepare_qkv with conv_initial_states
+//     for chunked prefill, _decode_conv for the cached decode step), with a
+//     slot-indexed conv state holding each request's last W-1 inputs;
+//   * the gated RMS normalisation of the recurrence output (ExtendedRMSNorm, an
+//     RMSNormGated; norm_before_gate chooses where the gate applies).
+// All three kernels are bandwidth-bound streams: consecutive threads take
+// consecutive 4-channel groups (8- or 16-byte accesses), the conv window lives in
+// registers, and the norm reduces one group per wave.
+
+#include "common.hpp"
+#include "gdr_internal.hpp"
+
+namespace gdr {
+
+namespace {
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ void load4in(const uint16_t *p, float (&x)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4in(const float *p, float (&x)[4]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void store4out(uint16_t *p, const float (&y)[4]) {
+  const uint2 u = {static_cast<uint32_t>(f32_to_bf16(y[0])) |
+                       (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16),
+                   static_cast<uint32_t>(f32_to_bf16(y[2])) |
+                       (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16)};
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+__device__ __forceinline__ void store4out(float *p, const float (&y)[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(y[0], y[1], y[2], y[3]);
+}
+
+// sequence holding token t: the last n with cu[n] <= t (cu non-decreasing)
+__device__ __forceinline__ int find_seq(const int32_t *cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int kConvTokens = 32;   // tokens per thread in the prefill conv
+
+// One output token: y = act(b + sum_j w_j x[t - (W-1) + j]); win holds the W-1
+// previous inputs (oldest first).
+template <int W>
+__device__ __forceinline__ void conv_step(const float (&w)[4][W], const float (&b)[4],
+                                          float (&win)[W - 1][4], const float (&x)[4],
+                                          int act, float (&y)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float acc = b[c] + w[c][W - 1] * x[c];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) acc += w[c][j] * win[j][c];
+    y[c] = act ? silu(acc) : acc;
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < W - 1; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) win[j][c] = win[j + 1][c];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) win[W - 2][c] = x[c];
+}
+
+template <int W>
+__device__ __forceinline__ void load_weights(const ConvParams &p, int c0, float (&w)[4][W],
+                                             float (&b)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int j = 0; j < W; ++j) w[c][j] = p.weight[static_cast<size_t>(c0 + c) * W + j];
+    b[c] = p.bias ? p.bias[c0 + c] : 0.0f;
+  }
+}
+
+// window of the W-1 inputs before sequence n's first token: its conv state row
+template <int W>
+__device__ __forceinline__ void load_window(const ConvParams &p, int n, int c0,
+                                            float (&win)[W - 1][4]) {
+  const float *st = nullptr;
+  if (p.conv_state) {
+    const int idx = p.state_indices ? p.state_indices[n] : n;
+    st = p.conv_state + (static_cast<size_t>(idx < 0 ? 0 : idx) * p.C + c0) * (W - 1);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) win[j][c] = st ? st[c * (W - 1) + j] : 0.0f;
+}
+
+// ---- prefill: outputs ---------------------------------------------------------------
+template <typename T, int W>
+__global__ void __launch_bounds__(256) conv_prefill_kernel(const ConvParams p) {
+  const int cg = blockIdx.y * 256 + threadIdx.x;   // 4-channel group
+  if (cg * 4 >= p.C) return;
+  const int c0 = 4 * cg;
+  const int tb = blockIdx.x * kConvTokens;
+  const int te = min(tb + kConvTokens, p.tokens);
+  if (tb >= te) return;
+  float w[4][W], b[4];
+  load_weights<W>(p, c0, w, b);
+  const T *x = static_cast<const T *>(p.x);
+  T *y = static_cast<T *>(p.out);
+
+  int n = find_seq(p.cu_seqlens, p.num_seqs, tb);
+  float win[W - 1][4];
+  // window before token tb: inputs of this sequence where they exist, else its state
+  {
+    const int t0 = p.cu_seqlens[n];
+    float sw[W - 1][4];
+    load_window<W>(p, n, c0, sw);
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+      const int tau = tb - (W - 1) + j;
+      if (tau >= t0) {
+        float v[4];
+        load4in(x + static_cast<size_t>(tau) * p.C + c0, v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) win[j][c] = v[c];
+      } else {
+        // tau - t0 in [-(W-1), -1] -> state entry (W-1) + (tau - t0)
+        const int e = (W - 1) + (tau - t0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float s = 0.0f;
+#pragma unroll
+          for (int k = 0; k < W - 1; ++k) s = (k == e) ? sw[k][c] : s;
+          win[j][c] = s;
+        }
+      }
+    }
+  }
+  int next = p.cu_seqlens[n + 1];
+  for (int t = tb; t < te; ++t) {
+    if (t >= next) {   // a new sequence starts at t: its window is its state
+      while (n + 1 < p.num_seqs && p.cu_seqlens[n + 1] <= t) ++n;
+      next = p.cu_seqlens[n + 1];
+      load_window<W>(p, n, c0, win);
+    }
+    float v[4], o[4];
+    load4in(x + static_cast<size_t>(t) * p.C + c0, v);
+    conv_step<W>(w, b, win, v, p.activation, o);
+    store4out(y + static_cast<size_t>(t) * p.C + c0, o);
+  }
+}
+
+// ---- prefill: conv states (after the outputs, so that no state is overwritten
+// before the first tokens of its sequence have read it) ---------------------------------
+template <typename T, int W>
+__global__ void __launch_bounds__(256) conv_state_kernel(const ConvParams p) {
+  const int cg = blockIdx.x * 256 + threadIdx.x;
+  const int n = blockIdx.y;
+  if (cg * 4 >= p.C) return;
+  const int idx = p.state_indices ? p.state_indices[n] : n;
+  if (idx < 0) return;   // padding writes nothing
+  const int c0 = 4 * cg;
+  const int t0 = p.cu_seqlens[n], t1 = p.cu_seqlens[n + 1];
+  float *st = p.conv_state + (static_cast<size_t>(idx) * p.C + c0) * (W - 1);
+  float old[W - 1][4], nw[W - 1][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) old[j][c] = st[c * (W - 1) + j];
+  const T *x = static_cast<const T *>(p.x);
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) {
+    const int tau = t1 - (W - 1) + j;   // the last W-1 inputs, oldest first
+    if (tau >= t0) {
+      float v[4];
+      load4in(x + static_cast<size_t>(tau) * p.C + c0, v);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) nw[j][c] = v[c];
+    } else {
+      const int e = (W - 1) + (tau - t0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k) s = (k == e) ? old[k][c] : s;
+        nw[j][c] = s;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) st[c * (W - 1) + j] = nw[j][c];
+}
+
+// ---- decode: T tokens per request over the cached window --------------------------------
+template <typename T, int W>
+__global__ void __launch_bounds__(256) conv_decode_kernel(const ConvParams p) {
+  const int cg = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.y;   // request
+  if (cg * 4 >= p.C) return;
+  const int c0 = 4 * cg;
+  const int r = p.state_indices ? p.state_indices[i] : i;
+  float *st = p.conv_state + (static_cast<size_t>(r < 0 ? 0 : r) * p.C + c0) * (W - 1);
+  float w[4][W], b[4], win[W - 1][4];
+  load_weights<W>(p, c0, w, b);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) win[j][c] = st[c * (W - 1) + j];
+  const T *x = static_cast<const T *>(p.x);
+  T *y = static_cast<T *>(p.out);
+  for (int t = 0; t < p.num_tokens; ++t) {
+    const size_t row = static_cast<size_t>(i) * p.num_tokens + t;
+    float v[4], o[4];
+    load4in(x + row * p.C + c0, v);
+    conv_step<W>(w, b, win, v, p.activation, o);
+    store4out(y + row * p.C + c0, o);
+    if (p.intermediate_state && r >= 0) {
+      float *is = p.intermediate_state + (row * p.C + c0) * (W - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) is[c * (W - 1) + j] = win[j][c];
+    }
+  }
+  if (r < 0) return;   // padding writes nothing
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) st[c * (W - 1) + j] = win[j][c];
+}
+
+// ---- gated RMS norm: one wave per (token, head) group of G elements -----------------------
+template <typename T, int G>
+__global__ void __launch_bounds__(256) gated_rmsnorm_kernel(const NormParams p) {
+  constexpr int EPT = G / 64;   // elements per lane (consecutive)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = static_cast<long>(blockIdx.x) * 4 + wave;   // token * heads + head
+  if (row >= p.rows) return;
+  const int head = static_cast<int>(row % p.heads);
+  const T *x = static_cast<const T *>(p.x) + row * G + lane * EPT;
+  const T *z = static_cast<const T *>(p.z) + row * G + lane * EPT;
+  float xv[EPT], zv[EPT], u[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    xv[e] = load_f32(x + e);
+    zv[e] = load_f32(z + e);
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    u[e] = p.norm_before_gate ? xv[e] : xv[e] * silu(zv[e]);
+    ss += u[e] * u[e];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float rs = 1.0f / sqrtf(ss / G + p.eps);
+  const float *wt = p.weight + static_cast<size_t>(head) * G + lane * EPT;
+  T *out = static_cast<T *>(p.out) + row * G + lane * EPT;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    float v = u[e] * rs * wt[e];
+    if (p.norm_before_gate) v *= silu(zv[e]);
+    store_f32(out + e, v);
+  }
+}
+
+template <typename T>
+hipError_t conv_dispatch(const ConvParams &p, int mode, hipStream_t s) {
+  const int groups = p.C / 4;
+  const dim3 block(256);
+  auto go = [&](auto width) -> hipError_t {
+    constexpr int W = decltype(width)::value;
+    if (mode == 0) {
+      const dim3 grid((p.tokens + kConvTokens - 1) / kConvTokens, (groups + 255) / 256);
+      if (p.tokens > 0) hipLaunchKernelGGL((conv_prefill_kernel<T, W>), grid, block, 0, s, p);
+      if (p.conv_state && p.num_seqs > 0)
+        hipLaunchKernelGGL((conv_state_kernel<T, W>), dim3((groups + 255) / 256, p.num_seqs),
+                           block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((conv_decode_kernel<T, W>), dim3((groups + 255) / 256, p.batch), block,
+                         0, s, p);
+    }
+    return hipGetLastError();
+  };
+  if (p.W == 2) return go(std::integral_constant<int, 2>());
+  if (p.W == 3) return go(std::integral_constant<int, 3>());
+  if (p.W == 4) return go(std::integral_constant<int, 4>());
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t norm_dispatch(const NormParams &p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.rows + 3) / 4)), block(256);
+  if (p.group == 64) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 64>), grid, block, 0, s, p);
+  else if (p.group == 128) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 128>), grid, block, 0, s, p);
+  else if (p.group == 256) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 256>), grid, block, 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvParams &p, int f32, int mode, hipStream_t stream) {
+  return f32 ? conv_dispatch<float>(p, mode, stream) : conv_dispatch<uint16_t>(p, mode, stream);
+}
+
+hipError_t launch_gated_rmsnorm(const NormParams &p, int f32, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  return f32 ? norm_dispatch<float>(p, stream) : norm_dispatch<uint16_t>(p, stream);
+}
+
+}  // namespace gdr

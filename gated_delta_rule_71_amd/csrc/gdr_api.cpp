@@ -186,4 +186,111 @@ int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+int gdr_validate_conv_prefill(const gdr_conv_prefill_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->tokens < 0 || a->num_seqs < 1 || a->channels <= 0 || a->channels % 4 != 0)
+    return GDR_ERR_INVALID_ARG;
+  if (!dtype_ok(a->dtype) || (a->activation != 0 && a->activation != 1))
+    return GDR_ERR_INVALID_ARG;
+  if (a->width < 2 || a->width > 4) return GDR_ERR_UNSUPPORTED;
+  if (int64_t{a->tokens} * a->channels >= (int64_t{1} << 40)) return GDR_ERR_UNSUPPORTED;
+  if (!a->weight || !a->cu_seqlens) return GDR_ERR_INVALID_ARG;
+  if (a->tokens > 0 && (!a->x || !a->out || !aligned16(a->x) || !aligned16(a->out)))
+    return GDR_ERR_INVALID_ARG;
+  if (a->state_indices && (!a->conv_state || a->num_slots <= 0)) return GDR_ERR_INVALID_ARG;
+  return GDR_OK;
+}
+
+int gdr_validate_conv_decode(const gdr_conv_decode_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->num_tokens < 1 || a->channels <= 0 || a->channels % 4 != 0)
+    return GDR_ERR_INVALID_ARG;
+  if (!dtype_ok(a->dtype) || (a->activation != 0 && a->activation != 1))
+    return GDR_ERR_INVALID_ARG;
+  if (a->width < 2 || a->width > 4) return GDR_ERR_UNSUPPORTED;
+  if (a->batch > 0) {
+    if (!a->x || !a->out || !a->weight || !a->conv_state || a->num_slots <= 0)
+      return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->x) || !aligned16(a->out)) return GDR_ERR_INVALID_ARG;
+    if (!a->batch_indices && a->batch > a->num_slots) return GDR_ERR_INVALID_ARG;
+    if (int64_t{a->batch} * a->num_tokens * a->channels >= (int64_t{1} << 40))
+      return GDR_ERR_UNSUPPORTED;
+  }
+  return GDR_OK;
+}
+
+int gdr_validate_gated_rmsnorm(const gdr_gated_rmsnorm_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->tokens < 0 || a->heads <= 0 || !dtype_ok(a->dtype)) return GDR_ERR_INVALID_ARG;
+  if (a->norm_before_gate != 0 && a->norm_before_gate != 1) return GDR_ERR_INVALID_ARG;
+  if (!(a->eps >= 0.0f) || isinf(a->eps)) return GDR_ERR_INVALID_ARG;
+  if (a->group != 64 && a->group != 128 && a->group != 256) return GDR_ERR_UNSUPPORTED;
+  if (a->tokens > 0) {
+    if (!a->x || !a->z || !a->weight || !a->out) return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->x) || !aligned16(a->z) || !aligned16(a->out)) return GDR_ERR_INVALID_ARG;
+  }
+  return GDR_OK;
+}
+
+int gdr_causal_conv1d_prefill(const gdr_conv_prefill_args *a, void *stream) {
+  const int st = gdr_validate_conv_prefill(a);
+  if (st != GDR_OK) return st;
+  gdr::ConvParams p{};
+  p.x = a->x;
+  p.weight = a->weight;
+  p.bias = a->bias;
+  p.cu_seqlens = a->cu_seqlens;
+  p.state_indices = a->state_indices;
+  p.conv_state = a->conv_state;
+  p.out = a->out;
+  p.tokens = a->tokens;
+  p.num_seqs = a->num_seqs;
+  p.C = a->channels;
+  p.W = a->width;
+  p.activation = a->activation;
+  const hipError_t e = gdr::launch_conv(p, a->dtype == GDR_DTYPE_F32, 0,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_causal_conv1d_decode(const gdr_conv_decode_args *a, void *stream) {
+  const int st = gdr_validate_conv_decode(a);
+  if (st != GDR_OK) return st;
+  if (a->batch == 0) return GDR_OK;
+  gdr::ConvParams p{};
+  p.x = a->x;
+  p.weight = a->weight;
+  p.bias = a->bias;
+  p.state_indices = a->batch_indices;
+  p.conv_state = a->conv_state;
+  p.intermediate_state = a->intermediate_state;
+  p.out = a->out;
+  p.batch = a->batch;
+  p.num_tokens = a->num_tokens;
+  p.C = a->channels;
+  p.W = a->width;
+  p.activation = a->activation;
+  const hipError_t e = gdr::launch_conv(p, a->dtype == GDR_DTYPE_F32, 1,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+int gdr_gated_rmsnorm(const gdr_gated_rmsnorm_args *a, void *stream) {
+  const int st = gdr_validate_gated_rmsnorm(a);
+  if (st != GDR_OK) return st;
+  gdr::NormParams p{};
+  p.x = a->x;
+  p.z = a->z;
+  p.weight = a->weight;
+  p.out = a->out;
+  p.rows = static_cast<long>(a->tokens) * a->heads;
+  p.heads = a->heads;
+  p.group = a->group;
+  p.norm_before_gate = a->norm_before_gate;
+  p.eps = a->eps;
+  const hipError_t e = gdr::launch_gated_rmsnorm(p, a->dtype == GDR_DTYPE_F32,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 }  // extern "C"

@@ -57,6 +57,36 @@ struct DecodeParams {
   float *intermediate_state;     // NULL, or [batch, num_tokens, Hv, K, V]
 };
 
+struct ConvParams {
+  const void *x;                 // [tokens, C] (prefill) or [batch, num_tokens, C] (decode)
+  const float *weight;           // [C, W]
+  const float *bias;             // [C] or NULL
+  const int32_t *cu_seqlens;     // prefill: [num_seqs + 1]
+  const int32_t *state_indices;  // prefill: per sequence; decode: per request; NULL: identity
+  float *conv_state;             // [rows, C, W - 1] or NULL (prefill only)
+  float *intermediate_state;     // decode: [batch, num_tokens, C, W - 1] or NULL
+  void *out;
+  int tokens;
+  int num_seqs;
+  int batch;
+  int num_tokens;
+  int C;
+  int W;
+  int activation;                // 0: none, 1: SiLU
+};
+
+struct NormParams {
+  const void *x;                 // [rows, group]
+  const void *z;                 // [rows, group]
+  const float *weight;           // [heads * group]
+  void *out;
+  long rows;                     // tokens * heads
+  int heads;
+  int group;
+  int norm_before_gate;
+  float eps;
+};
+
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k);
 // State waves (32 value columns each) per prefill workgroup.
@@ -66,5 +96,8 @@ hipError_t launch_prefill(const PrefillParams &p, int qkv_f32, int head_k, int r
                           int state_waves, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int qkv_f32, int dk, int dv, int nh,
                          hipStream_t stream);
+// mode 0: prefill (outputs, then conv states); mode 1: decode
+hipError_t launch_conv(const ConvParams &p, int f32, int mode, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const NormParams &p, int f32, hipStream_t stream);
 
 }  // namespace gdr

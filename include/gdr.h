@@ -198,6 +198,87 @@ typedef struct {
   float *intermediate_state; /* [n, T, Hv, K, V] float32 or NULL                    */
 } gdr_decode_args;
 
+/*
+ * Short depthwise causal convolution over a packed token stream (the conv on the
+ * V/K/Q projection before the recurrence: GatedDeltaProductMixer d_conv = 4 and
+ * _prepare_qkv with conv_initial_states on page "core.ssm.gated_delta_product").
+ *
+ *   y[t][c] = act(bias[c] + sum_{j<W} weight[c][j] * x[t - (W-1) + j][c])
+ *
+ * where inputs before a sequence's first token come from its conv state: row
+ * [c][0 .. W-2] holds the W-1 inputs preceding the sequence, oldest first (zeros
+ * when conv_state is NULL).  act is SiLU (activation = 1) or the identity (0);
+ * the pages do not name the activation, and SiLU is the one of the Mamba-style
+ * conv these layers use.
+ * Prefill (gdr_causal_conv1d_prefill): x, out [tokens, C]; cu_seqlens int32
+ *   [num_seqs + 1] (required; one sequence = [0, tokens]); conv_state float32
+ *   [rows, C, W-1] or NULL, addressed by state_indices[n] (NULL: row n); -1 marks
+ *   padding: it reads row 0 and writes nothing.  After the outputs, each sequence's
+ *   row receives its last W-1 inputs (from the old row when the sequence is
+ *   shorter than W-1), in place.  Rows must be distinct across sequences.
+ * Decode (gdr_causal_conv1d_decode, _decode_conv): x, out [batch, num_tokens, C];
+ *   conv_state [num_slots, C, W-1] in place, row batch_indices[i] (NULL: i; -1:
+ *   padding reads row 0, writes nothing); intermediate_state [batch, num_tokens,
+ *   C, W-1] float32 or NULL receives the window after each token.
+ * Supported: C a multiple of 4, W in {2, 3, 4}, x/out F32 or BF16 (one dtype).
+ */
+typedef struct {
+  int32_t tokens;             /* packed tokens                                     */
+  int32_t num_seqs;
+  int32_t channels;           /* C                                                 */
+  int32_t width;              /* W                                                 */
+  int32_t dtype;              /* gdr_dtype of x and out                            */
+  int32_t activation;         /* 1: SiLU, 0: none                                  */
+  int32_t num_slots;          /* rows of conv_state when state_indices is given    */
+  const void *x;
+  const float *weight;        /* [C, W]                                            */
+  const float *bias;          /* [C] or NULL                                       */
+  const int32_t *cu_seqlens;
+  const int32_t *state_indices;
+  float *conv_state;
+  void *out;
+} gdr_conv_prefill_args;
+
+typedef struct {
+  int32_t batch;              /* requests                                          */
+  int32_t num_tokens;         /* tokens per request (>= 1)                         */
+  int32_t channels;
+  int32_t width;
+  int32_t dtype;
+  int32_t activation;
+  int32_t num_slots;
+  const void *x;
+  const float *weight;
+  const float *bias;
+  const int32_t *batch_indices;
+  float *conv_state;          /* [num_slots, C, W-1], in place                     */
+  float *intermediate_state;  /* [batch, num_tokens, C, W-1] or NULL               */
+  void *out;
+} gdr_conv_decode_args;
+
+/*
+ * Gated RMS normalisation of the recurrence output (ExtendedRMSNorm, an
+ * RMSNormGated, page "core.ssm.gated_delta_product"; norm_before_gate as in
+ * GatedDeltaProductMixer).  For each token and head, over the group of `group`
+ * elements:
+ *   norm_before_gate = 0:  u = x * silu(z),  y = u / sqrt(mean(u^2) + eps) * w
+ *   norm_before_gate = 1:  y = x / sqrt(mean(x^2) + eps) * w * silu(z)
+ * x, z, out [tokens, heads, group] (one dtype, F32 or BF16); weight float32
+ * [heads * group].  Supported: group in {64, 128, 256}.
+ */
+typedef struct {
+  int32_t tokens;
+  int32_t heads;
+  int32_t group;
+  int32_t dtype;
+  int32_t norm_before_gate;
+  float eps;
+  const void *x;
+  const void *z;
+  const float *weight;
+  void *out;
+} gdr_gated_rmsnorm_args;
+
 /* Version of this ABI (GDR_ABI_VERSION). */
 int gdr_abi_version(void);
 
@@ -214,6 +295,14 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *args);
 /* Enqueue a prefill / a decode step on `stream` (hipStream_t). */
 int gdr_chunk_gated_delta_rule(const gdr_prefill_args *args, void *stream);
 int gdr_ssm_decode(const gdr_decode_args *args, void *stream);
+
+/* Host-only checks and enqueue of the causal conv and the gated RMS norm. */
+int gdr_validate_conv_prefill(const gdr_conv_prefill_args *args);
+int gdr_validate_conv_decode(const gdr_conv_decode_args *args);
+int gdr_validate_gated_rmsnorm(const gdr_gated_rmsnorm_args *args);
+int gdr_causal_conv1d_prefill(const gdr_conv_prefill_args *args, void *stream);
+int gdr_causal_conv1d_decode(const gdr_conv_decode_args *args, void *stream);
+int gdr_gated_rmsnorm(const gdr_gated_rmsnorm_args *args, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,8 @@ Two independent CPU evaluations of the recurrence, both in fp64:
   unchanged for any chunk size.
 * :func:`gates` (``oracle/gating.py``) — the gates g and beta from the raw
   per-token projections and the per-head parameters A_log and dt_bias.
+* ``oracle/conv_norm.py`` — the short causal conv (prefill and cached decode)
+  and the gated RMS norm around the recurrence.
 
 The recurrence is the gated delta rule named on the Megatron Core API page
 "core.ssm.gated_delta_net.gdn" (function torch_chunk_gated_delta_rule) and, with
@@ -30,6 +32,7 @@ import threading
 import numpy as np
 
 from .gating import gates  # noqa: F401  (re-exported)
+from . import conv_norm  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr_oracle.c")
