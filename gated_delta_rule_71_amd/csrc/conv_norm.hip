@@ -18,7 +18,12 @@ namespace gdr {
 
 namespace {
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+// SiLU(x) = x / (1 + e^-x) on the hardware base-2 exponential and reciprocal
+// (about one ulp each); e^-x = inf for very negative x gives x * 0 = -0.
+__device__ __forceinline__ float silu(float x) {
+  const float e = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 __device__ __forceinline__ void load4in(const uint16_t *p, float (&x)[4]) {
   const uint2 u = *reinterpret_cast<const uint2 *>(p);
@@ -144,16 +149,28 @@ __global__ void __launch_bounds__(256) conv_prefill_kernel(const ConvParams p) {
     }
   }
   int next = p.cu_seqlens[n + 1];
-  for (int t = tb; t < te; ++t) {
-    if (t >= next) {   // a new sequence starts at t: its window is its state
-      while (n + 1 < p.num_seqs && p.cu_seqlens[n + 1] <= t) ++n;
-      next = p.cu_seqlens[n + 1];
-      load_window<W>(p, n, c0, win);
+  // eight tokens' inputs are loaded together, so that eight loads are in flight
+  constexpr int kAhead = 8;
+  for (int tg = tb; tg < te; tg += kAhead) {
+    float v[kAhead][4];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int t = min(tg + u, te - 1);   // clamped; only t < te is used
+      load4in(x + static_cast<size_t>(t) * p.C + c0, v[u]);
     }
-    float v[4], o[4];
-    load4in(x + static_cast<size_t>(t) * p.C + c0, v);
-    conv_step<W>(w, b, win, v, p.activation, o);
-    store4out(y + static_cast<size_t>(t) * p.C + c0, o);
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int t = tg + u;
+      if (t >= te) break;
+      if (t >= next) {   // a new sequence starts at t: its window is its state
+        while (n + 1 < p.num_seqs && p.cu_seqlens[n + 1] <= t) ++n;
+        next = p.cu_seqlens[n + 1];
+        load_window<W>(p, n, c0, win);
+      }
+      float o[4];
+      conv_step<W>(w, b, win, v[u], p.activation, o);
+      store4out(y + static_cast<size_t>(t) * p.C + c0, o);
+    }
   }
 }
 
@@ -238,39 +255,52 @@ __global__ void __launch_bounds__(256) conv_decode_kernel(const ConvParams p) {
     for (int j = 0; j < W - 1; ++j) st[c * (W - 1) + j] = win[j][c];
 }
 
-// ---- gated RMS norm: one wave per (token, head) group of G elements -----------------------
+// ---- gated RMS norm: G/8 lanes per (token, head) group, 8 elements per lane ------------
+__device__ __forceinline__ void load8e(const uint16_t *p, float (&x)[8]) { load8(p, x); }
+__device__ __forceinline__ void load8e(const float *p, float (&x)[8]) { load8(p, x); }
+__device__ __forceinline__ void store8e(uint16_t *p, const float (&y)[8]) {
+  const float a[4] = {y[0], y[1], y[2], y[3]}, b[4] = {y[4], y[5], y[6], y[7]};
+  store4out(p, a);
+  store4out(p + 4, b);
+}
+__device__ __forceinline__ void store8e(float *p, const float (&y)[8]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(y[0], y[1], y[2], y[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(y[4], y[5], y[6], y[7]);
+}
+
 template <typename T, int G>
 __global__ void __launch_bounds__(256) gated_rmsnorm_kernel(const NormParams p) {
-  constexpr int EPT = G / 64;   // elements per lane (consecutive)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = static_cast<long>(blockIdx.x) * 4 + wave;   // token * heads + head
-  if (row >= p.rows) return;
-  const int head = static_cast<int>(row % p.heads);
-  const T *x = static_cast<const T *>(p.x) + row * G + lane * EPT;
-  const T *z = static_cast<const T *>(p.z) + row * G + lane * EPT;
-  float xv[EPT], zv[EPT], u[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    xv[e] = load_f32(x + e);
-    zv[e] = load_f32(z + e);
-  }
+  constexpr int LPR = G / 8;            // lanes per row
+  constexpr int RPB = 256 / LPR;        // rows per block
+  const int sub = threadIdx.x % LPR;
+  const long row = static_cast<long>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const bool ok = row < p.rows;
+  const long r = ok ? row : p.rows - 1;   // clamped: every lane of a row group reduces
+  const int head = static_cast<int>(r % p.heads);
+  const size_t base = static_cast<size_t>(r) * G + 8 * sub;
+  float xv[8], zv[8], u[8];
+  load8e(static_cast<const T *>(p.x) + base, xv);
+  load8e(static_cast<const T *>(p.z) + base, zv);
   float ss = 0.0f;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
+  for (int e = 0; e < 8; ++e) {
     u[e] = p.norm_before_gate ? xv[e] : xv[e] * silu(zv[e]);
     ss += u[e] * u[e];
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   const float rs = 1.0f / sqrtf(ss / G + p.eps);
-  const float *wt = p.weight + static_cast<size_t>(head) * G + lane * EPT;
-  T *out = static_cast<T *>(p.out) + row * G + lane * EPT;
+  const float *wt = p.weight + static_cast<size_t>(head) * G + 8 * sub;
+  const float4 w0 = *reinterpret_cast<const float4 *>(wt);
+  const float4 w1 = *reinterpret_cast<const float4 *>(wt + 4);
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float yv[8];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    float v = u[e] * rs * wt[e];
-    if (p.norm_before_gate) v *= silu(zv[e]);
-    store_f32(out + e, v);
+  for (int e = 0; e < 8; ++e) {
+    yv[e] = u[e] * rs * wv[e];
+    if (p.norm_before_gate) yv[e] *= silu(zv[e]);
   }
+  if (ok) store8e(static_cast<T *>(p.out) + base, yv);
 }
 
 template <typename T>
@@ -299,10 +329,15 @@ hipError_t conv_dispatch(const ConvParams &p, int mode, hipStream_t s) {
 
 template <typename T>
 hipError_t norm_dispatch(const NormParams &p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((p.rows + 3) / 4)), block(256);
-  if (p.group == 64) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 64>), grid, block, 0, s, p);
-  else if (p.group == 128) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 128>), grid, block, 0, s, p);
-  else if (p.group == 256) hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 256>), grid, block, 0, s, p);
+  const dim3 block(256);
+  auto grid = [&](int g) { return dim3(static_cast<unsigned>((p.rows + 256 / (g / 8) - 1) /
+                                                             (256 / (g / 8)))); };
+  if (p.group == 64)
+    hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 64>), grid(64), block, 0, s, p);
+  else if (p.group == 128)
+    hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 128>), grid(128), block, 0, s, p);
+  else if (p.group == 256)
+    hipLaunchKernelGGL((gated_rmsnorm_kernel<T, 256>), grid(256), block, 0, s, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

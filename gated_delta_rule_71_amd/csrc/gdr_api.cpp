@@ -227,7 +227,8 @@ int gdr_validate_gated_rmsnorm(const gdr_gated_rmsnorm_args *a) {
   if (a->group != 64 && a->group != 128 && a->group != 256) return GDR_ERR_UNSUPPORTED;
   if (a->tokens > 0) {
     if (!a->x || !a->z || !a->weight || !a->out) return GDR_ERR_INVALID_ARG;
-    if (!aligned16(a->x) || !aligned16(a->z) || !aligned16(a->out)) return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->x) || !aligned16(a->z) || !aligned16(a->out) || !aligned16(a->weight))
+      return GDR_ERR_INVALID_ARG;
   }
   return GDR_OK;
 }
