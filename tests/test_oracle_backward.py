@@ -1,0 +1,172 @@
+"""The backward oracle (oracle/backward.py) against facts that do not come from itself.
+
+* its forward pass equals the pinned C oracle (so it differentiates the definition);
+* its gradients equal central finite differences of the C oracle's forward;
+* closed forms: one token from a zero state; beta = 0 (pure decay of H0);
+* the chunked form equals it at many chunk sizes, packed and grouped;
+* planted mistakes in the chunked form are each caught by the chunked check.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as OB
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _unit(r, shape):
+    x = r.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _problem(seed, B=1, T=9, Hk=1, Hv=2, K=4, V=3, decay=0.4, h0=True):
+    r = np.random.default_rng(seed)
+    q = _unit(r, (B, T, Hk, K))
+    k = _unit(r, (B, T, Hk, K))
+    v = r.standard_normal((B, T, Hv, V))
+    g = -decay * r.uniform(0.0, 1.0, (B, T, Hv))
+    beta = r.uniform(0.05, 0.95, (B, T, Hv))
+    s0 = 0.5 * r.standard_normal((B, Hv, K, V)) if h0 else None
+    do = r.standard_normal((B, T, Hv, V))
+    dht = r.standard_normal((B, Hv, K, V))
+    return q, k, v, g, beta, s0, do, dht
+
+
+def _maxdiff(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b)))) if a.size else 0.0
+
+
+def test_forward_equals_c_oracle():
+    q, k, v, g, beta, s0, do, dht = _problem(1, B=2, T=11, Hk=2, Hv=4, K=5, V=5)
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0, scale=0.7,
+                              return_forward=True)
+    o, fs = oracle.prefill(q, k, v, g, beta, initial_state=s0, scale=0.7,
+                           output_final_state=True)
+    assert _maxdiff(res["o"], o) < 1e-13
+    assert _maxdiff(res["final_state"], fs) < 1e-13
+
+
+def _loss_c(q, k, v, g, beta, s0, do, dht, scale):
+    """<o, do> + <H_T, dht> evaluated with the C oracle (an independent forward)."""
+    o, fs = oracle.prefill(q, k, v, g, beta, initial_state=s0, scale=scale,
+                           output_final_state=True)
+    return float(np.sum(o * do) + np.sum(fs * dht))
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_gradients_equal_finite_differences(seed):
+    q, k, v, g, beta, s0, do, dht = _problem(seed, T=6, Hk=1, Hv=2, K=3, V=3)
+    scale = 0.8
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0, scale=scale)
+    args = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "s0": s0}
+    grad_name = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "s0": "dh0"}
+    eps = 1e-6
+    for name, x in args.items():
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            ap, am = dict(args, **{name: xp}), dict(args, **{name: xm})
+            fd[i] = (_loss_c(**ap, do=do, dht=dht, scale=scale)
+                     - _loss_c(**am, do=do, dht=dht, scale=scale)) / (2 * eps)
+        err = _maxdiff(res[grad_name[name]], fd)
+        assert err < 1e-7, (name, err)
+
+
+def test_single_token_closed_form():
+    # one token from a zero state: o = scale beta (k.q) v, H = beta k v^T
+    r = np.random.default_rng(4)
+    K = V = 5
+    q, k = _unit(r, (1, 1, 1, K)), _unit(r, (1, 1, 1, K))
+    v, do = r.standard_normal((1, 1, 1, V)), r.standard_normal((1, 1, 1, V))
+    dht = r.standard_normal((1, 1, K, V))
+    g, beta, scale = np.array([[[-0.3]]]), np.array([[[0.6]]]), 0.9
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, scale=scale)
+    qq, kk, vv, dd, D = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], do[0, 0, 0], dht[0, 0]
+    b, c = 0.6, kk @ qq
+    assert _maxdiff(res["dv"][0, 0, 0], scale * b * c * dd + b * D.T @ kk) < 1e-14
+    assert _maxdiff(res["dq"][0, 0, 0], scale * b * (dd @ vv) * kk) < 1e-14
+    assert _maxdiff(res["dk"][0, 0, 0], scale * b * (dd @ vv) * qq + b * D @ vv) < 1e-14
+    assert _maxdiff(res["dbeta"][0, 0, 0], scale * c * (dd @ vv) + kk @ D @ vv) < 1e-14
+    assert abs(res["dg"][0, 0, 0]) < 1e-15      # a zero state does not see the decay
+
+
+def test_beta_zero_closed_form():
+    # beta = 0: H_t = e^{G_t} H0 and o_t = scale e^{G_t} H0^T q_t
+    q, k, v, g, beta, s0, do, dht = _problem(5, T=7, Hk=1, Hv=1, K=4, V=4)
+    beta = np.zeros_like(beta)
+    scale = 0.6
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0, scale=scale)
+    G = np.cumsum(g[0, :, 0])
+    H0 = s0[0, 0]
+    assert np.max(np.abs(res["dv"])) == 0.0 and np.max(np.abs(res["dk"])) < 1e-15
+    dq = scale * np.exp(G)[:, None] * (do[0, :, 0] @ H0.T)
+    assert _maxdiff(res["dq"][0, :, 0], dq) < 1e-14
+    dh0 = scale * np.einsum("t,tk,tv->kv", np.exp(G), q[0, :, 0], do[0, :, 0]) \
+        + np.exp(G[-1]) * dht[0, 0]
+    assert _maxdiff(res["dh0"][0, 0], dh0) < 1e-14
+    per_t = scale * np.exp(G) * np.einsum("tk,kv,tv->t", q[0, :, 0], H0, do[0, :, 0])
+    per_t[-1] += np.exp(G[-1]) * np.sum(dht[0, 0] * H0)
+    assert _maxdiff(res["dg"][0, :, 0], np.cumsum(per_t[::-1])[::-1]) < 1e-13
+
+
+@pytest.mark.parametrize("C", [1, 5, 16, 64])
+def test_chunked_equals_autograd_packed_grouped(C):
+    r = np.random.default_rng(6)
+    lens = [0, 23, 70, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, _, do, _ = _problem(7, B=1, T=int(cu[-1]), Hk=2, Hv=4, K=5, V=4)
+    s0 = 0.5 * r.standard_normal((len(lens), 4, 5, 4))
+    dht = r.standard_normal((len(lens), 4, 5, 4))
+    a = OB.prefill_backward(q, k, v, g, beta, do, dht, cu_seqlens=cu, initial_state=s0)
+    c = OB.chunked_backward(q, k, v, g, beta, do, dht, chunk_size=C, cu_seqlens=cu,
+                            initial_state=s0)
+    for n in NAMES:
+        assert _maxdiff(c[n], a[n]) < 1e-12, n
+
+
+def test_packed_equals_separate_and_groups_sum():
+    q, k, v, g, beta, s0, do, dht = _problem(8, B=2, T=8, Hk=1, Hv=2, K=3, V=3)
+    batched = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0)
+    cu = np.array([0, 8, 16])
+    packed = OB.prefill_backward(*(x.reshape((1, 16) + x.shape[2:]) for x in (q, k, v, g, beta)),
+                                 do.reshape(1, 16, 2, 3), dht, cu_seqlens=cu, initial_state=s0)
+    for n in NAMES:
+        assert _maxdiff(packed[n].reshape(batched[n].shape), batched[n]) < 1e-14, n
+    # a shared q/k head gets the sum of the gradients of its repeated copies
+    rep = OB.prefill_backward(np.repeat(q, 2, axis=2), np.repeat(k, 2, axis=2), v, g, beta, do,
+                              dht, initial_state=s0)
+    assert _maxdiff(batched["dq"][:, :, 0], rep["dq"].sum(axis=2)) < 1e-14
+    assert _maxdiff(batched["dk"][:, :, 0], rep["dk"].sum(axis=2)) < 1e-14
+
+
+# Planted mistakes in the chunked form: each must break its agreement with autograd.
+CHUNK_MUTANTS = {
+    "dR_not_transposed": ("dR = Tm.T @ dD", "dR = Tm @ dD"),
+    "no_state_path_in_dD": ("dD = P.T @ dOc + Kt @ dHn", "dD = P.T @ dOc"),
+    "dA_sign": ("dA = -np.where(strict, dR @ D.T, 0.0)", "dA = np.where(strict, dR @ D.T, 0.0)"),
+    "no_w_term": ("dG[-1] += np.exp(G[-1]) * np.sum(dHn * H0) + w.sum()",
+                  "dG[-1] += np.exp(G[-1]) * np.sum(dHn * H0)"),
+    "forward_cumsum_dg": ("dg = np.cumsum(dG[::-1])[::-1]", "dg = np.cumsum(dG)"),
+    "no_decay_on_dH0": ("dH0 = np.exp(G[-1]) * dHn", "dH0 = dHn"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_MUTANTS))
+def test_chunked_check_rejects_mutant(name):
+    import inspect
+    src = inspect.getsource(OB)
+    old, new = CHUNK_MUTANTS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("backward_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "backward_mutant", "exec"), mod.__dict__)
+    q, k, v, g, beta, s0, do, dht = _problem(9, T=20, Hk=1, Hv=1, K=4, V=4)
+    a = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0)
+    c = mod.chunked_backward(q, k, v, g, beta, do, dht, chunk_size=8, initial_state=s0)
+    assert max(_maxdiff(c[n], a[n]) for n in NAMES) > 1e-6, name
