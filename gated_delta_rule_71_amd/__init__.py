@@ -26,8 +26,8 @@ import math
 
 from . import _lib
 
-__all__ = ["chunk_gated_delta_rule", "ssm_decode", "causal_conv1d", "causal_conv1d_update",
-           "gated_rmsnorm", "library", "abi_version"]
+__all__ = ["chunk_gated_delta_rule", "chunk_gated_delta_rule_backward", "ssm_decode",
+           "causal_conv1d", "causal_conv1d_update", "gated_rmsnorm", "library", "abi_version"]
 
 
 def library():
@@ -392,3 +392,88 @@ def gated_rmsnorm(x, z, weight, *, eps=1e-5, norm_before_gate=False, out=None, s
     a.x, a.z, a.weight, a.out = _ptr(x), _ptr(z), _ptr(weight), _ptr(out)
     _raise(lib.gdr_gated_rmsnorm(a, _stream(stream)), "gdr_gated_rmsnorm")
     return out
+
+
+def backward_args(q, k, v, g, beta, do, *, dq, dk, dv, dg, dbeta, dh0=None, dht=None,
+                  scale=None, initial_state=None, cu_seqlens=None, workspace=None):
+    """Fill a gdr_backward_args struct from tensors (no checks beyond shapes)."""
+    B, T, Hk, K = q.shape
+    Hv, V = v.shape[-2], v.shape[-1]
+    a = _lib.BackwardArgs()
+    a.batch, a.seqlen = B, T
+    a.num_seqs = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    a.num_qk_heads, a.num_v_heads, a.head_k, a.head_v = Hk, Hv, K, V
+    a.qkv_dtype = _dtype_code(q.dtype)
+    a.scale = float("nan") if scale is None else float(scale)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.initial_state = _ptr(initial_state)
+    a.d_out = _ptr(do)
+    a.d_final_state = _ptr(dht)
+    a.dq, a.dk, a.dv, a.dg, a.dbeta = _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta)
+    a.d_initial_state = _ptr(dh0)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel()
+    return a
+
+
+def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
+                                    initial_state=None, cu_seqlens=None, *, workspace=None,
+                                    stream=None):
+    """Gradients of the chunked prefill (gated delta rule, n_h = 1, gates as given).
+
+    q, k [B,T,Hk,D]; v, do [B,T,Hv,D] (float32 or bfloat16, one dtype); g, beta
+    [B,T,Hv] float32; dht (gradient of the final state) and initial_state float32
+    [N,Hv,D,D] or None; cu_seqlens int32 [N+1] (B must be 1).
+    Returns (dq, dk, dv, dg, dbeta, dh0), float32, shaped like q, k, v, g, beta and
+    the initial state ([N,Hv,D,D]).  ``workspace``: a uint8 GPU tensor of at least
+    the library's gdr_backward_workspace_bytes (allocated here when None).
+    """
+    torch = _torch()
+    lib = library()
+    _check(q, "q", ndim=4)
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        _check(t, name, dtype=q.dtype, ndim=4)
+    _check(g, "g", dtype=torch.float32, ndim=3)
+    _check(beta, "beta", dtype=torch.float32, ndim=3)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
+    for name, st in (("initial_state", initial_state), ("dht", dht)):
+        if st is not None:
+            _check(st, name, dtype=torch.float32, ndim=4)
+    B, T, Hk, K = q.shape
+    Hv, V = v.shape[-2], v.shape[-1]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    dev = q.device
+    f32 = torch.float32
+    dq = torch.empty((B, T, Hk, K), dtype=f32, device=dev)
+    dk = torch.empty((B, T, Hk, K), dtype=f32, device=dev)
+    dv = torch.empty((B, T, Hv, V), dtype=f32, device=dev)
+    dg = torch.empty((B, T, Hv), dtype=f32, device=dev)
+    dbeta = torch.empty((B, T, Hv), dtype=f32, device=dev)
+    dh0 = torch.empty((N, Hv, K, V), dtype=f32, device=dev)
+    a = backward_args(q, k, v, g, beta, do, dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0,
+                      dht=dht, scale=scale, initial_state=initial_state, cu_seqlens=cu_seqlens)
+    need = int(lib.gdr_backward_workspace_bytes(a))
+    if workspace is None:
+        # 256-byte alignment: the caching allocator hands out 512-byte aligned blocks
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", dtype=torch.uint8, ndim=1)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    _raise(lib.gdr_chunk_gated_delta_rule_backward(a, _stream(stream)),
+           "gdr_chunk_gated_delta_rule_backward")
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def backward_workspace_bytes(q, v, *, num_seqs=None, num_qk_heads=None):
+    """gdr_backward_workspace_bytes for these shapes (host-only)."""
+    B, T, Hk, K = q.shape
+    a = _lib.BackwardArgs()
+    a.batch, a.seqlen = B, T
+    a.num_seqs = B if num_seqs is None else int(num_seqs)
+    a.num_qk_heads = Hk if num_qk_heads is None else int(num_qk_heads)
+    a.num_v_heads, a.head_k, a.head_v = v.shape[-2], K, v.shape[-1]
+    a.qkv_dtype = _dtype_code(q.dtype)
+    return int(library().gdr_backward_workspace_bytes(a))

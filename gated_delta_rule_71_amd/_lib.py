@@ -18,7 +18,7 @@ GDR_ERR_WORKSPACE = 3
 GDR_ERR_HIP = 4
 GDR_DTYPE_F32 = 0
 GDR_DTYPE_BF16 = 1
-ABI_VERSION = 2   # GDR_ABI_VERSION the structures below are laid out for
+ABI_VERSION = 3   # GDR_ABI_VERSION the structures below are laid out for
 
 # Every symbol include/gdr.h declares.
 EXPORTS = (
@@ -35,6 +35,9 @@ EXPORTS = (
     "gdr_causal_conv1d_prefill",
     "gdr_causal_conv1d_decode",
     "gdr_gated_rmsnorm",
+    "gdr_validate_backward",
+    "gdr_backward_workspace_bytes",
+    "gdr_chunk_gated_delta_rule_backward",
 )
 
 
@@ -139,6 +142,23 @@ class GatedRMSNormArgs(ctypes.Structure):
     ]
 
 
+class BackwardArgs(ctypes.Structure):
+    """gdr_backward_args."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("num_qk_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("head_k", ctypes.c_int32), ("head_v", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("d_out", ctypes.c_void_p),
+        ("d_final_state", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -179,6 +199,13 @@ def load(path: str = LIB_PATH):
             f = getattr(lib, f"gdr_{name}")
             f.argtypes = [ctypes.POINTER(typ), ctypes.c_void_p]
             f.restype = ctypes.c_int
+        lib.gdr_validate_backward.argtypes = [ctypes.POINTER(BackwardArgs)]
+        lib.gdr_validate_backward.restype = ctypes.c_int
+        lib.gdr_backward_workspace_bytes.argtypes = [ctypes.POINTER(BackwardArgs)]
+        lib.gdr_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdr_chunk_gated_delta_rule_backward.argtypes = [ctypes.POINTER(BackwardArgs),
+                                                            ctypes.c_void_p]
+        lib.gdr_chunk_gated_delta_rule_backward.restype = ctypes.c_int
         if lib.gdr_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{path} has ABI version {lib.gdr_abi_version()}, the bindings "
                                f"expect {ABI_VERSION}: rebuild it")

@@ -1,0 +1,679 @@
+// Chunked backward of the gated delta rule on gfx950 (training through
+// torch_chunk_gated_delta_rule, Megatron Core API page
+// "core.ssm.gated_delta_net.gdn"; the chunked training kernels of the Gated
+// DeltaNet and Gated Delta Product pages).
+//
+// Given the gradients dO of the outputs and dH_T of the final state, produce the
+// gradients of q, k, v, g, beta and the initial state.  With the state kept as
+// H = S^T (K x V) and one chunk of n = 64 tokens entering with state H0
+// (G the cumulative decay inside the chunk, Gamma[r, i] = exp(G_r - G_i)):
+//   forward   A = strict_lower(diag(beta) (K K^T) * Gamma),  T = (I + A)^-1,
+//             R = diag(beta) V - diag(beta e^G) K H0,  D = T R,
+//             O = diag(scale e^G) Q H0 + P D,  P = scale (Q K^T) * Gamma * [i <= r],
+//             H_n = e^{G_n} H0 + K~^T D,  K~ = diag(e^{G_n - G}) K;
+//   backward  dD = P^T dO + K~ dH_n,  dR = T^T dD,  dV = diag(beta) dR,
+//             dH0 = e^{G_n} dH_n + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR,
+//             dA = -strict_lower(dR D^T),  dP = lower(dO D^T),
+//             dQ = diag(scale e^G) dO H0^T + dPs K,
+//             dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) dR H0^T
+//                  + diag(e^{G_n - G}) D dH_n^T,
+//   with dAs = dA * diag(beta) Gamma, dPs = scale dP * Gamma, and dbeta, dg from
+//   the same quantities (row sums, see bwd_grads_kernel).
+// Only the dH0 recursion is sequential over a sequence's chunks; everything else
+// is local to a chunk once the chunk's entering state H0 and leaving gradient
+// dH_n are known.  Hence four launches after a table of chunk offsets:
+//   1. the forward prefill with a boundary state every 64 tokens (the H0 of every
+//      chunk after the first) into the workspace;
+//   2. bwd_local_kernel, one workgroup per (chunk, value head): Gamma, A, P,
+//      T = (I + A)^-1 (forward substitution) and D = T R;
+//   3. bwd_sweep_kernel, one workgroup per (sequence, value head, 32 value
+//      columns), last chunk to first: dH_n of every chunk, dR, dV and dH0;
+//   4. bwd_grads_kernel, one workgroup per (chunk, value head): dQ, dK, dbeta, dg;
+//   5. with grouped heads (Hv > Hk), a sum of dQ, dK over each group.
+// All arithmetic is fp32 on the vector ALUs, with operands tiled through LDS; the
+// cumulative decay is summed in fp64 so that differences of large sums stay exact.
+
+#include "common.hpp"
+#include "gdr_internal.hpp"
+
+namespace gdr {
+namespace {
+
+constexpr int BC = 64;        // tokens per backward chunk
+constexpr int BT = 256;       // threads per workgroup
+constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
+
+// acc[i][j] += sum_p A(r_i, p) B(p, c_j), r_i = ty + 16 i, c_j = tx + 16 j, with
+// A(r, p) = A[r * ars + p * acs] and B(p, c) = B[p * brs + c * bcs] in LDS.  Odd
+// leading dimensions keep the 16 columns a wave reads in distinct banks.
+template <int TM, int TN>
+__device__ __forceinline__ void mm(float (&acc)[TM][TN], const float *A, int ars, int acs,
+                                   const float *B, int brs, int bcs, int P, int ty, int tx) {
+#pragma unroll 4
+  for (int p = 0; p < P; ++p) {
+    float a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = A[(ty + 16 * i) * ars + p * acs];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = B[p * brs + (tx + 16 * j) * bcs];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+}
+
+// the sequence holding global chunk c: the last n with cb[n] <= c
+__device__ __forceinline__ int chunk_seq(const int32_t *cb, int N, int c) {
+  int lo = 0, hi = N;   // cb[lo] <= c < cb[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cb[mid] <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void seq_span(const BackwardParams &p, int n, int &t0, int &t1) {
+  if (p.cu_seqlens) {
+    t0 = p.cu_seqlens[n];
+    t1 = p.cu_seqlens[n + 1];
+  } else {
+    t0 = n * p.seqlen;
+    t1 = t0 + p.seqlen;
+  }
+}
+
+// Per-chunk row factors in LDS: the fp64 cumulative decay G (restarting at the
+// chunk), beta, e^G and e^{G_n - G} (rows past the sequence end carry g = beta = 0,
+// so that G_63 is the decay of the whole chunk).  Wave 0 runs the scan.
+struct RowFactors {
+  double G[BC];
+  float beta[BC], eG[BC], eGl[BC];
+};
+__device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams &p, int h, int ts,
+                                            int rows, int tid) {
+  if (tid < BC) {
+    double x = tid < rows ? static_cast<double>(p.g[static_cast<size_t>(ts + tid) * p.Hv + h]) : 0.0;
+#pragma unroll
+    for (int o = 1; o < BC; o <<= 1) {
+      const double y = __shfl_up(x, o, 64);
+      if (tid >= o) x += y;
+    }
+    const double last = __shfl(x, BC - 1, 64);
+    rf.G[tid] = x;
+    rf.beta[tid] = tid < rows ? p.beta[static_cast<size_t>(ts + tid) * p.Hv + h] : 0.0f;
+    rf.eG[tid] = expf(static_cast<float>(x));
+    rf.eGl[tid] = expf(static_cast<float>(last - x));
+  }
+}
+
+// rows [0, 64) x D of a [tokens, heads, D] input (head `hd`) -> fp32 LDS rows of
+// leading dimension ld; rows past `rows` are zero
+template <typename TIn, int D>
+__device__ __forceinline__ void load_rows(float *dst, int ld, const TIn *src, int heads, int hd,
+                                          int ts, int rows, int col0, int ncols, int tid) {
+  for (int idx = tid; idx < BC * ncols; idx += BT) {
+    const int r = idx / ncols, e = idx % ncols;
+    dst[r * ld + e] = r < rows
+        ? load_f32<TIn>(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + e)
+        : 0.0f;
+  }
+}
+
+// the state a chunk enters with: the initial state for a sequence's first chunk,
+// else the forward's boundary state after the previous chunk (NULL = zeros)
+__device__ __forceinline__ const float *entry_state(const BackwardParams &p, int n, int j, int h,
+                                                    int D) {
+  const size_t ss = static_cast<size_t>(D) * D;
+  if (j == 0)
+    return p.initial_state ? p.initial_state + (static_cast<size_t>(n) * p.Hv + h) * ss : nullptr;
+  return p.states + (static_cast<size_t>(p.bb[n] + j - 1) * p.Hv + h) * ss;
+}
+
+}  // namespace
+
+// chunk table: cb[n] = first global chunk of sequence n (cb[N] = chunk count),
+// bb[n] = first boundary state of sequence n (sum of floor(L_m / 64), m < n)
+__global__ void bwd_table_kernel(const BackwardParams p) {
+  if (threadIdx.x != 0) return;
+  int cb = 0, bb = 0;
+  for (int n = 0; n < p.num_seqs; ++n) {
+    p.cb[n] = cb;
+    p.bb[n] = bb;
+    int t0, t1;
+    seq_span(p, n, t0, t1);
+    const int L = t1 - t0;
+    cb += (L + BC - 1) / BC;
+    bb += L / BC;
+  }
+  p.cb[p.num_seqs] = cb;
+  p.bb[p.num_seqs] = bb;
+}
+
+// Per (chunk, value head): Araw = strict_lower((K K^T) * Gamma), P, T = (I + A)^-1
+// with A = diag(beta) Araw, and D = T R, R = diag(beta) (V - diag(e^G) K H0).
+template <typename TIn, int D>
+__global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
+  constexpr int LDD = D + 1;
+  __shared__ float sK[BC * LDD];
+  __shared__ float sQ[BC * LDD];    // later R
+  __shared__ float sA[BC * LDC];
+  __shared__ float sT[BC * LDC];
+  __shared__ float sH[32 * LDD];    // 32 rows of H0 at a time; also the solve's partial sums
+  __shared__ RowFactors rf;
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= p.cb[p.num_seqs]) return;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int n = chunk_seq(p.cb, p.num_seqs, c);
+  const int j = c - p.cb[n];
+  int t0, t1;
+  seq_span(p, n, t0, t1);
+  const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
+  const int hk = h / (p.Hv / p.Hk);
+
+  load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
+  load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
+  row_factors(rf, p, h, ts, rows, tid);
+  __syncthreads();
+
+  const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+  {
+    float kk[4][4], qk[4][4];
+    zero(kk);
+    zero(qk);
+    mm(kk, sK, LDD, 1, sK, 1, LDD, D, ty, tx);
+    mm(qk, sQ, LDD, 1, sK, 1, LDD, D, ty, tx);
+    float *araw = p.araw + cc * BC * BC;
+    float *pm = p.pmat + cc * BC * BC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = ty + 16 * i, q = tx + 16 * jj;
+        // mask before the exponential
+        const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
+        const float a = q < r ? kk[i][jj] * gam : 0.0f;
+        araw[r * BC + q] = a;
+        pm[r * BC + q] = q <= r ? p.scale * qk[i][jj] * gam : 0.0f;
+        sA[r * LDC + q] = rf.beta[r] * a;
+      }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1 row by row: T_r = e_r - sum_{i<r} A_ri T_i.  Thread (column jc,
+  // part) sums the i = part (mod 4) terms; the four parts meet in LDS.
+  {
+    const int jc = tid & 63, part = tid >> 6;
+    float *red = sH;
+    for (int r = 0; r < BC; ++r) {
+      float s = 0.0f;
+      for (int i = part; i < r; i += 4) s = fmaf(sA[r * LDC + i], sT[i * LDC + jc], s);
+      red[part * BC + jc] = s;
+      __syncthreads();
+      if (part == 0)
+        sT[r * LDC + jc] = (r == jc ? 1.0f : 0.0f) -
+                           ((red[jc] + red[BC + jc]) + (red[2 * BC + jc] + red[3 * BC + jc]));
+      __syncthreads();
+    }
+    float *tm = p.tmat + cc * BC * BC;
+    for (int idx = tid; idx < BC * BC; idx += BT) tm[idx] = sT[(idx / BC) * LDC + idx % BC];
+  }
+
+  // X = K H0, H0 streamed 32 rows at a time
+  constexpr int TN = D / 16;
+  float x[4][TN];
+  zero(x);
+  const float *h0 = entry_state(p, n, j, h, D);
+  if (h0) {
+    for (int kb = 0; kb < D; kb += 32) {
+      __syncthreads();
+      for (int idx = tid; idx < 32 * D; idx += BT)
+        sH[(idx / D) * LDD + idx % D] = h0[static_cast<size_t>(kb + idx / D) * D + idx % D];
+      __syncthreads();
+      mm(x, sK + kb, LDD, 1, sH, LDD, 1, 32, ty, tx);
+    }
+  }
+  // R = diag(beta) (V - diag(e^G) X) -> sQ
+  const TIn *v = static_cast<const TIn *>(p.v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty + 16 * i;
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) {
+      const int col = tx + 16 * jj;
+      const float vv =
+          r < rows ? load_f32<TIn>(v + (static_cast<size_t>(ts + r) * p.Hv + h) * D + col) : 0.0f;
+      sQ[r * LDD + col] = rf.beta[r] * (vv - rf.eG[r] * x[i][jj]);
+    }
+  }
+  __syncthreads();
+  // D = T R
+  float d[4][TN];
+  zero(d);
+  mm(d, sT, LDC, 1, sQ, LDD, 1, BC, ty, tx);
+  float *dm = p.dmat + cc * BC * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) dm[(ty + 16 * i) * D + tx + 16 * jj] = d[i][jj];
+}
+
+// Per (sequence, value head, 32 value columns), last chunk to first, carrying
+// dH (D x 32 columns): store dH_n, then dD = P^T dO + diag(e^{G_n - G}) K dH,
+// dR = T^T dD (kept for bwd_grads_kernel), dV = diag(beta) dR, and
+// dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
+template <typename TIn, int D>
+__global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
+  constexpr int LDD = D + 1, LDV = 33, TMH = D / 16;
+  __shared__ float sK[BC * LDD];
+  __shared__ float sQ[BC * LDD];
+  __shared__ float sP[BC * LDC];
+  __shared__ float sT[BC * LDC];
+  __shared__ float sO[BC * LDV];    // dO columns, later diag(scale e^G) dO
+  __shared__ float sD[BC * LDV];    // dD, later -diag(beta e^G) dR
+  __shared__ float sdH[D * LDV];
+  __shared__ RowFactors rf;
+
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  constexpr int NVT = D / 32;
+  const int vt = blockIdx.x % NVT;
+  const int h = (blockIdx.x / NVT) % p.Hv;
+  const int n = blockIdx.x / NVT / p.Hv;
+  const int col0 = 32 * vt;
+  const int hk = h / (p.Hv / p.Hk);
+  int t0, t1;
+  seq_span(p, n, t0, t1);
+  const int nch = (t1 - t0 + BC - 1) / BC;
+  const size_t ss = static_cast<size_t>(D) * D;
+
+  // dH rows ty + 16 i, columns col0 + tx + 16 j
+  float dh[TMH][2];
+  zero(dh);
+  if (p.d_final_state) {
+    const float *s = p.d_final_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
+#pragma unroll
+    for (int i = 0; i < TMH; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) dh[i][jj] = s[(ty + 16 * i) * D + col0 + tx + 16 * jj];
+  }
+  const TIn *dO = static_cast<const TIn *>(p.d_out);
+  for (int jc = nch - 1; jc >= 0; --jc) {
+    const int c = p.cb[n] + jc;
+    const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
+    const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+    float *dhn = p.dhn + cc * ss;
+#pragma unroll
+    for (int i = 0; i < TMH; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int r = ty + 16 * i, q = tx + 16 * jj;
+        dhn[r * D + col0 + q] = dh[i][jj];
+        sdH[r * LDV + q] = dh[i][jj];
+      }
+    load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
+    load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
+    load_rows<TIn, D>(sO, LDV, dO, p.Hv, h, ts, rows, col0, 32, tid);
+    for (int idx = tid; idx < BC * BC; idx += BT) {
+      const int r = idx / BC, q = idx % BC;
+      sP[r * LDC + q] = p.pmat[cc * BC * BC + idx];
+      sT[r * LDC + q] = p.tmat[cc * BC * BC + idx];
+    }
+    row_factors(rf, p, h, ts, rows, tid);
+    __syncthreads();
+
+    // dD = P^T dO + diag(e^{G_n - G}) (K dH)
+    {
+      float a1[4][2], a2[4][2];
+      zero(a1);
+      zero(a2);
+      mm(a1, sP, 1, LDC, sO, LDV, 1, BC, ty, tx);
+      mm(a2, sK, LDD, 1, sdH, LDV, 1, D, ty, tx);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int r = ty + 16 * i;
+          sD[r * LDV + tx + 16 * jj] = a1[i][jj] + rf.eGl[r] * a2[i][jj];
+        }
+    }
+    __syncthreads();
+    // dR = T^T dD
+    float dr[4][2];
+    zero(dr);
+    mm(dr, sT, 1, LDC, sD, LDV, 1, BC, ty, tx);
+    __syncthreads();
+    {
+      float *drm = p.drmat + cc * BC * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int r = ty + 16 * i, q = tx + 16 * jj;
+          drm[r * D + col0 + q] = dr[i][jj];
+          if (r < rows)
+            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] = rf.beta[r] * dr[i][jj];
+          sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[i][jj];
+        }
+      for (int idx = tid; idx < BC * 32; idx += BT) {
+        const int r = idx / 32, q = idx % 32;
+        sO[r * LDV + q] *= p.scale * rf.eG[r];
+      }
+    }
+    __syncthreads();
+    // dH <- e^{G_n} dH + Q^T (diag(scale e^G) dO) + K^T (-diag(beta e^G) dR)
+    {
+      const float en = rf.eG[BC - 1];
+#pragma unroll
+      for (int i = 0; i < TMH; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) dh[i][jj] *= en;
+      mm(dh, sQ, 1, LDD, sO, LDV, 1, BC, ty, tx);
+      mm(dh, sK, 1, LDD, sD, LDV, 1, BC, ty, tx);
+    }
+    __syncthreads();
+  }
+  if (p.d_initial_state) {
+    float *s = p.d_initial_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
+#pragma unroll
+    for (int i = 0; i < TMH; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) s[(ty + 16 * i) * D + col0 + tx + 16 * jj] = dh[i][jj];
+  }
+}
+
+// Per (chunk, value head): the gradients of q, k (per value head), beta and g.
+//   phase 1 (over 32-column slices of V): dA = -(dR D^T), dP = dO D^T,
+//     U1 = dO H0^T, Ua = dR H0^T, Ub = D dH_n^T, dR_r . v_r and <dH_n, H0>;
+//   phase 2: dAs, dPs, E + F = dA * A + dP * P, dA * Araw (masked to the triangles);
+//   phase 3: dQ = dPs K + diag(scale e^G) U1,
+//            dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub,
+//            dbeta_r = (dA * Araw) row sum + dR_r . v_r - e^{G_r} k_r . Ua_r,
+//            dG_r = rowsum(E + F) - colsum(E + F) + scale e^{G_r} q_r . U1_r
+//                   - beta_r e^{G_r} k_r . Ua_r - w_r,  w_r = e^{G_n - G_r} k_r . Ub_r,
+//            plus e^{G_n} <dH_n, H0> + sum w on the last row; dg = reverse cumsum.
+template <typename TIn, int D>
+__global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
+  constexpr int LDD = D + 1, LDV = 33, TN = D / 16;
+  // phase 1 and phases 2-3 share one LDS arena
+  constexpr int P1 = 4 * BC * LDV + 2 * D * LDV;
+  constexpr int P23 = 4 * BC * LDC + 2 * BC * LDD;
+  constexpr int ARENA = P1 > P23 ? P1 : P23;
+  __shared__ float arena[ARENA];
+  __shared__ RowFactors rf;
+  __shared__ float srow[3][BC];     // row sums of E + F, column sums of E + F, row sums of dA * Araw
+  __shared__ float sdot[4][BC];     // q.U1, k.Ua, k.Ub (per row), dR . v
+  __shared__ float sred[BT / 64];
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= p.cb[p.num_seqs]) return;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int n = chunk_seq(p.cb, p.num_seqs, c);
+  const int j = c - p.cb[n];
+  int t0, t1;
+  seq_span(p, n, t0, t1);
+  const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
+  const int hk = h / (p.Hv / p.Hk);
+  const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+  const size_t ss = static_cast<size_t>(D) * D;
+  row_factors(rf, p, h, ts, rows, tid);
+
+  const float *h0 = entry_state(p, n, j, h, D);
+  const float *dhn = p.dhn + cc * ss;
+  const float *dm = p.dmat + cc * BC * D;
+  const float *drm = p.drmat + cc * BC * D;
+
+  float dA[4][4], dP[4][4], U1[4][TN], Ua[4][TN], Ub[4][TN];
+  zero(dA);
+  zero(dP);
+  zero(U1);
+  zero(Ua);
+  zero(Ub);
+  float hh = 0.0f, rv = 0.0f;
+  {
+    float *sDb = arena, *sRb = sDb + BC * LDV, *sOb = sRb + BC * LDV, *svb = sOb + BC * LDV;
+    float *sHb = svb + BC * LDV, *sGb = sHb + D * LDV;
+    for (int vb = 0; vb < D; vb += 32) {
+      __syncthreads();
+      for (int idx = tid; idx < BC * 32; idx += BT) {
+        const int r = idx / 32, q = idx % 32;
+        sDb[r * LDV + q] = dm[r * D + vb + q];
+        sRb[r * LDV + q] = drm[r * D + vb + q];
+      }
+      load_rows<TIn, D>(sOb, LDV, static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, 32, tid);
+      load_rows<TIn, D>(svb, LDV, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, 32, tid);
+      for (int idx = tid; idx < D * 32; idx += BT) {
+        const int r = idx / 32, q = idx % 32;
+        const float a = h0 ? h0[r * D + vb + q] : 0.0f;
+        const float b = dhn[r * D + vb + q];
+        sHb[r * LDV + q] = a;
+        sGb[r * LDV + q] = b;
+        hh = fmaf(a, b, hh);
+      }
+      __syncthreads();
+      mm(dA, sRb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
+      mm(dP, sOb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
+      mm(U1, sOb, LDV, 1, sHb, 1, LDV, 32, ty, tx);
+      mm(Ua, sRb, LDV, 1, sHb, 1, LDV, 32, ty, tx);
+      mm(Ub, sDb, LDV, 1, sGb, 1, LDV, 32, ty, tx);
+      if (tid < BC)
+        for (int q = 0; q < 32; ++q) rv = fmaf(sRb[tid * LDV + q], svb[tid * LDV + q], rv);
+    }
+  }
+  __syncthreads();
+
+  float *sdAs = arena, *sdPs = sdAs + BC * LDC, *sM1 = sdPs + BC * LDC, *sM2 = sM1 + BC * LDC;
+  float *sK = sM2 + BC * LDC, *sQ = sK + BC * LDD;
+  {
+    const float *araw = p.araw + cc * BC * BC;
+    const float *pm = p.pmat + cc * BC * BC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = ty + 16 * i, q = tx + 16 * jj;
+        const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
+        const float a = q < r ? -dA[i][jj] : 0.0f;
+        const float pp = q <= r ? dP[i][jj] : 0.0f;
+        const float ar = araw[r * BC + q];
+        sdAs[r * LDC + q] = a * rf.beta[r] * gam;
+        sdPs[r * LDC + q] = p.scale * pp * gam;
+        sM1[r * LDC + q] = a * rf.beta[r] * ar + pp * pm[r * BC + q];
+        sM2[r * LDC + q] = a * ar;
+      }
+  }
+  load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
+  load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
+  if (tid < BC) sdot[3][tid] = rv;
+  // <dH_n, H0>: wave sums, then across waves
+  {
+    float s = hh;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if ((tid & 63) == 0) sred[tid >> 6] = s;
+  }
+  __syncthreads();
+
+  if (tid < BC) {
+    float rs = 0.0f, cs = 0.0f, r2 = 0.0f;
+    for (int q = 0; q < BC; ++q) {
+      rs += sM1[tid * LDC + q];
+      cs += sM1[q * LDC + tid];
+      r2 += sM2[tid * LDC + q];
+    }
+    srow[0][tid] = rs;
+    srow[1][tid] = cs;
+    srow[2][tid] = r2;
+  }
+  // row dots of U1, Ua, Ub with the rows of Q and K (16 lanes share a row)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty + 16 * i;
+    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) {
+      const int col = tx + 16 * jj;
+      s1 = fmaf(sQ[r * LDD + col], U1[i][jj], s1);
+      s2 = fmaf(sK[r * LDD + col], Ua[i][jj], s2);
+      s3 = fmaf(sK[r * LDD + col], Ub[i][jj], s3);
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      s1 += __shfl_xor(s1, o, 64);
+      s2 += __shfl_xor(s2, o, 64);
+      s3 += __shfl_xor(s3, o, 64);
+    }
+    if (tx == 0) {
+      sdot[0][r] = s1;
+      sdot[1][r] = s2;
+      sdot[2][r] = s3;
+    }
+  }
+
+  // dQ = dPs K + diag(scale e^G) U1
+  {
+    float dq[4][TN];
+    zero(dq);
+    mm(dq, sdPs, LDC, 1, sK, LDD, 1, BC, ty, tx);
+    float *dst;
+    size_t rs;
+    if (p.Hk == p.Hv) {
+      dst = p.dq + static_cast<size_t>(hk) * D;
+      rs = static_cast<size_t>(p.Hk) * D;
+    } else {
+      dst = p.dq_h + static_cast<size_t>(h) * D;
+      rs = static_cast<size_t>(p.Hv) * D;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ty + 16 * i;
+      if (r < rows)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          dst[static_cast<size_t>(ts + r) * rs + tx + 16 * jj] =
+              dq[i][jj] + p.scale * rf.eG[r] * U1[i][jj];
+    }
+  }
+  // dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub
+  {
+    float dk[4][TN];
+    zero(dk);
+    mm(dk, sdAs, LDC, 1, sK, LDD, 1, BC, ty, tx);
+    mm(dk, sdAs, 1, LDC, sK, LDD, 1, BC, ty, tx);
+    mm(dk, sdPs, 1, LDC, sQ, LDD, 1, BC, ty, tx);
+    float *dst;
+    size_t rs;
+    if (p.Hk == p.Hv) {
+      dst = p.dk + static_cast<size_t>(hk) * D;
+      rs = static_cast<size_t>(p.Hk) * D;
+    } else {
+      dst = p.dk_h + static_cast<size_t>(h) * D;
+      rs = static_cast<size_t>(p.Hv) * D;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ty + 16 * i;
+      if (r < rows)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          dst[static_cast<size_t>(ts + r) * rs + tx + 16 * jj] =
+              dk[i][jj] - rf.beta[r] * rf.eG[r] * Ua[i][jj] + rf.eGl[r] * Ub[i][jj];
+    }
+  }
+  __syncthreads();
+
+  // dbeta and dG per row, then dg = reverse cumulative sum of dG (wave 0)
+  if (tid < BC) {
+    const int r = tid;
+    const float x = sdot[1][r];
+    const float w = rf.eGl[r] * sdot[2][r];
+    float dG = srow[0][r] - srow[1][r] + p.scale * rf.eG[r] * sdot[0][r] -
+               rf.beta[r] * rf.eG[r] * x - w;
+    float wsum = w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+    if (r == BC - 1) {
+      const float hsum = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+      dG += rf.eG[BC - 1] * hsum + wsum;
+    }
+    const float db = srow[2][r] + sdot[3][r] - rf.eG[r] * x;
+    // reverse inclusive scan: dg_r = sum_{r' >= r} dG_r'
+    float s = dG;
+#pragma unroll
+    for (int o = 1; o < BC; o <<= 1) {
+      const float y = __shfl_down(s, o, 64);
+      if (r + o < BC) s += y;
+    }
+    if (r < rows) {
+      p.dbeta[static_cast<size_t>(ts + r) * p.Hv + h] = db;
+      p.dg[static_cast<size_t>(ts + r) * p.Hv + h] = s;
+    }
+  }
+}
+
+// grouped heads: dq[t, hk] = sum of the group's per-value-head dq (same for dk)
+template <int D>
+__global__ void bwd_group_sum_kernel(const BackwardParams p, long total) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int e = static_cast<int>(i % D);
+  const long th = i / D;                 // token * Hk + hk
+  const int hk = static_cast<int>(th % p.Hk);
+  const long t = th / p.Hk;
+  const int grp = p.Hv / p.Hk;
+  float sq = 0.0f, sk = 0.0f;
+  for (int m = 0; m < grp; ++m) {
+    const size_t src = (static_cast<size_t>(t) * p.Hv + hk * grp + m) * D + e;
+    sq += p.dq_h[src];
+    sk += p.dk_h[src];
+  }
+  p.dq[i] = sq;
+  p.dk[i] = sk;
+}
+
+namespace {
+
+template <typename TIn, int D>
+hipError_t launch_bwd_d(const BackwardParams &p, int max_chunks, long tokens, hipStream_t s) {
+  if (max_chunks > 0)
+    hipLaunchKernelGGL((bwd_local_kernel<TIn, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s, p);
+  // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0
+  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, D>), dim3(p.num_seqs * p.Hv * (D / 32)), dim3(BT), 0,
+                     s, p);
+  if (max_chunks > 0)
+    hipLaunchKernelGGL((bwd_grads_kernel<TIn, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s, p);
+  if (p.Hv != p.Hk && tokens > 0) {
+    const long total = tokens * p.Hk * D;
+    hipLaunchKernelGGL((bwd_group_sum_kernel<D>), dim3((total + 255) / 256), dim3(256), 0, s, p,
+                       total);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BackwardParams &p, int qkv_f32, int head, int max_chunks,
+                           long tokens, hipStream_t stream) {
+  if (head == 64)
+    return qkv_f32 ? launch_bwd_d<float, 64>(p, max_chunks, tokens, stream)
+                   : launch_bwd_d<uint16_t, 64>(p, max_chunks, tokens, stream);
+  if (head == 128)
+    return qkv_f32 ? launch_bwd_d<float, 128>(p, max_chunks, tokens, stream)
+                   : launch_bwd_d<uint16_t, 128>(p, max_chunks, tokens, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -186,6 +186,179 @@ int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+// ---- backward ------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carve-up of the backward (byte offsets from the base, each aligned).
+struct BwdLayout {
+  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, total;
+  int max_chunks;
+};
+
+BwdLayout bwd_layout(const gdr_backward_args *a) {
+  BwdLayout L{};
+  const size_t tokens = static_cast<size_t>(a->batch) * a->seqlen;
+  const size_t N = static_cast<size_t>(a->num_seqs);
+  const size_t D = static_cast<size_t>(a->head_k);
+  const size_t Hv = static_cast<size_t>(a->num_v_heads);
+  // chunks: sum of ceil(L_n / 64) <= (tokens + 63 N) / 64; boundary states:
+  // sum of floor(L_n / 64) <= tokens / 64
+  const size_t chunks = (tokens + 63 * N) / 64;
+  const size_t entries = tokens / 64;
+  L.max_chunks = static_cast<int>(chunks);
+  const size_t elem = a->qkv_dtype == GDR_DTYPE_F32 ? 4 : 2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes);
+    return at;
+  };
+  L.tab = take(2 * (N + 1) * sizeof(int32_t));
+  L.states = take(entries * Hv * D * D * 4);
+  L.o = take(tokens * Hv * D * elem);
+  L.dhn = take(chunks * Hv * D * D * 4);
+  L.araw = take(chunks * Hv * 64 * 64 * 4);
+  L.pmat = take(chunks * Hv * 64 * 64 * 4);
+  L.tmat = take(chunks * Hv * 64 * 64 * 4);
+  L.dmat = take(chunks * Hv * 64 * D * 4);
+  L.drmat = take(chunks * Hv * 64 * D * 4);
+  const bool grouped = a->num_v_heads != a->num_qk_heads;
+  L.dqh = take(grouped ? tokens * Hv * D * 4 : 0);
+  L.dkh = take(grouped ? tokens * Hv * D * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+int gdr_validate_backward(const gdr_backward_args *a) {
+  if (!a) return GDR_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->seqlen < 0 || a->num_seqs < 0) return GDR_ERR_INVALID_ARG;
+  if (a->num_qk_heads <= 0 || a->num_v_heads <= 0) return GDR_ERR_INVALID_ARG;
+  if (a->num_v_heads % a->num_qk_heads != 0) return GDR_ERR_INVALID_ARG;
+  if (a->head_k <= 0 || a->head_v <= 0) return GDR_ERR_INVALID_ARG;
+  if (!dtype_ok(a->qkv_dtype)) return GDR_ERR_INVALID_ARG;
+  if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (a->cu_seqlens) {
+    if (a->batch != 1) return GDR_ERR_INVALID_ARG;
+  } else if (a->num_seqs != a->batch) {
+    return GDR_ERR_INVALID_ARG;
+  }
+  if (a->head_k != a->head_v || !head_ok(a->head_k)) return GDR_ERR_UNSUPPORTED;
+  const int64_t tokens = int64_t{a->batch} * a->seqlen;
+  if (tokens > kMaxRows) return GDR_ERR_UNSUPPORTED;
+  {
+    const int64_t kw = int64_t{a->num_qk_heads} * a->head_k;
+    const int64_t vw = int64_t{a->num_v_heads} * a->head_v;
+    if (tokens * (kw > vw ? kw : vw) >= (int64_t{1} << 32)) return GDR_ERR_UNSUPPORTED;
+  }
+  if (int64_t{a->num_seqs} * a->num_v_heads * (a->head_v / 32) > kMaxRows)
+    return GDR_ERR_UNSUPPORTED;
+  if (tokens > 0) {
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->d_out) return GDR_ERR_INVALID_ARG;
+    if (!a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta) return GDR_ERR_INVALID_ARG;
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->d_out))
+      return GDR_ERR_INVALID_ARG;
+  }
+  if ((a->initial_state && !aligned16(a->initial_state)) ||
+      (a->d_final_state && !aligned16(a->d_final_state)))
+    return GDR_ERR_INVALID_ARG;
+  if (a->num_seqs > 0) {
+    if (a->workspace_bytes < gdr_backward_workspace_bytes(a)) return GDR_ERR_WORKSPACE;
+    if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & (kAlign - 1)) != 0)
+      return GDR_ERR_WORKSPACE;
+  }
+  return GDR_OK;
+}
+
+size_t gdr_backward_workspace_bytes(const gdr_backward_args *a) {
+  if (!a || a->num_seqs <= 0 || a->batch < 0 || a->seqlen < 0 || a->head_k <= 0 ||
+      a->num_v_heads <= 0 || a->num_qk_heads <= 0)
+    return 0;
+  return bwd_layout(a).total;
+}
+
+int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream) {
+  const int st = gdr_validate_backward(a);
+  if (st != GDR_OK) return st;
+  if (a->num_seqs == 0) return GDR_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const BwdLayout L = bwd_layout(a);
+  char *ws = static_cast<char *>(a->workspace);
+  const long tokens = static_cast<long>(a->batch) * a->seqlen;
+
+  gdr::BackwardParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.g = a->g;
+  p.beta = a->beta;
+  p.cu_seqlens = a->cu_seqlens;
+  p.initial_state = a->initial_state;
+  p.d_out = a->d_out;
+  p.d_final_state = a->d_final_state;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.dg = a->dg;
+  p.dbeta = a->dbeta;
+  p.d_initial_state = a->d_initial_state;
+  p.seqlen = a->seqlen;
+  p.num_seqs = a->num_seqs;
+  p.Hk = a->num_qk_heads;
+  p.Hv = a->num_v_heads;
+  p.scale = isnan(a->scale) ? 1.0f / sqrtf(static_cast<float>(a->head_k)) : a->scale;
+  p.cb = reinterpret_cast<int32_t *>(ws + L.tab);
+  p.bb = p.cb + (a->num_seqs + 1);
+  p.states = reinterpret_cast<float *>(ws + L.states);
+  p.dhn = reinterpret_cast<float *>(ws + L.dhn);
+  p.araw = reinterpret_cast<float *>(ws + L.araw);
+  p.pmat = reinterpret_cast<float *>(ws + L.pmat);
+  p.tmat = reinterpret_cast<float *>(ws + L.tmat);
+  p.dmat = reinterpret_cast<float *>(ws + L.dmat);
+  p.drmat = reinterpret_cast<float *>(ws + L.drmat);
+  p.dq_h = reinterpret_cast<float *>(ws + L.dqh);
+  p.dk_h = reinterpret_cast<float *>(ws + L.dkh);
+
+  if (gdr::launch_backward_table(p, s) != hipSuccess) return GDR_ERR_HIP;
+  if (tokens > 0) {
+    // forward recompute: the state after every 64 tokens of each sequence
+    gdr_prefill_args f{};
+    f.batch = a->batch;
+    f.seqlen = a->seqlen;
+    f.num_seqs = a->num_seqs;
+    f.num_qk_heads = a->num_qk_heads;
+    f.num_v_heads = a->num_v_heads;
+    f.head_k = a->head_k;
+    f.head_v = a->head_v;
+    f.num_householder = 1;
+    f.chunk_size = 64;
+    f.qkv_dtype = a->qkv_dtype;
+    f.out_dtype = a->qkv_dtype;
+    f.use_qk_l2norm = 0;
+    f.scale = a->scale;
+    f.q = a->q;
+    f.k = a->k;
+    f.v = a->v;
+    f.g = a->g;
+    f.beta = a->beta;
+    f.cu_seqlens = a->cu_seqlens;
+    f.initial_state = a->initial_state;
+    f.out = ws + L.o;
+    f.boundary_states = p.states;
+    f.boundary_interval = 64;
+    const int fs = gdr_chunk_gated_delta_rule(&f, stream);
+    if (fs != GDR_OK) return fs;
+  }
+  const hipError_t e = gdr::launch_backward(p, a->qkv_dtype == GDR_DTYPE_F32, a->head_k,
+                                            L.max_chunks, tokens, s);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
 int gdr_validate_conv_prefill(const gdr_conv_prefill_args *a) {
   if (!a) return GDR_ERR_INVALID_ARG;
   if (a->tokens < 0 || a->num_seqs < 1 || a->channels <= 0 || a->channels % 4 != 0)

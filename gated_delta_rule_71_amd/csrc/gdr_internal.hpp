@@ -87,6 +87,41 @@ struct NormParams {
   float eps;
 };
 
+struct BackwardParams {
+  const void *q;                 // [Tt, Hk, D]
+  const void *k;                 // [Tt, Hk, D]
+  const void *v;                 // [Tt, Hv, D]
+  const float *g;                // [Tt, Hv]
+  const float *beta;             // [Tt, Hv]
+  const int32_t *cu_seqlens;     // NULL: batched
+  const float *initial_state;    // [N, Hv, D, D] or NULL (zeros)
+  const void *d_out;             // [Tt, Hv, D], q's dtype
+  const float *d_final_state;    // [N, Hv, D, D] or NULL (zeros)
+  float *dq;                     // [Tt, Hk, D]
+  float *dk;                     // [Tt, Hk, D]
+  float *dv;                     // [Tt, Hv, D]
+  float *dg;                     // [Tt, Hv]
+  float *dbeta;                  // [Tt, Hv]
+  float *d_initial_state;        // [N, Hv, D, D] or NULL (not written)
+  int seqlen;
+  int num_seqs;
+  int Hk;
+  int Hv;
+  float scale;
+  // workspace
+  int32_t *cb;                   // [N + 1] first chunk of each sequence
+  int32_t *bb;                   // [N + 1] first boundary state of each sequence
+  float *states;                 // [E, Hv, D, D] forward state after every 64 tokens
+  float *dhn;                    // [chunks, Hv, D, D] gradient of the state leaving a chunk
+  float *araw;                   // [chunks, Hv, 64, 64] strict_lower((K K^T) * Gamma)
+  float *pmat;                   // [chunks, Hv, 64, 64] scale (Q K^T) * Gamma, causal
+  float *tmat;                   // [chunks, Hv, 64, 64] (I + A)^-1
+  float *dmat;                   // [chunks, Hv, 64, D] D = T R
+  float *drmat;                  // [chunks, Hv, 64, D] dR = T^T dD
+  float *dq_h;                   // [Tt, Hv, D] per value head (grouped heads only)
+  float *dk_h;                   // [Tt, Hv, D]
+};
+
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k);
 // State waves (32 value columns each) per prefill workgroup.
@@ -99,5 +134,9 @@ hipError_t launch_decode(const DecodeParams &p, int qkv_f32, int dk, int dv, int
 // mode 0: prefill (outputs, then conv states); mode 1: decode
 hipError_t launch_conv(const ConvParams &p, int f32, int mode, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const NormParams &p, int f32, hipStream_t stream);
+// the chunk table of the backward, then its kernels (after the forward recompute)
+hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream);
+hipError_t launch_backward(const BackwardParams &p, int qkv_f32, int head, int max_chunks,
+                           long tokens, hipStream_t stream);
 
 }  // namespace gdr

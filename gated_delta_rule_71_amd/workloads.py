@@ -283,3 +283,39 @@ def config3(n=128, num_slots=256, Hk=16, Hv=32, K=128, V=128, num_padding=16, se
     return DecodeWorkload(f"decode_bf16_n{n}_slots{num_slots}_Hk{Hk}_Hv{Hv}_D{K}", BF16, q, k,
                           v, g, beta, cache, idx, meta={"seed": seed, "padding_rows":
                                                         pad_rows.tolist()})
+
+
+@dataclass
+class BackwardWorkload:
+    """Inputs of a backward call: the forward's inputs (dense initial states) plus
+    the upstream gradients of the outputs and of the final state."""
+    fwd: PrefillWorkload
+    do: np.ndarray                  # [B,T,Hv,V] storage dtype, ~ N(0,1)
+    dht: Optional[np.ndarray]       # [N,Hv,K,V] float32 ~ N(0,1), or None
+
+
+def backward_workload(name, seed, *, Hk, Hv, D, dtype, B=1, T=None, lengths=None,
+                      decay="config", initial_state=True, final_grad=True):
+    """Backward inputs: batched (B, T) or packed (``lengths``, B = 1), q/k/v/g/beta as
+    in the forward recipe, initial states ~ N(0, 0.1), dO and dH_T ~ N(0, 1)."""
+    rng = np.random.default_rng([seed, 0xBAC])
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        N = len(lengths)
+        cu = np.zeros(N + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B, T = 1, int(cu[-1])
+    else:
+        N, cu = B, None
+    q = store(_unit_rows(rng, (B, T, Hk, D)), dtype)
+    k = store(_unit_rows(rng, (B, T, Hk, D)), dtype)
+    v = store(rng.standard_normal((B, T, Hv, D), dtype=np.float32), dtype)
+    beta = _beta(rng, (B, T, Hv))
+    g = _gates(rng, T, Hv, decay, batch=B)
+    h0 = (0.1 * rng.standard_normal((N, Hv, D, D), dtype=np.float32)).astype(np.float32) \
+        if initial_state else None
+    fwd = PrefillWorkload(name, dtype, q, k, v, g, beta, 64, 1, cu_seqlens=cu,
+                          initial_state=h0, meta={"seed": seed, "decay": decay})
+    do = store(rng.standard_normal((B, T, Hv, D), dtype=np.float32), dtype)
+    dht = rng.standard_normal((N, Hv, D, D), dtype=np.float32) if final_grad else None
+    return BackwardWorkload(fwd, do, dht)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 typedef enum {
@@ -279,6 +279,61 @@ typedef struct {
   void *out;
 } gdr_gated_rmsnorm_args;
 
+/*
+ * Chunked backward of the gated delta rule (training through
+ * torch_chunk_gated_delta_rule, page "core.ssm.gated_delta_net.gdn"; the chunked
+ * training kernels of the Gated DeltaNet and Gated Delta Product pages).  Given
+ * d_out = dL/do and d_final_state = dL/dS_T of some loss L of the forward call
+ * with the same inputs, writes dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and
+ * dL/d(initial_state).  The forward states every 64 tokens are recomputed inside
+ * the call (into the workspace), so nothing from the forward call is needed.
+ *
+ * Shapes (Tt = batch * seqlen tokens; with cu_seqlens, batch must be 1; n_h = 1):
+ *   q, k [Tt, Hk, D]; v, d_out [Tt, Hv, D] (qkv_dtype, one dtype for all four);
+ *   g, beta [Tt, Hv] float32; initial_state, d_final_state [N, Hv, D, D] float32
+ *   (the [K, V] layout of states) or NULL (zeros);
+ *   outputs, all float32: dq, dk [Tt, Hk, D] (a q/k head receives the sum over
+ *   the value heads that read it), dv [Tt, Hv, D], dg, dbeta [Tt, Hv],
+ *   d_initial_state [N, Hv, D, D] or NULL (not written).
+ * Gates are taken as given (gate_mode 0) and q, k without the L2 norm; dg and
+ *   dbeta are the gradients with respect to those gate values.
+ * Workspace: gdr_backward_workspace_bytes(args) bytes of device memory, 256-byte
+ *   aligned, owned by the caller; its contents on entry do not matter.  It holds
+ *   per 64-token chunk and value head the entering state, the gradient of the
+ *   leaving state and five 64 x 64 or 64 x D float32 matrices (about
+ *   2 D^2 + 3 * 64^2 + 2 * 64 D floats, 200 KiB at D = 128).
+ * Supported: head_k == head_v = D in {64, 128}; q/k/v/d_out F32 or BF16.
+ * The outputs must not alias the inputs or the workspace.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t seqlen;
+  int32_t num_seqs;
+  int32_t num_qk_heads;     /* Hk                                                   */
+  int32_t num_v_heads;      /* Hv                                                   */
+  int32_t head_k;           /* D                                                    */
+  int32_t head_v;           /* must equal head_k                                    */
+  int32_t qkv_dtype;        /* gdr_dtype of q, k, v and d_out                       */
+  float scale;              /* NaN => 1/sqrt(head_k)                                */
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *g;
+  const float *beta;
+  const int32_t *cu_seqlens;
+  const float *initial_state;
+  const void *d_out;
+  const float *d_final_state;
+  float *dq;
+  float *dk;
+  float *dv;
+  float *dg;
+  float *dbeta;
+  float *d_initial_state;
+  void *workspace;
+  size_t workspace_bytes;
+} gdr_backward_args;
+
 /* Version of this ABI (GDR_ABI_VERSION). */
 int gdr_abi_version(void);
 
@@ -303,6 +358,11 @@ int gdr_validate_gated_rmsnorm(const gdr_gated_rmsnorm_args *args);
 int gdr_causal_conv1d_prefill(const gdr_conv_prefill_args *args, void *stream);
 int gdr_causal_conv1d_decode(const gdr_conv_decode_args *args, void *stream);
 int gdr_gated_rmsnorm(const gdr_gated_rmsnorm_args *args, void *stream);
+
+/* Host-only checks, workspace size and enqueue of the chunked backward. */
+int gdr_validate_backward(const gdr_backward_args *args);
+size_t gdr_backward_workspace_bytes(const gdr_backward_args *args);
+int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *args, void *stream);
 
 #ifdef __cplusplus
 }

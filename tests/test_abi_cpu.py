@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdr_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.gdr_abi_version() == _lib.ABI_VERSION == 3
     for code, name in [(0, "GDR_OK"), (1, "GDR_ERR_INVALID_ARG"), (2, "GDR_ERR_UNSUPPORTED"),
                        (3, "GDR_ERR_WORKSPACE"), (4, "GDR_ERR_HIP"), (99, "GDR_ERR_UNKNOWN")]:
         assert lib.gdr_status_string(code).decode() == name
@@ -148,3 +148,52 @@ def test_invalid_call_launches_nothing(lib):
 def test_python_binding_raises_without_fallback(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def _backward(**kw):
+    a = _lib.BackwardArgs()
+    base = dict(batch=2, seqlen=100, num_seqs=2, num_qk_heads=2, num_v_heads=4, head_k=128,
+                head_v=128, qkv_dtype=1, scale=math.nan, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+                beta=FAKE, d_out=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE,
+                workspace=FAKE)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    if "workspace_bytes" not in kw:
+        a.workspace_bytes = _lib.load().gdr_backward_workspace_bytes(ctypes.byref(a))
+    return a
+
+
+def test_backward_workspace_size(lib):
+    a = _backward()
+    need = lib.gdr_backward_workspace_bytes(ctypes.byref(a))
+    # 2 sequences of 100 tokens (cu_seqlens may be anything on the device, so the
+    # host sizes for the most chunks any split of 200 tokens into 2 sequences has:
+    # (200 + 63 * 2) // 64 = 5), 200 // 64 = 3 boundary states, Hv = 4, D = 128
+    chunks, entries, Hv, D = 5, 3, 4, 128
+    floats = entries * Hv * D * D + chunks * Hv * (D * D + 3 * 64 * 64 + 2 * 64 * D) \
+        + 2 * 200 * Hv * D
+    assert need >= floats * 4 + 200 * Hv * D * 2
+    assert need < floats * 4 + 200 * Hv * D * 2 + 16 * 256
+    assert lib.gdr_validate_backward(ctypes.byref(a)) == _lib.GDR_OK
+    same_heads = _backward(num_qk_heads=4)
+    assert lib.gdr_backward_workspace_bytes(ctypes.byref(same_heads)) < need
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_v=64), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(head_k=96, head_v=96), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(num_v_heads=3), _lib.GDR_ERR_INVALID_ARG),
+    (dict(qkv_dtype=7), _lib.GDR_ERR_INVALID_ARG),
+    (dict(scale=math.inf), _lib.GDR_ERR_INVALID_ARG),
+    (dict(num_seqs=3), _lib.GDR_ERR_INVALID_ARG),
+    (dict(cu_seqlens=FAKE), _lib.GDR_ERR_INVALID_ARG),   # needs batch = 1
+    (dict(dg=None), _lib.GDR_ERR_INVALID_ARG),
+    (dict(d_out=FAKE + 4), _lib.GDR_ERR_INVALID_ARG),
+    (dict(workspace_bytes=1024), _lib.GDR_ERR_WORKSPACE),
+    (dict(workspace=FAKE + 16), _lib.GDR_ERR_WORKSPACE),
+])
+def test_backward_validation(lib, kw, code):
+    assert lib.gdr_validate_backward(ctypes.byref(_backward(**kw))) == code
+    # the enqueue entry point runs the same checks and launches nothing on error
+    assert lib.gdr_chunk_gated_delta_rule_backward(ctypes.byref(_backward(**kw)), None) == code
