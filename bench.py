@@ -1,9 +1,9 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs prefill,decode,gdp,gates,boundary,conv_norm]
+                    [--legs prefill,decode,gdp,gates,boundary,conv_norm,backward]
 
-Six legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Seven legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
@@ -22,6 +22,10 @@ Six legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   conv_norm: the short causal conv over the workload's V/K/Q projection (prefill
            and a 128-request decode step) and the gated RMS norm of its output;
            kernel times and achieved bandwidth.
+  backward: the chunked backward (gradients of q, k, v, g, beta and the initial
+           state) at B=4, T=4096, H=16, D=128, bf16 inputs; one call = the forward
+           recompute plus the backward kernels; tokens/s and the fraction of the
+           fp32 vector peak its dense contractions reach.
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -44,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s (H=32,K=V=128) + decode state GB/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2516.6   # dense fp16/bf16
+FP32_VALU_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -51,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary,conv_norm")
+    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary,conv_norm,backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -345,6 +350,56 @@ def run_conv_norm_leg(wl2, steps, warmup):
     }
 
 
+def backward_flops_per_token(Hv, D, C=64):
+    """Dense-tile flops per token of the backward kernels (forward recompute excluded):
+    per chunk and value head, eleven C x C x D products (K K^T, Q K^T, T R; P^T dO,
+    T^T dD; dR D^T, dO D^T, dPs K, dAs K, dAs^T K, dPs^T Q) and seven C x D x D ones
+    (K H0; K dH, Q^T dO, K^T dR; dO H0^T, dR H0^T, D dH^T), 2 flops per multiply-add."""
+    return Hv * (22 * C * D + 14 * D * D)
+
+
+def run_backward_leg(steps, warmup):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    from gated_delta_rule_71_amd import workloads as W
+    bw = W.backward_workload("bwd_bf16_B4_T4096_H16_D128", 1, Hk=16, Hv=16, D=128, dtype=W.BF16,
+                             B=4, T=4096, decay="config")
+    f = bw.fwd
+    d = {n: up(getattr(f, n)) for n in ("q", "k", "v", "g", "beta")}
+    do, dht, h0 = up(bw.do), up(bw.dht), up(f.initial_state)
+    gdr.chunk_gated_delta_rule_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], do, dht=dht,
+                                        initial_state=h0)
+    B, T, Hk, D = f.q.shape
+    Hv = f.v.shape[2]
+    outs = [torch.empty(s, dtype=torch.float32, device="cuda")
+            for s in ((B, T, Hk, D), (B, T, Hk, D), (B, T, Hv, D), (B, T, Hv), (B, T, Hv),
+                      (B, Hv, D, D))]
+    a = gdr.backward_args(d["q"], d["k"], d["v"], d["g"], d["beta"], do, dq=outs[0],
+                          dk=outs[1], dv=outs[2], dg=outs[3], dbeta=outs[4], dh0=outs[5],
+                          dht=dht, initial_state=h0)
+    lib = gdr.library()
+    ws = torch.empty(int(lib.gdr_backward_workspace_bytes(a)), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def launch():
+        rc = lib.gdr_chunk_gated_delta_rule_backward(a, stream)
+        assert rc == 0, rc
+
+    wall, kern = time_launches(launch, steps, warmup)
+    tokens = B * T
+    F = backward_flops_per_token(Hv, D)
+    tf = F * tokens / (kern * 1e-3) / 1e12
+    return {"workload": bw.fwd.name, "tokens": tokens, "call_ms": kern, "wall_ms": wall,
+            "value": tokens / (kern * 1e-3), "unit": "tokens/s",
+            "workspace_bytes": ws.numel(),
+            "flops_per_token": F, "achieved_tflops": tf,
+            "alu": {"bound": "alu", "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / FP32_VALU_PEAK_TFLOPS,
+                    "note": "backward contractions run as fp32 vector FMAs; the call time "
+                            "includes the forward recompute"}}
+
+
 def profile_run():
     """3 prefill launches, 3 decode launches (cache flushed before each) and a copy probe."""
     import torch
@@ -468,6 +523,12 @@ def main():
             print(f"[bench] boundary states every {iv}: {kb:.3f} ms ({E} entries)",
                   file=sys.stderr, flush=True)
 
+    # ---- chunked backward at the batched training shape ------------------------------
+    if "backward" in legs:
+        res["backward"] = run_backward_leg(max(2, args.steps // 4), min(args.warmup, 2))
+        print(f"[bench] backward: {res['backward']['call_ms']:.3f} ms per call",
+              file=sys.stderr, flush=True)
+
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -555,6 +616,8 @@ def main():
         line["boundary_states"] = res["boundary"]
     if "conv_norm" in res:
         line["conv_norm"] = res["conv_norm"]
+    if "backward" in res:
+        line["backward"] = res["backward"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     line["bench_wall_s"] = time.perf_counter() - t_start

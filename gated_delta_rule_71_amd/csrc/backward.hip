@@ -115,16 +115,58 @@ __device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams
   }
 }
 
-// rows [0, 64) x D of a [tokens, heads, D] input (head `hd`) -> fp32 LDS rows of
-// leading dimension ld; rows past `rows` are zero
-template <typename TIn, int D>
+// rows [0, 64) x NC columns (from col0) of a [tokens, heads, D] input (head `hd`)
+// -> fp32 LDS rows of leading dimension ld; rows past `rows` are zero.  Every
+// thread issues all of its 8-element loads (addresses clamped to the sequence)
+// before it converts and stores any of them.
+template <typename TIn, int D, int NC>
 __device__ __forceinline__ void load_rows(float *dst, int ld, const TIn *src, int heads, int hd,
-                                          int ts, int rows, int col0, int ncols, int tid) {
-  for (int idx = tid; idx < BC * ncols; idx += BT) {
-    const int r = idx / ncols, e = idx % ncols;
-    dst[r * ld + e] = r < rows
-        ? load_f32<TIn>(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + e)
-        : 0.0f;
+                                          int ts, int rows, int col0, int tid) {
+  constexpr int SEGS = NC / 8, UNITS = BC * SEGS, PER = (UNITS + BT - 1) / BT;
+  Seg8<TIn> buf[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int u = tid + j * BT;
+    const int r = min(u / SEGS, rows - 1), sg = u % SEGS;
+    if (UNITS % BT == 0 || u < UNITS)
+      buf[j].load(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + 8 * sg);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int u = tid + j * BT;
+    const int r = u / SEGS, sg = u % SEGS;
+    if (UNITS % BT == 0 || u < UNITS) {
+      float x[8];
+      buf[j].get(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[r * ld + 8 * sg + e] = r < rows ? x[e] : 0.0f;
+    }
+  }
+}
+
+// an NR x NC float32 matrix (global row stride gs; NULL reads as zeros) -> LDS
+// (leading dimension ld), all 16-byte loads issued first
+template <int NR, int NC>
+__device__ __forceinline__ void load_mat(float *dst, int ld, const float *src, size_t gs, int tid) {
+  constexpr int Q4 = NC / 4, UNITS = NR * Q4, PER = (UNITS + BT - 1) / BT;
+  float4 buf[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int u = tid + j * BT;
+    buf[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (src && (UNITS % BT == 0 || u < UNITS))
+      buf[j] = *reinterpret_cast<const float4 *>(src + (u / Q4) * gs + 4 * (u % Q4));
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int u = tid + j * BT;
+    if (UNITS % BT == 0 || u < UNITS) {
+      float *d = dst + (u / Q4) * ld + 4 * (u % Q4);
+      d[0] = buf[j].x;
+      d[1] = buf[j].y;
+      d[2] = buf[j].z;
+      d[3] = buf[j].w;
+    }
   }
 }
 
@@ -180,8 +222,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
   const int hk = h / (p.Hv / p.Hk);
 
-  load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
-  load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
+  load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
   row_factors(rf, p, h, ts, rows, tid);
   __syncthreads();
 
@@ -236,23 +278,22 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   if (h0) {
     for (int kb = 0; kb < D; kb += 32) {
       __syncthreads();
-      for (int idx = tid; idx < 32 * D; idx += BT)
-        sH[(idx / D) * LDD + idx % D] = h0[static_cast<size_t>(kb + idx / D) * D + idx % D];
+      load_mat<32, D>(sH, LDD, h0 + static_cast<size_t>(kb) * D, D, tid);
       __syncthreads();
       mm(x, sK + kb, LDD, 1, sH, LDD, 1, 32, ty, tx);
     }
   }
-  // R = diag(beta) (V - diag(e^G) X) -> sQ
-  const TIn *v = static_cast<const TIn *>(p.v);
+  // R = diag(beta) (V - diag(e^G) X) -> sQ (V is staged there first)
+  __syncthreads();
+  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = ty + 16 * i;
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) {
-      const int col = tx + 16 * jj;
-      const float vv =
-          r < rows ? load_f32<TIn>(v + (static_cast<size_t>(ts + r) * p.Hv + h) * D + col) : 0.0f;
-      sQ[r * LDD + col] = rf.beta[r] * (vv - rf.eG[r] * x[i][jj]);
+      float &y = sQ[r * LDD + tx + 16 * jj];
+      y = rf.beta[r] * (y - rf.eG[r] * x[i][jj]);
     }
   }
   __syncthreads();
@@ -319,14 +360,11 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
         dhn[r * D + col0 + q] = dh[i][jj];
         sdH[r * LDV + q] = dh[i][jj];
       }
-    load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
-    load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
-    load_rows<TIn, D>(sO, LDV, dO, p.Hv, h, ts, rows, col0, 32, tid);
-    for (int idx = tid; idx < BC * BC; idx += BT) {
-      const int r = idx / BC, q = idx % BC;
-      sP[r * LDC + q] = p.pmat[cc * BC * BC + idx];
-      sT[r * LDC + q] = p.tmat[cc * BC * BC + idx];
-    }
+    load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+    load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+    load_rows<TIn, D, 32>(sO, LDV, dO, p.Hv, h, ts, rows, col0, tid);
+    load_mat<BC, BC>(sP, LDC, p.pmat + cc * BC * BC, BC, tid);
+    load_mat<BC, BC>(sT, LDC, p.tmat + cc * BC * BC, BC, tid);
     row_factors(rf, p, h, ts, rows, tid);
     __syncthreads();
 
@@ -443,22 +481,19 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     float *sHb = svb + BC * LDV, *sGb = sHb + D * LDV;
     for (int vb = 0; vb < D; vb += 32) {
       __syncthreads();
-      for (int idx = tid; idx < BC * 32; idx += BT) {
-        const int r = idx / 32, q = idx % 32;
-        sDb[r * LDV + q] = dm[r * D + vb + q];
-        sRb[r * LDV + q] = drm[r * D + vb + q];
-      }
-      load_rows<TIn, D>(sOb, LDV, static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, 32, tid);
-      load_rows<TIn, D>(svb, LDV, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, 32, tid);
+      load_mat<BC, 32>(sDb, LDV, dm + vb, D, tid);
+      load_mat<BC, 32>(sRb, LDV, drm + vb, D, tid);
+      load_rows<TIn, D, 32>(sOb, LDV, static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb,
+                            tid);
+      load_rows<TIn, D, 32>(svb, LDV, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
+      load_mat<D, 32>(sHb, LDV, h0 ? h0 + vb : nullptr, D, tid);
+      load_mat<D, 32>(sGb, LDV, dhn + vb, D, tid);
+      __syncthreads();
+      // <dH_n, H0> over this slice (each thread its share of the elements)
       for (int idx = tid; idx < D * 32; idx += BT) {
         const int r = idx / 32, q = idx % 32;
-        const float a = h0 ? h0[r * D + vb + q] : 0.0f;
-        const float b = dhn[r * D + vb + q];
-        sHb[r * LDV + q] = a;
-        sGb[r * LDV + q] = b;
-        hh = fmaf(a, b, hh);
+        hh = fmaf(sHb[r * LDV + q], sGb[r * LDV + q], hh);
       }
-      __syncthreads();
       mm(dA, sRb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
       mm(dP, sOb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
       mm(U1, sOb, LDV, 1, sHb, 1, LDV, 32, ty, tx);
@@ -490,8 +525,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         sM2[r * LDC + q] = a * ar;
       }
   }
-  load_rows<TIn, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, D, tid);
-  load_rows<TIn, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, D, tid);
+  load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
   if (tid < BC) sdot[3][tid] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
