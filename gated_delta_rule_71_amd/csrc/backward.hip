@@ -40,10 +40,13 @@ namespace gdr {
 namespace {
 
 constexpr int BC = 64;        // tokens per backward chunk
-constexpr int BT = 256;       // threads per workgroup
+constexpr int BT = 512;       // threads per workgroup (two waves per SIMD)
+constexpr int RS = BT / 16;   // rows between the output rows of one thread
+constexpr int TM = BC / RS;   // a thread's rows of a 64-row output tile
+constexpr int NPART = BT / 64;
 constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
 
-// acc[i][j] += sum_p A(r_i, p) B(p, c_j), r_i = ty + 16 i, c_j = tx + 16 j, with
+// acc[i][j] += sum_p A(r_i, p) B(p, c_j), r_i = ty + RS i, c_j = tx + 16 j, with
 // A(r, p) = A[r * ars + p * acs] and B(p, c) = B[p * brs + c * bcs] in LDS.  Odd
 // leading dimensions keep the 16 columns a wave reads in distinct banks.
 template <int TM, int TN>
@@ -53,7 +56,7 @@ __device__ __forceinline__ void mm(float (&acc)[TM][TN], const float *A, int ars
   for (int p = 0; p < P; ++p) {
     float a[TM], b[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = A[(ty + 16 * i) * ars + p * acs];
+    for (int i = 0; i < TM; ++i) a[i] = A[(ty + RS * i) * ars + p * acs];
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = B[p * brs + (tx + 16 * j) * bcs];
 #pragma unroll
@@ -229,7 +232,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 
   const size_t cc = static_cast<size_t>(c) * p.Hv + h;
   {
-    float kk[4][4], qk[4][4];
+    float kk[TM][4], qk[TM][4];
     zero(kk);
     zero(qk);
     mm(kk, sK, LDD, 1, sK, 1, LDD, D, ty, tx);
@@ -237,10 +240,10 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
     float *araw = p.araw + cc * BC * BC;
     float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int r = ty + 16 * i, q = tx + 16 * jj;
+        const int r = ty + RS * i, q = tx + 16 * jj;
         // mask before the exponential
         const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
         const float a = q < r ? kk[i][jj] * gam : 0.0f;
@@ -252,18 +255,21 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   __syncthreads();
 
   // T = (I + A)^-1 row by row: T_r = e_r - sum_{i<r} A_ri T_i.  Thread (column jc,
-  // part) sums the i = part (mod 4) terms; the four parts meet in LDS.
+  // part) sums the i = part (mod NPART) terms; the parts meet in LDS.
   {
     const int jc = tid & 63, part = tid >> 6;
     float *red = sH;
     for (int r = 0; r < BC; ++r) {
       float s = 0.0f;
-      for (int i = part; i < r; i += 4) s = fmaf(sA[r * LDC + i], sT[i * LDC + jc], s);
+      for (int i = part; i < r; i += NPART) s = fmaf(sA[r * LDC + i], sT[i * LDC + jc], s);
       red[part * BC + jc] = s;
       __syncthreads();
-      if (part == 0)
-        sT[r * LDC + jc] = (r == jc ? 1.0f : 0.0f) -
-                           ((red[jc] + red[BC + jc]) + (red[2 * BC + jc] + red[3 * BC + jc]));
+      if (part == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NPART; ++m) t += red[m * BC + jc];
+        sT[r * LDC + jc] = (r == jc ? 1.0f : 0.0f) - t;
+      }
       __syncthreads();
     }
     float *tm = p.tmat + cc * BC * BC;
@@ -272,7 +278,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 
   // X = K H0, H0 streamed 32 rows at a time
   constexpr int TN = D / 16;
-  float x[4][TN];
+  float x[TM][TN];
   zero(x);
   const float *h0 = entry_state(p, n, j, h, D);
   if (h0) {
@@ -288,8 +294,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = ty + 16 * i;
+  for (int i = 0; i < TM; ++i) {
+    const int r = ty + RS * i;
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) {
       float &y = sQ[r * LDD + tx + 16 * jj];
@@ -298,14 +304,14 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   }
   __syncthreads();
   // D = T R
-  float d[4][TN];
+  float d[TM][TN];
   zero(d);
   mm(d, sT, LDC, 1, sQ, LDD, 1, BC, ty, tx);
   float *dm = p.dmat + cc * BC * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) dm[(ty + 16 * i) * D + tx + 16 * jj] = d[i][jj];
+    for (int jj = 0; jj < TN; ++jj) dm[(ty + RS * i) * D + tx + 16 * jj] = d[i][jj];
 }
 
 // Per (sequence, value head, 32 value columns), last chunk to first, carrying
@@ -314,7 +320,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 // dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = 33, TMH = D / 16;
+  constexpr int LDD = D + 1, LDV = 33, TMH = D / RS;
   __shared__ float sK[BC * LDD];
   __shared__ float sQ[BC * LDD];
   __shared__ float sP[BC * LDC];
@@ -336,7 +342,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   const int nch = (t1 - t0 + BC - 1) / BC;
   const size_t ss = static_cast<size_t>(D) * D;
 
-  // dH rows ty + 16 i, columns col0 + tx + 16 j
+  // dH rows ty + RS i, columns col0 + tx + 16 j
   float dh[TMH][2];
   zero(dh);
   if (p.d_final_state) {
@@ -344,7 +350,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 #pragma unroll
     for (int i = 0; i < TMH; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) dh[i][jj] = s[(ty + 16 * i) * D + col0 + tx + 16 * jj];
+      for (int jj = 0; jj < 2; ++jj) dh[i][jj] = s[(ty + RS * i) * D + col0 + tx + 16 * jj];
   }
   const TIn *dO = static_cast<const TIn *>(p.d_out);
   for (int jc = nch - 1; jc >= 0; --jc) {
@@ -356,7 +362,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     for (int i = 0; i < TMH; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const int r = ty + 16 * i, q = tx + 16 * jj;
+        const int r = ty + RS * i, q = tx + 16 * jj;
         dhn[r * D + col0 + q] = dh[i][jj];
         sdH[r * LDV + q] = dh[i][jj];
       }
@@ -370,32 +376,32 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 
     // dD = P^T dO + diag(e^{G_n - G}) (K dH)
     {
-      float a1[4][2], a2[4][2];
+      float a1[TM][2], a2[TM][2];
       zero(a1);
       zero(a2);
       mm(a1, sP, 1, LDC, sO, LDV, 1, BC, ty, tx);
       mm(a2, sK, LDD, 1, sdH, LDV, 1, D, ty, tx);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int r = ty + 16 * i;
+          const int r = ty + RS * i;
           sD[r * LDV + tx + 16 * jj] = a1[i][jj] + rf.eGl[r] * a2[i][jj];
         }
     }
     __syncthreads();
     // dR = T^T dD
-    float dr[4][2];
+    float dr[TM][2];
     zero(dr);
     mm(dr, sT, 1, LDC, sD, LDV, 1, BC, ty, tx);
     __syncthreads();
     {
       float *drm = p.drmat + cc * BC * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int r = ty + 16 * i, q = tx + 16 * jj;
+          const int r = ty + RS * i, q = tx + 16 * jj;
           drm[r * D + col0 + q] = dr[i][jj];
           if (r < rows)
             p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] = rf.beta[r] * dr[i][jj];
@@ -424,7 +430,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 #pragma unroll
     for (int i = 0; i < TMH; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) s[(ty + 16 * i) * D + col0 + tx + 16 * jj] = dh[i][jj];
+      for (int jj = 0; jj < 2; ++jj) s[(ty + RS * i) * D + col0 + tx + 16 * jj] = dh[i][jj];
   }
 }
 
@@ -469,7 +475,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   const float *dm = p.dmat + cc * BC * D;
   const float *drm = p.drmat + cc * BC * D;
 
-  float dA[4][4], dP[4][4], U1[4][TN], Ua[4][TN], Ub[4][TN];
+  float dA[TM][4], dP[TM][4], U1[TM][TN], Ua[TM][TN], Ub[TM][TN];
   zero(dA);
   zero(dP);
   zero(U1);
@@ -511,10 +517,10 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     const float *araw = p.araw + cc * BC * BC;
     const float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int r = ty + 16 * i, q = tx + 16 * jj;
+        const int r = ty + RS * i, q = tx + 16 * jj;
         const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
         const float a = q < r ? -dA[i][jj] : 0.0f;
         const float pp = q <= r ? dP[i][jj] : 0.0f;
@@ -550,8 +556,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   }
   // row dots of U1, Ua, Ub with the rows of Q and K (16 lanes share a row)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = ty + 16 * i;
+  for (int i = 0; i < TM; ++i) {
+    const int r = ty + RS * i;
     float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj) {
@@ -575,7 +581,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 
   // dQ = dPs K + diag(scale e^G) U1
   {
-    float dq[4][TN];
+    float dq[TM][TN];
     zero(dq);
     mm(dq, sdPs, LDC, 1, sK, LDD, 1, BC, ty, tx);
     float *dst;
@@ -588,8 +594,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       rs = static_cast<size_t>(p.Hv) * D;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ty + 16 * i;
+    for (int i = 0; i < TM; ++i) {
+      const int r = ty + RS * i;
       if (r < rows)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj)
@@ -599,7 +605,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   }
   // dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub
   {
-    float dk[4][TN];
+    float dk[TM][TN];
     zero(dk);
     mm(dk, sdAs, LDC, 1, sK, LDD, 1, BC, ty, tx);
     mm(dk, sdAs, 1, LDC, sK, LDD, 1, BC, ty, tx);
@@ -614,8 +620,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       rs = static_cast<size_t>(p.Hv) * D;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ty + 16 * i;
+    for (int i = 0; i < TM; ++i) {
+      const int r = ty + RS * i;
       if (r < rows)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj)
@@ -636,7 +642,9 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
     if (r == BC - 1) {
-      const float hsum = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+      float hsum = 0.0f;
+#pragma unroll
+      for (int m = 0; m < BT / 64; ++m) hsum += sred[m];
       dG += rf.eG[BC - 1] * hsum + wsum;
     }
     const float db = srow[2][r] + sdot[3][r] - rf.eG[r] * x;
