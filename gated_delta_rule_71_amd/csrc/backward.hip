@@ -30,8 +30,9 @@
 //      columns), last chunk to first: dH_n of every chunk, dR, dV and dH0;
 //   4. bwd_grads_kernel, one workgroup per (chunk, value head): dQ, dK, dbeta, dg;
 //   5. with grouped heads (Hv > Hk), a sum of dQ, dK over each group.
-// All arithmetic is fp32 on the vector ALUs, with operands tiled through LDS; the
-// cumulative decay is summed in fp64 so that differences of large sums stay exact.
+// The contractions run on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with
+// operands in LDS; the cumulative decay is summed in fp64 so that differences of
+// large sums stay exact.
 
 #include "common.hpp"
 #include "gdr_internal.hpp"
@@ -41,37 +42,51 @@ namespace {
 
 constexpr int BC = 64;        // tokens per backward chunk
 constexpr int BT = 512;       // threads per workgroup (two waves per SIMD)
-constexpr int RS = BT / 16;   // rows between the output rows of one thread
-constexpr int TM = BC / RS;   // a thread's rows of a 64-row output tile
+constexpr int NW = BT / 64;   // waves per workgroup
 constexpr int NPART = BT / 64;
 constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
 
-// acc[i][j] += sum_p A(r_i, p) B(p, c_j), r_i = ty + RS i, c_j = tx + 16 j, with
-// A(r, p) = A[r * ars + p * acs] and B(p, c) = B[p * brs + c * bcs] in LDS.  Odd
-// leading dimensions keep the 16 columns a wave reads in distinct banks.
-template <int TM, int TN>
-__device__ __forceinline__ void mm(float (&acc)[TM][TN], const float *A, int ars, int acs,
-                                   const float *B, int brs, int bcs, int P, int ty, int tx) {
+// Wave-tiled fp32 matrix-core products.  An M x N output is cut into 16 x 16
+// tiles, numbered row by row; wave w owns the TPW consecutive tiles w*TPW ..
+// w*TPW + TPW - 1, which lie in one tile row (TPW divides N / 16).  Lane l holds,
+// of each of its tiles, column l % 16 and rows 4 (l / 16) + v, v = 0..3: the
+// accumulator layout of v_mfma_f32_16x16x4f32, whose operands are A[l % 16][l / 16]
+// (16 rows x 4) and B[l / 16][l % 16] (4 x 16 columns).
+template <int N, int TPW>
+struct WTile {
+  static_assert((N / 16) % TPW == 0, "a wave's tiles share one tile row");
+  int r0, c0;
+  __device__ __forceinline__ explicit WTile(int wave) {
+    const int idx = wave * TPW;
+    r0 = (idx / (N / 16)) * 16;
+    c0 = (idx % (N / 16)) * 16;
+  }
+  __device__ __forceinline__ int row(int v, int lane) const { return r0 + 4 * (lane >> 4) + v; }
+  __device__ __forceinline__ int col(int t, int lane) const { return c0 + 16 * t + (lane & 15); }
+};
+
+// acc[t] += A(rows of the tile row, p) B(p, columns of tile t) over p in [0, P),
+// A(r, p) = A[r * ars + p * acs], B(p, c) = B[p * brs + c * bcs] in LDS, P % 4 == 0
+template <int N, int TPW>
+__device__ __forceinline__ void mmf(f32x4 (&acc)[TPW], const WTile<N, TPW> &w, const float *A,
+                                    int ars, int acs, const float *B, int brs, int bcs, int P,
+                                    int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const float *a = A + (w.r0 + i) * ars + g * acs;
+  const float *b = B + g * brs + (w.c0 + i) * bcs;
 #pragma unroll 4
-  for (int p = 0; p < P; ++p) {
-    float a[TM], b[TN];
+  for (int p = 0; p < P; p += 4) {
+    const float av = a[p * acs];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = A[(ty + RS * i) * ars + p * acs];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = B[p * brs + (tx + 16 * j) * bcs];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int t = 0; t < TPW; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[p * brs + 16 * t * bcs], acc[t], 0, 0, 0);
   }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
+template <int TPW>
+__device__ __forceinline__ void zero(f32x4 (&acc)[TPW]) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+  for (int t = 0; t < TPW; ++t) acc[t] = zero4();
 }
 
 // the sequence holding global chunk c: the last n with cb[n] <= c
@@ -208,8 +223,10 @@ __global__ void bwd_table_kernel(const BackwardParams p) {
 template <typename TIn, int D>
 __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   constexpr int LDD = D + 1;
+  constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
+  constexpr int TPD = (BC / 16) * (D / 16) / NW;    // 64 x D tiles per wave
   __shared__ float sK[BC * LDD];
-  __shared__ float sQ[BC * LDD];    // later R
+  __shared__ float sQ[BC * LDD];    // later V, then R
   __shared__ float sA[BC * LDC];
   __shared__ float sT[BC * LDC];
   __shared__ float sH[32 * LDD];    // 32 rows of H0 at a time; also the solve's partial sums
@@ -217,7 +234,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= p.cb[p.num_seqs]) return;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = chunk_seq(p.cb, p.num_seqs, c);
   const int j = c - p.cb[n];
   int t0, t1;
@@ -232,23 +249,24 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 
   const size_t cc = static_cast<size_t>(c) * p.Hv + h;
   {
-    float kk[TM][4], qk[TM][4];
+    const WTile<BC, TPC> w(wave);
+    f32x4 kk[TPC], qk[TPC];
     zero(kk);
     zero(qk);
-    mm(kk, sK, LDD, 1, sK, 1, LDD, D, ty, tx);
-    mm(qk, sQ, LDD, 1, sK, 1, LDD, D, ty, tx);
+    mmf(kk, w, sK, LDD, 1, sK, 1, LDD, D, lane);
+    mmf(qk, w, sQ, LDD, 1, sK, 1, LDD, D, lane);
     float *araw = p.araw + cc * BC * BC;
     float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int t = 0; t < TPC; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = ty + RS * i, q = tx + 16 * jj;
+      for (int v = 0; v < 4; ++v) {
+        const int r = w.row(v, lane), q = w.col(t, lane);
         // mask before the exponential
         const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
-        const float a = q < r ? kk[i][jj] * gam : 0.0f;
+        const float a = q < r ? kk[t][v] * gam : 0.0f;
         araw[r * BC + q] = a;
-        pm[r * BC + q] = q <= r ? p.scale * qk[i][jj] * gam : 0.0f;
+        pm[r * BC + q] = q <= r ? p.scale * qk[t][v] * gam : 0.0f;
         sA[r * LDC + q] = rf.beta[r] * a;
       }
   }
@@ -277,8 +295,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   }
 
   // X = K H0, H0 streamed 32 rows at a time
-  constexpr int TN = D / 16;
-  float x[TM][TN];
+  const WTile<D, TPD> wd(wave);
+  f32x4 x[TPD];
   zero(x);
   const float *h0 = entry_state(p, n, j, h, D);
   if (h0) {
@@ -286,7 +304,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
       __syncthreads();
       load_mat<32, D>(sH, LDD, h0 + static_cast<size_t>(kb) * D, D, tid);
       __syncthreads();
-      mm(x, sK + kb, LDD, 1, sH, LDD, 1, 32, ty, tx);
+      mmf(x, wd, sK + kb, LDD, 1, sH, LDD, 1, 32, lane);
     }
   }
   // R = diag(beta) (V - diag(e^G) X) -> sQ (V is staged there first)
@@ -294,24 +312,23 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = ty + RS * i;
+  for (int t = 0; t < TPD; ++t)
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) {
-      float &y = sQ[r * LDD + tx + 16 * jj];
-      y = rf.beta[r] * (y - rf.eG[r] * x[i][jj]);
+    for (int v = 0; v < 4; ++v) {
+      const int r = wd.row(v, lane);
+      float &y = sQ[r * LDD + wd.col(t, lane)];
+      y = rf.beta[r] * (y - rf.eG[r] * x[t][v]);
     }
-  }
   __syncthreads();
   // D = T R
-  float d[TM][TN];
+  f32x4 d[TPD];
   zero(d);
-  mm(d, sT, LDC, 1, sQ, LDD, 1, BC, ty, tx);
+  mmf(d, wd, sT, LDC, 1, sQ, LDD, 1, BC, lane);
   float *dm = p.dmat + cc * BC * D;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int t = 0; t < TPD; ++t)
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) dm[(ty + RS * i) * D + tx + 16 * jj] = d[i][jj];
+    for (int v = 0; v < 4; ++v) dm[wd.row(v, lane) * D + wd.col(t, lane)] = d[t][v];
 }
 
 // Per (sequence, value head, 32 value columns), last chunk to first, carrying
@@ -320,7 +337,9 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 // dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = 33, TMH = D / RS;
+  constexpr int LDD = D + 1, LDV = 33;
+  constexpr int TPH = (D / 16) * 2 / NW;   // D x 32 tiles per wave
+  constexpr int TPS = (BC / 16) * 2 / NW;  // 64 x 32 tiles per wave
   __shared__ float sK[BC * LDD];
   __shared__ float sQ[BC * LDD];
   __shared__ float sP[BC * LDC];
@@ -330,7 +349,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   __shared__ float sdH[D * LDV];
   __shared__ RowFactors rf;
 
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NVT = D / 32;
   const int vt = blockIdx.x % NVT;
   const int h = (blockIdx.x / NVT) % p.Hv;
@@ -342,15 +361,16 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   const int nch = (t1 - t0 + BC - 1) / BC;
   const size_t ss = static_cast<size_t>(D) * D;
 
-  // dH rows ty + RS i, columns col0 + tx + 16 j
-  float dh[TMH][2];
+  const WTile<32, TPH> wh(wave);
+  const WTile<32, TPS> ws(wave);
+  f32x4 dh[TPH];
   zero(dh);
   if (p.d_final_state) {
     const float *s = p.d_final_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
 #pragma unroll
-    for (int i = 0; i < TMH; ++i)
+    for (int t = 0; t < TPH; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) dh[i][jj] = s[(ty + RS * i) * D + col0 + tx + 16 * jj];
+      for (int v = 0; v < 4; ++v) dh[t][v] = s[wh.row(v, lane) * D + col0 + wh.col(t, lane)];
   }
   const TIn *dO = static_cast<const TIn *>(p.d_out);
   for (int jc = nch - 1; jc >= 0; --jc) {
@@ -359,12 +379,12 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     const size_t cc = static_cast<size_t>(c) * p.Hv + h;
     float *dhn = p.dhn + cc * ss;
 #pragma unroll
-    for (int i = 0; i < TMH; ++i)
+    for (int t = 0; t < TPH; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int r = ty + RS * i, q = tx + 16 * jj;
-        dhn[r * D + col0 + q] = dh[i][jj];
-        sdH[r * LDV + q] = dh[i][jj];
+      for (int v = 0; v < 4; ++v) {
+        const int r = wh.row(v, lane), q = wh.col(t, lane);
+        dhn[r * D + col0 + q] = dh[t][v];
+        sdH[r * LDV + q] = dh[t][v];
       }
     load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
     load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
@@ -376,36 +396,36 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 
     // dD = P^T dO + diag(e^{G_n - G}) (K dH)
     {
-      float a1[TM][2], a2[TM][2];
+      f32x4 a1[TPS], a2[TPS];
       zero(a1);
       zero(a2);
-      mm(a1, sP, 1, LDC, sO, LDV, 1, BC, ty, tx);
-      mm(a2, sK, LDD, 1, sdH, LDV, 1, D, ty, tx);
+      mmf(a1, ws, sP, 1, LDC, sO, LDV, 1, BC, lane);
+      mmf(a2, ws, sK, LDD, 1, sdH, LDV, 1, D, lane);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TPS; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int r = ty + RS * i;
-          sD[r * LDV + tx + 16 * jj] = a1[i][jj] + rf.eGl[r] * a2[i][jj];
+        for (int v = 0; v < 4; ++v) {
+          const int r = ws.row(v, lane);
+          sD[r * LDV + ws.col(t, lane)] = a1[t][v] + rf.eGl[r] * a2[t][v];
         }
     }
     __syncthreads();
     // dR = T^T dD
-    float dr[TM][2];
+    f32x4 dr[TPS];
     zero(dr);
-    mm(dr, sT, 1, LDC, sD, LDV, 1, BC, ty, tx);
+    mmf(dr, ws, sT, 1, LDC, sD, LDV, 1, BC, lane);
     __syncthreads();
     {
       float *drm = p.drmat + cc * BC * D;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < TPS; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int r = ty + RS * i, q = tx + 16 * jj;
-          drm[r * D + col0 + q] = dr[i][jj];
+        for (int v = 0; v < 4; ++v) {
+          const int r = ws.row(v, lane), q = ws.col(t, lane);
+          drm[r * D + col0 + q] = dr[t][v];
           if (r < rows)
-            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] = rf.beta[r] * dr[i][jj];
-          sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[i][jj];
+            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] = rf.beta[r] * dr[t][v];
+          sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[t][v];
         }
       for (int idx = tid; idx < BC * 32; idx += BT) {
         const int r = idx / 32, q = idx % 32;
@@ -417,20 +437,18 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     {
       const float en = rf.eG[BC - 1];
 #pragma unroll
-      for (int i = 0; i < TMH; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) dh[i][jj] *= en;
-      mm(dh, sQ, 1, LDD, sO, LDV, 1, BC, ty, tx);
-      mm(dh, sK, 1, LDD, sD, LDV, 1, BC, ty, tx);
+      for (int t = 0; t < TPH; ++t) dh[t] *= en;
+      mmf(dh, wh, sQ, 1, LDD, sO, LDV, 1, BC, lane);
+      mmf(dh, wh, sK, 1, LDD, sD, LDV, 1, BC, lane);
     }
     __syncthreads();
   }
   if (p.d_initial_state) {
     float *s = p.d_initial_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
 #pragma unroll
-    for (int i = 0; i < TMH; ++i)
+    for (int t = 0; t < TPH; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) s[(ty + RS * i) * D + col0 + tx + 16 * jj] = dh[i][jj];
+      for (int v = 0; v < 4; ++v) s[wh.row(v, lane) * D + col0 + wh.col(t, lane)] = dh[t][v];
   }
 }
 
@@ -446,20 +464,24 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 //            plus e^{G_n} <dH_n, H0> + sum w on the last row; dg = reverse cumsum.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = 33, TN = D / 16;
+  constexpr int LDD = D + 1, LDV = 33;
+  constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
+  constexpr int TPD = (BC / 16) * (D / 16) / NW;    // 64 x D tiles per wave
+  constexpr int HALVES = NW / (BC / 16);            // waves sharing one tile row of 64 x D
   // phase 1 and phases 2-3 share one LDS arena
   constexpr int P1 = 4 * BC * LDV + 2 * D * LDV;
   constexpr int P23 = 4 * BC * LDC + 2 * BC * LDD;
   constexpr int ARENA = P1 > P23 ? P1 : P23;
   __shared__ float arena[ARENA];
   __shared__ RowFactors rf;
-  __shared__ float srow[3][BC];     // row sums of E + F, column sums of E + F, row sums of dA * Araw
-  __shared__ float sdot[4][BC];     // q.U1, k.Ua, k.Ub (per row), dR . v
-  __shared__ float sred[BT / 64];
+  __shared__ float srow[3][BC];         // row sums of E + F, column sums of E + F, row sums of dA * Araw
+  __shared__ float sdot[3][HALVES][BC]; // q.U1, k.Ua, k.Ub per row, one partial per wave of a tile row
+  __shared__ float srv[BC];             // dR . v per row
+  __shared__ float sred[NW];
 
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= p.cb[p.num_seqs]) return;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = chunk_seq(p.cb, p.num_seqs, c);
   const int j = c - p.cb[n];
   int t0, t1;
@@ -475,7 +497,9 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   const float *dm = p.dmat + cc * BC * D;
   const float *drm = p.drmat + cc * BC * D;
 
-  float dA[TM][4], dP[TM][4], U1[TM][TN], Ua[TM][TN], Ub[TM][TN];
+  const WTile<BC, TPC> wc(wave);
+  const WTile<D, TPD> wd(wave);
+  f32x4 dA[TPC], dP[TPC], U1[TPD], Ua[TPD], Ub[TPD];
   zero(dA);
   zero(dP);
   zero(U1);
@@ -500,11 +524,11 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         const int r = idx / 32, q = idx % 32;
         hh = fmaf(sHb[r * LDV + q], sGb[r * LDV + q], hh);
       }
-      mm(dA, sRb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
-      mm(dP, sOb, LDV, 1, sDb, 1, LDV, 32, ty, tx);
-      mm(U1, sOb, LDV, 1, sHb, 1, LDV, 32, ty, tx);
-      mm(Ua, sRb, LDV, 1, sHb, 1, LDV, 32, ty, tx);
-      mm(Ub, sDb, LDV, 1, sGb, 1, LDV, 32, ty, tx);
+      mmf(dA, wc, sRb, LDV, 1, sDb, 1, LDV, 32, lane);
+      mmf(dP, wc, sOb, LDV, 1, sDb, 1, LDV, 32, lane);
+      mmf(U1, wd, sOb, LDV, 1, sHb, 1, LDV, 32, lane);
+      mmf(Ua, wd, sRb, LDV, 1, sHb, 1, LDV, 32, lane);
+      mmf(Ub, wd, sDb, LDV, 1, sGb, 1, LDV, 32, lane);
       if (tid < BC)
         for (int q = 0; q < 32; ++q) rv = fmaf(sRb[tid * LDV + q], svb[tid * LDV + q], rv);
     }
@@ -517,13 +541,13 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     const float *araw = p.araw + cc * BC * BC;
     const float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int t = 0; t < TPC; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = ty + RS * i, q = tx + 16 * jj;
+      for (int v = 0; v < 4; ++v) {
+        const int r = wc.row(v, lane), q = wc.col(t, lane);
         const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
-        const float a = q < r ? -dA[i][jj] : 0.0f;
-        const float pp = q <= r ? dP[i][jj] : 0.0f;
+        const float a = q < r ? -dA[t][v] : 0.0f;
+        const float pp = q <= r ? dP[t][v] : 0.0f;
         const float ar = araw[r * BC + q];
         sdAs[r * LDC + q] = a * rf.beta[r] * gam;
         sdPs[r * LDC + q] = p.scale * pp * gam;
@@ -533,13 +557,13 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   }
   load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
   load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
-  if (tid < BC) sdot[3][tid] = rv;
+  if (tid < BC) srv[tid] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
     float s = hh;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if ((tid & 63) == 0) sred[tid >> 6] = s;
+    if (lane == 0) sred[wave] = s;
   }
   __syncthreads();
 
@@ -554,17 +578,18 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     srow[1][tid] = cs;
     srow[2][tid] = r2;
   }
-  // row dots of U1, Ua, Ub with the rows of Q and K (16 lanes share a row)
+  // row dots of U1, Ua, Ub with the rows of Q and K: the 16 lanes of a lane group
+  // hold one row's columns of a tile; the HALVES waves of a tile row add in LDS
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = ty + RS * i;
+  for (int v = 0; v < 4; ++v) {
+    const int r = wd.row(v, lane);
     float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) {
-      const int col = tx + 16 * jj;
-      s1 = fmaf(sQ[r * LDD + col], U1[i][jj], s1);
-      s2 = fmaf(sK[r * LDD + col], Ua[i][jj], s2);
-      s3 = fmaf(sK[r * LDD + col], Ub[i][jj], s3);
+    for (int t = 0; t < TPD; ++t) {
+      const int col = wd.col(t, lane);
+      s1 = fmaf(sQ[r * LDD + col], U1[t][v], s1);
+      s2 = fmaf(sK[r * LDD + col], Ua[t][v], s2);
+      s3 = fmaf(sK[r * LDD + col], Ub[t][v], s3);
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) {
@@ -572,18 +597,19 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       s2 += __shfl_xor(s2, o, 64);
       s3 += __shfl_xor(s3, o, 64);
     }
-    if (tx == 0) {
-      sdot[0][r] = s1;
-      sdot[1][r] = s2;
-      sdot[2][r] = s3;
+    if ((lane & 15) == 0) {
+      const int half = wave % HALVES;
+      sdot[0][half][r] = s1;
+      sdot[1][half][r] = s2;
+      sdot[2][half][r] = s3;
     }
   }
 
   // dQ = dPs K + diag(scale e^G) U1
   {
-    float dq[TM][TN];
+    f32x4 dq[TPD];
     zero(dq);
-    mm(dq, sdPs, LDC, 1, sK, LDD, 1, BC, ty, tx);
+    mmf(dq, wd, sdPs, LDC, 1, sK, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
@@ -594,22 +620,22 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       rs = static_cast<size_t>(p.Hv) * D;
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = ty + RS * i;
-      if (r < rows)
+    for (int t = 0; t < TPD; ++t)
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj)
-          dst[static_cast<size_t>(ts + r) * rs + tx + 16 * jj] =
-              dq[i][jj] + p.scale * rf.eG[r] * U1[i][jj];
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int r = wd.row(v, lane);
+        if (r < rows)
+          dst[static_cast<size_t>(ts + r) * rs + wd.col(t, lane)] =
+              dq[t][v] + p.scale * rf.eG[r] * U1[t][v];
+      }
   }
   // dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub
   {
-    float dk[TM][TN];
+    f32x4 dk[TPD];
     zero(dk);
-    mm(dk, sdAs, LDC, 1, sK, LDD, 1, BC, ty, tx);
-    mm(dk, sdAs, 1, LDC, sK, LDD, 1, BC, ty, tx);
-    mm(dk, sdPs, 1, LDC, sQ, LDD, 1, BC, ty, tx);
+    mmf(dk, wd, sdAs, LDC, 1, sK, LDD, 1, BC, lane);
+    mmf(dk, wd, sdAs, 1, LDC, sK, LDD, 1, BC, lane);
+    mmf(dk, wd, sdPs, 1, LDC, sQ, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
@@ -620,34 +646,39 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       rs = static_cast<size_t>(p.Hv) * D;
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = ty + RS * i;
-      if (r < rows)
+    for (int t = 0; t < TPD; ++t)
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj)
-          dst[static_cast<size_t>(ts + r) * rs + tx + 16 * jj] =
-              dk[i][jj] - rf.beta[r] * rf.eG[r] * Ua[i][jj] + rf.eGl[r] * Ub[i][jj];
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int r = wd.row(v, lane);
+        if (r < rows)
+          dst[static_cast<size_t>(ts + r) * rs + wd.col(t, lane)] =
+              dk[t][v] - rf.beta[r] * rf.eG[r] * Ua[t][v] + rf.eGl[r] * Ub[t][v];
+      }
   }
   __syncthreads();
 
   // dbeta and dG per row, then dg = reverse cumulative sum of dG (wave 0)
   if (tid < BC) {
     const int r = tid;
-    const float x = sdot[1][r];
-    const float w = rf.eGl[r] * sdot[2][r];
-    float dG = srow[0][r] - srow[1][r] + p.scale * rf.eG[r] * sdot[0][r] -
-               rf.beta[r] * rf.eG[r] * x - w;
+    float d0 = 0.0f, x = 0.0f, wb = 0.0f;
+#pragma unroll
+    for (int m = 0; m < HALVES; ++m) {
+      d0 += sdot[0][m][r];
+      x += sdot[1][m][r];
+      wb += sdot[2][m][r];
+    }
+    const float w = rf.eGl[r] * wb;
+    float dG = srow[0][r] - srow[1][r] + p.scale * rf.eG[r] * d0 - rf.beta[r] * rf.eG[r] * x - w;
     float wsum = w;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
     if (r == BC - 1) {
       float hsum = 0.0f;
 #pragma unroll
-      for (int m = 0; m < BT / 64; ++m) hsum += sred[m];
+      for (int m = 0; m < NW; ++m) hsum += sred[m];
       dG += rf.eG[BC - 1] * hsum + wsum;
     }
-    const float db = srow[2][r] + sdot[3][r] - rf.eG[r] * x;
+    const float db = srow[2][r] + srv[r] - rf.eG[r] * x;
     // reverse inclusive scan: dg_r = sum_{r' >= r} dG_r'
     float s = dG;
 #pragma unroll
