@@ -25,7 +25,7 @@
 //   1. the forward prefill with a boundary state every 64 tokens (the H0 of every
 //      chunk after the first) into the workspace;
 //   2. bwd_local_kernel, one workgroup per (chunk, value head): Gamma, A, P,
-//      T = (I + A)^-1 (forward substitution) and D = T R;
+//      T = (I + A)^-1 (by 16 x 16 blocks) and D = T R;
 //   3. bwd_sweep_kernel, one workgroup per (sequence, value head, 32 value
 //      columns), last chunk to first: dH_n of every chunk, dR, dV and dH0;
 //   4. bwd_grads_kernel, one workgroup per (chunk, value head): dQ, dK, dbeta, dg;
@@ -43,7 +43,6 @@ namespace {
 constexpr int BC = 64;        // tokens per backward chunk
 constexpr int BT = 512;       // threads per workgroup (two waves per SIMD)
 constexpr int NW = BT / 64;   // waves per workgroup
-constexpr int NPART = BT / 64;
 constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
 
 // Wave-tiled fp32 matrix-core products.  An M x N output is cut into 16 x 16
@@ -133,59 +132,82 @@ __device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams
   }
 }
 
-// rows [0, 64) x NC columns (from col0) of a [tokens, heads, D] input (head `hd`)
-// -> fp32 LDS rows of leading dimension ld; rows past `rows` are zero.  Every
-// thread issues all of its 8-element loads (addresses clamped to the sequence)
-// before it converts and stores any of them.
+// Rows [0, 64) x NC columns (from col0) of a [tokens, heads, D] input (head `hd`),
+// fetched into registers with 8-element loads (addresses clamped to the sequence),
+// then stored as fp32 LDS rows of leading dimension ld with rows past `rows` zero.
+// Fetch and store are separate so that a fetch can be in flight during other work.
+template <typename TIn, int D, int NC>
+struct RowsRegs {
+  static constexpr int SEGS = NC / 8, UNITS = BC * SEGS, PER = (UNITS + BT - 1) / BT;
+  Seg8<TIn> buf[PER];
+  __device__ __forceinline__ void fetch(const TIn *src, int heads, int hd, int ts, int rows,
+                                        int col0, int tid) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      const int r = min(u / SEGS, rows - 1), sg = u % SEGS;
+      if (UNITS % BT == 0 || u < UNITS)
+        buf[j].load(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + 8 * sg);
+    }
+  }
+  __device__ __forceinline__ void store(float *dst, int ld, int rows, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      const int r = u / SEGS, sg = u % SEGS;
+      if (UNITS % BT == 0 || u < UNITS) {
+        float x[8];
+        buf[j].get(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[r * ld + 8 * sg + e] = r < rows ? x[e] : 0.0f;
+      }
+    }
+  }
+};
+
 template <typename TIn, int D, int NC>
 __device__ __forceinline__ void load_rows(float *dst, int ld, const TIn *src, int heads, int hd,
                                           int ts, int rows, int col0, int tid) {
-  constexpr int SEGS = NC / 8, UNITS = BC * SEGS, PER = (UNITS + BT - 1) / BT;
-  Seg8<TIn> buf[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int u = tid + j * BT;
-    const int r = min(u / SEGS, rows - 1), sg = u % SEGS;
-    if (UNITS % BT == 0 || u < UNITS)
-      buf[j].load(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + 8 * sg);
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int u = tid + j * BT;
-    const int r = u / SEGS, sg = u % SEGS;
-    if (UNITS % BT == 0 || u < UNITS) {
-      float x[8];
-      buf[j].get(x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[r * ld + 8 * sg + e] = r < rows ? x[e] : 0.0f;
-    }
-  }
+  RowsRegs<TIn, D, NC> r;
+  r.fetch(src, heads, hd, ts, rows, col0, tid);
+  r.store(dst, ld, rows, tid);
 }
 
-// an NR x NC float32 matrix (global row stride gs; NULL reads as zeros) -> LDS
-// (leading dimension ld), all 16-byte loads issued first
+// An NR x NC float32 matrix (global row stride gs; NULL reads as zeros) through
+// registers (16-byte loads) into LDS (leading dimension ld).
 template <int NR, int NC>
-__device__ __forceinline__ void load_mat(float *dst, int ld, const float *src, size_t gs, int tid) {
-  constexpr int Q4 = NC / 4, UNITS = NR * Q4, PER = (UNITS + BT - 1) / BT;
+struct MatRegs {
+  static constexpr int Q4 = NC / 4, UNITS = NR * Q4, PER = (UNITS + BT - 1) / BT;
   float4 buf[PER];
+  __device__ __forceinline__ void fetch(const float *src, size_t gs, int tid) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int u = tid + j * BT;
-    buf[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (src && (UNITS % BT == 0 || u < UNITS))
-      buf[j] = *reinterpret_cast<const float4 *>(src + (u / Q4) * gs + 4 * (u % Q4));
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int u = tid + j * BT;
-    if (UNITS % BT == 0 || u < UNITS) {
-      float *d = dst + (u / Q4) * ld + 4 * (u % Q4);
-      d[0] = buf[j].x;
-      d[1] = buf[j].y;
-      d[2] = buf[j].z;
-      d[3] = buf[j].w;
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      buf[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (src && (UNITS % BT == 0 || u < UNITS))
+        buf[j] = *reinterpret_cast<const float4 *>(src + (u / Q4) * gs + 4 * (u % Q4));
     }
   }
+  __device__ __forceinline__ void store(float *dst, int ld, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      if (UNITS % BT == 0 || u < UNITS) {
+        float *d = dst + (u / Q4) * ld + 4 * (u % Q4);
+        d[0] = buf[j].x;
+        d[1] = buf[j].y;
+        d[2] = buf[j].z;
+        d[3] = buf[j].w;
+      }
+    }
+  }
+};
+
+template <int NR, int NC>
+__device__ __forceinline__ void load_mat(float *dst, int ld, const float *src, size_t gs, int tid) {
+  MatRegs<NR, NC> m;
+  m.fetch(src, gs, tid);
+  m.store(dst, ld, tid);
 }
 
 // the state a chunk enters with: the initial state for a sequence's first chunk,
@@ -229,7 +251,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   __shared__ float sQ[BC * LDD];    // later V, then R
   __shared__ float sA[BC * LDC];
   __shared__ float sT[BC * LDC];
-  __shared__ float sH[32 * LDD];    // 32 rows of H0 at a time; also the solve's partial sums
+  __shared__ float sH[32 * LDD];    // 32 rows of H0 at a time; also the solve's 16 x 16 blocks
   __shared__ RowFactors rf;
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -272,21 +294,51 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   }
   __syncthreads();
 
-  // T = (I + A)^-1 row by row: T_r = e_r - sum_{i<r} A_ri T_i.  Thread (column jc,
-  // part) sums the i = part (mod NPART) terms; the parts meet in LDS.
+  // T = (I + A)^-1 by 16 x 16 blocks (A strictly lower, so T is unit lower):
+  //   diagonal blocks T_bb = (I + A_bb)^-1: wave b, lane jc < 16 solves column jc by
+  //   forward substitution, t_r = [r == jc] - sum_{i<r} A_bb[r][i] t_i;
+  //   off-diagonal blocks, block row by block row: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  //   (16 x 16 matrix-core products, wave j takes block column j).
   {
-    const int jc = tid & 63, part = tid >> 6;
-    float *red = sH;
-    for (int r = 0; r < BC; ++r) {
-      float s = 0.0f;
-      for (int i = part; i < r; i += NPART) s = fmaf(sA[r * LDC + i], sT[i * LDC + jc], s);
-      red[part * BC + jc] = s;
-      __syncthreads();
-      if (part == 0) {
-        float t = 0.0f;
+    for (int idx = tid; idx < BC * BC; idx += BT) sT[(idx / BC) * LDC + idx % BC] = 0.0f;
+    __syncthreads();
+    if (wave < BC / 16 && lane < 16) {
+      const int b = 16 * wave, jc = lane;
+      float t[16];
 #pragma unroll
-        for (int m = 0; m < NPART; ++m) t += red[m * BC + jc];
-        sT[r * LDC + jc] = (r == jc ? 1.0f : 0.0f) - t;
+      for (int r = 0; r < 16; ++r) {
+        float x = r == jc ? 1.0f : 0.0f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) x = fmaf(-sA[(b + r) * LDC + b + i], t[i], x);
+        t[r] = x;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(b + r) * LDC + b + jc] = t[r];
+    }
+    __syncthreads();
+    constexpr int LDM = 17;
+    float *sM = sH;   // one 16 x 16 block per block column
+    const WTile<16, 1> w0(0);
+    for (int i = 1; i < BC / 16; ++i) {
+      if (wave < i) {
+        const int jb = wave;
+        f32x4 m[1];
+        zero(m);
+        for (int k = jb; k < i; ++k)
+          mmf(m, w0, sA + (16 * i) * LDC + 16 * k, LDC, 1, sT + (16 * k) * LDC + 16 * jb, LDC, 1,
+              16, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sM[jb * 16 * LDM + w0.row(v, lane) * LDM + w0.col(0, lane)] = m[0][v];
+      }
+      __syncthreads();
+      if (wave < i) {
+        const int jb = wave;
+        f32x4 m[1];
+        zero(m);
+        mmf(m, w0, sT + (16 * i) * LDC + 16 * i, LDC, 1, sM + jb * 16 * LDM, LDM, 1, 16, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sT[(16 * i + w0.row(v, lane)) * LDC + 16 * jb + w0.col(0, lane)] = -m[0][v];
       }
       __syncthreads();
     }
@@ -373,6 +425,21 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
       for (int v = 0; v < 4; ++v) dh[t][v] = s[wh.row(v, lane) * D + col0 + wh.col(t, lane)];
   }
   const TIn *dO = static_cast<const TIn *>(p.d_out);
+  // the inputs of the chunk after next in the sweep are fetched into registers
+  // while the current chunk's products run
+  RowsRegs<TIn, D, D> fk, fq;
+  RowsRegs<TIn, D, 32> fo;
+  MatRegs<BC, BC> fp, ft;
+  auto fetch = [&](int jc) {
+    const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
+    const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
+    fk.fetch(static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+    fq.fetch(static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+    fo.fetch(dO, p.Hv, h, ts, rows, col0, tid);
+    fp.fetch(p.pmat + cc * BC * BC, BC, tid);
+    ft.fetch(p.tmat + cc * BC * BC, BC, tid);
+  };
+  if (nch > 0) fetch(nch - 1);
   for (int jc = nch - 1; jc >= 0; --jc) {
     const int c = p.cb[n] + jc;
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
@@ -386,12 +453,13 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
         dhn[r * D + col0 + q] = dh[t][v];
         sdH[r * LDV + q] = dh[t][v];
       }
-    load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-    load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
-    load_rows<TIn, D, 32>(sO, LDV, dO, p.Hv, h, ts, rows, col0, tid);
-    load_mat<BC, BC>(sP, LDC, p.pmat + cc * BC * BC, BC, tid);
-    load_mat<BC, BC>(sT, LDC, p.tmat + cc * BC * BC, BC, tid);
+    fk.store(sK, LDD, rows, tid);
+    fq.store(sQ, LDD, rows, tid);
+    fo.store(sO, LDV, rows, tid);
+    fp.store(sP, LDC, tid);
+    ft.store(sT, LDC, tid);
     row_factors(rf, p, h, ts, rows, tid);
+    if (jc > 0) fetch(jc - 1);
     __syncthreads();
 
     // dD = P^T dO + diag(e^{G_n - G}) (K dH)
@@ -509,15 +577,28 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   {
     float *sDb = arena, *sRb = sDb + BC * LDV, *sOb = sRb + BC * LDV, *svb = sOb + BC * LDV;
     float *sHb = svb + BC * LDV, *sGb = sHb + D * LDV;
+    // the next slice is fetched into registers while this one's products run
+    MatRegs<BC, 32> fD, fR;
+    RowsRegs<TIn, D, 32> fO, fV;
+    MatRegs<D, 32> fH, fG;
+    auto fetch = [&](int vb) {
+      fD.fetch(dm + vb, D, tid);
+      fR.fetch(drm + vb, D, tid);
+      fO.fetch(static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, tid);
+      fV.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
+      fH.fetch(h0 ? h0 + vb : nullptr, D, tid);
+      fG.fetch(dhn + vb, D, tid);
+    };
+    fetch(0);
     for (int vb = 0; vb < D; vb += 32) {
       __syncthreads();
-      load_mat<BC, 32>(sDb, LDV, dm + vb, D, tid);
-      load_mat<BC, 32>(sRb, LDV, drm + vb, D, tid);
-      load_rows<TIn, D, 32>(sOb, LDV, static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb,
-                            tid);
-      load_rows<TIn, D, 32>(svb, LDV, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
-      load_mat<D, 32>(sHb, LDV, h0 ? h0 + vb : nullptr, D, tid);
-      load_mat<D, 32>(sGb, LDV, dhn + vb, D, tid);
+      fD.store(sDb, LDV, tid);
+      fR.store(sRb, LDV, tid);
+      fO.store(sOb, LDV, rows, tid);
+      fV.store(svb, LDV, rows, tid);
+      fH.store(sHb, LDV, tid);
+      fG.store(sGb, LDV, tid);
+      if (vb + 32 < D) fetch(vb + 32);
       __syncthreads();
       // <dH_n, H0> over this slice (each thread its share of the elements)
       for (int idx = tid; idx < D * 32; idx += BT) {
