@@ -15,6 +15,10 @@ gradient of the same function, so the oracle is that gradient, by definition:
   reverse-mode automatic differentiation.  Its forward pass is checked against the
   C oracle and its gradients against central finite differences and closed forms
   (tests/test_oracle_backward.py).
+* With the in-kernel q/k L2 norm and the gates formed from raw projections (the
+  module's defaults on the same page: use_qk_l2norm_in_kernel, _compute_gates),
+  the same differentiation runs through those steps too (:func:`l2norm_torch`,
+  :func:`gates_torch`, the definitions of ``oracle/gating.py``).
 * :func:`chunked_backward` is the chunk-by-chunk evaluation of the same gradient
   (the algebra the GPU backward follows), in fp64 NumPy.  It is checked against
   :func:`prefill_backward`, never against the GPU.
@@ -76,12 +80,33 @@ def forward_torch(q, k, v, g, beta, scale, H0):
     return o, H
 
 
+def l2norm_torch(x):
+    """x / sqrt(sum x^2 + 1e-6) over the last axis (the in-kernel q/k norm)."""
+    import torch
+    return x / torch.sqrt((x * x).sum(-1, keepdim=True) + 1e-6)
+
+
+def gates_torch(alpha, b, A_log, dt_bias):
+    """g = -exp(A_log) softplus(alpha + dt_bias), beta = sigmoid(b) on torch tensors
+    (the definitions of oracle/gating.py; A_log, dt_bias broadcast over the last axis)."""
+    import torch
+    x = alpha + dt_bias
+    # log(1 + e^x) = max(x, 0) + log(1 + e^-|x|): exp of a non-positive number only
+    softplus = torch.clamp(x, min=0.0) + torch.log1p(torch.exp(-torch.abs(x)))
+    return -torch.exp(A_log) * softplus, 1.0 / (1.0 + torch.exp(-b))
+
+
 def prefill_backward(q, k, v, g, beta, do, dht=None, *, scale=None, cu_seqlens=None,
-                     initial_state=None, return_forward=False):
+                     initial_state=None, return_forward=False, use_qk_l2norm=False,
+                     A_log=None, dt_bias=None):
     """fp64 gradients of  L = <o, do> + <H_final, dht>  for the GDN recurrence.
 
     Batched layout as in :func:`oracle.prefill` (n_h = 1): q, k [B,T,Hk,K];
     v, do [B,T,Hv,V]; g, beta [B,T,Hv]; initial_state, dht [N,Hv,K,V] or None.
+    With ``use_qk_l2norm`` the recurrence reads q, k divided by their L2 norm and
+    dq, dk are the gradients of the raw q, k.  With ``A_log`` and ``dt_bias`` ([Hv])
+    g and beta hold the raw projections alpha and b, the gates are formed from them,
+    dg and dbeta are the gradients of alpha and b, and dA_log, ddt_bias [Hv] are added.
     Returns dict dq, dk [B,T,Hk,K]; dv [B,T,Hv,V]; dg, dbeta [B,T,Hv];
     dh0 [N,Hv,K,V] (all fp64), plus o and final_state when ``return_forward``.
     """
@@ -103,11 +128,21 @@ def prefill_backward(q, k, v, g, beta, do, dht=None, *, scale=None, cu_seqlens=N
     def leaf(x):
         return torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
 
+    raw_gates = A_log is not None
+    if raw_gates:
+        res["dA_log"] = np.zeros(Hv)
+        res["ddt_bias"] = np.zeros(Hv)
     for n, (b, t0, t1) in enumerate(spans):
         qs, ks, vs = leaf(q[b, t0:t1]), leaf(np.asarray(k)[b, t0:t1]), leaf(np.asarray(v)[b, t0:t1])
         gs, bs = leaf(np.asarray(g)[b, t0:t1]), leaf(np.asarray(beta)[b, t0:t1])
         h0 = leaf(np.zeros((Hv, K, V)) if initial_state is None else initial_state[n])
-        o, H = forward_torch(qs, ks, vs, gs, bs, float(scale), h0)
+        qe, ke, ge, be = qs, ks, gs, bs
+        if use_qk_l2norm:
+            qe, ke = l2norm_torch(qs), l2norm_torch(ks)
+        if raw_gates:
+            al, dtb = leaf(A_log), leaf(dt_bias)
+            ge, be = gates_torch(gs, bs, al, dtb)
+        o, H = forward_torch(qe, ke, vs, ge, be, float(scale), h0)
         loss = (o * torch.tensor(np.asarray(do, dtype=np.float64)[b, t0:t1])).sum()
         if dht is not None:
             loss = loss + (H * torch.tensor(np.asarray(dht[n], dtype=np.float64))).sum()
@@ -118,6 +153,10 @@ def prefill_backward(q, k, v, g, beta, do, dht=None, *, scale=None, cu_seqlens=N
                 res[name][b, t0:t1] = x.grad.numpy()
         if h0.grad is not None:
             res["dh0"][n] = h0.grad.numpy()
+        if raw_gates:
+            for name, x in (("dA_log", al), ("ddt_bias", dtb)):
+                if x.grad is not None:
+                    res[name] += x.grad.numpy()
         if return_forward:
             res["o"][b, t0:t1] = o.detach().numpy()
             res["final_state"][n] = H.detach().numpy()

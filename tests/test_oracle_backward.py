@@ -170,3 +170,60 @@ def test_chunked_check_rejects_mutant(name):
     a = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0)
     c = mod.chunked_backward(q, k, v, g, beta, do, dht, chunk_size=8, initial_state=s0)
     assert max(_maxdiff(c[n], a[n]) for n in NAMES) > 1e-6, name
+
+
+def test_torch_gates_equal_gate_oracle():
+    import torch
+    r = np.random.default_rng(20)
+    alpha = r.standard_normal((50, 3)) * 30
+    b = r.standard_normal((50, 3)) * 30
+    A_log, dt_bias = np.log(r.uniform(1, 16, 3)), r.standard_normal(3)
+    g, beta = OB.gates_torch(*(torch.tensor(x) for x in (alpha, b, A_log, dt_bias)))
+    g0, b0 = oracle.gates(alpha, b, A_log, dt_bias)
+    assert _maxdiff(g.numpy(), g0) < 1e-14 and _maxdiff(beta.numpy(), b0) < 1e-15
+
+
+def _raw_problem(seed):
+    q, k, v, g, beta, s0, do, dht = _problem(seed, T=6, Hk=1, Hv=2, K=3, V=3)
+    r = np.random.default_rng(seed + 100)
+    q, k = 2.5 * q + 0.3 * r.standard_normal(q.shape), 0.7 * k + 0.2 * r.standard_normal(k.shape)
+    alpha, b = r.standard_normal(g.shape), r.standard_normal(beta.shape)
+    A_log, dt_bias = np.log(r.uniform(1, 4, 2)), np.log(np.expm1(r.uniform(0.01, 0.1, 2)))
+    return q, k, v, alpha, b, s0, do, dht, A_log, dt_bias
+
+
+def test_l2norm_and_raw_gate_gradients_equal_finite_differences():
+    q, k, v, alpha, b, s0, do, dht, A_log, dt_bias = _raw_problem(21)
+    scale = 0.8
+    res = OB.prefill_backward(q, k, v, alpha, b, do, dht, initial_state=s0, scale=scale,
+                              use_qk_l2norm=True, A_log=A_log, dt_bias=dt_bias)
+    args = {"q": q, "k": k, "v": v, "alpha": alpha, "b": b, "A_log": A_log, "dt_bias": dt_bias}
+    name = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dg", "b": "dbeta", "A_log": "dA_log",
+            "dt_bias": "ddt_bias"}
+
+    def loss(a):
+        gg, bb = oracle.gates(a["alpha"], a["b"], a["A_log"], a["dt_bias"])
+        o, fs = oracle.prefill(a["q"], a["k"], a["v"], gg, bb, initial_state=s0, scale=scale,
+                               output_final_state=True, use_qk_l2norm=True)
+        return float(np.sum(o * do) + np.sum(fs * dht))
+
+    eps = 1e-6
+    for nm, x in args.items():
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            fd[i] = (loss(dict(args, **{nm: xp})) - loss(dict(args, **{nm: xm}))) / (2 * eps)
+        err = _maxdiff(res[name[nm]], fd)
+        assert err < 1e-6, (nm, err)
+
+
+def test_l2norm_gradient_is_orthogonal_to_the_input():
+    # the loss sees q only through q / |q| (up to the 1e-6 inside the root), so the
+    # gradient has no component along q
+    q, k, v, alpha, b, s0, do, dht, A_log, dt_bias = _raw_problem(22)
+    res = OB.prefill_backward(q, k, v, alpha, b, do, dht, initial_state=s0, use_qk_l2norm=True)
+    for x, dx in ((q, res["dq"]), (k, res["dk"])):
+        dots = np.sum(x * dx, axis=-1)
+        assert np.max(np.abs(dots)) < 1e-5 * np.max(np.abs(dx)), np.max(np.abs(dots))
