@@ -395,7 +395,9 @@ def gated_rmsnorm(x, z, weight, *, eps=1e-5, norm_before_gate=False, out=None, s
 
 
 def backward_args(q, k, v, g, beta, do, *, dq, dk, dv, dg, dbeta, dh0=None, dht=None,
-                  scale=None, initial_state=None, cu_seqlens=None, workspace=None):
+                  scale=None, initial_state=None, cu_seqlens=None, workspace=None,
+                  use_qk_l2norm_in_kernel=False, A_log=None, dt_bias=None, dA_log=None,
+                  ddt_bias=None):
     """Fill a gdr_backward_args struct from tensors (no checks beyond shapes)."""
     B, T, Hk, K = q.shape
     Hv, V = v.shape[-2], v.shape[-1]
@@ -414,19 +416,29 @@ def backward_args(q, k, v, g, beta, do, *, dq, dk, dv, dg, dbeta, dh0=None, dht=
     a.d_initial_state = _ptr(dh0)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel()
+    a.use_qk_l2norm = int(bool(use_qk_l2norm_in_kernel))
+    a.gate_mode = 0 if A_log is None else 1
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.dA_log, a.ddt_bias = _ptr(dA_log), _ptr(ddt_bias)
     return a
 
 
 def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
                                     initial_state=None, cu_seqlens=None, *, workspace=None,
-                                    stream=None):
-    """Gradients of the chunked prefill (gated delta rule, n_h = 1, gates as given).
+                                    stream=None, use_qk_l2norm_in_kernel=False, A_log=None,
+                                    dt_bias=None):
+    """Gradients of the chunked prefill (gated delta rule, n_h = 1).
+
+    With ``use_qk_l2norm_in_kernel`` the forward normalised q and k, and dq, dk are
+    the gradients of the raw q, k.  With ``A_log`` and ``dt_bias`` ([Hv] float32), g
+    and beta are the raw gate projections; dg and dbeta are then their gradients
+    and the result gains dA_log, ddt_bias ([Hv]).
 
     q, k [B,T,Hk,D]; v, do [B,T,Hv,D] (float32 or bfloat16, one dtype); g, beta
     [B,T,Hv] float32; dht (gradient of the final state) and initial_state float32
     [N,Hv,D,D] or None; cu_seqlens int32 [N+1] (B must be 1).
     Returns (dq, dk, dv, dg, dbeta, dh0), float32, shaped like q, k, v, g, beta and
-    the initial state ([N,Hv,D,D]).  ``workspace``: a uint8 GPU tensor of at least
+    the initial state ([N,Hv,D,D]) (plus dA_log, ddt_bias with raw gates).  ``workspace``: a uint8 GPU tensor of at least
     the library's gdr_backward_workspace_bytes (allocated here when None).
     """
     torch = _torch()
@@ -452,8 +464,13 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
     dg = torch.empty((B, T, Hv), dtype=f32, device=dev)
     dbeta = torch.empty((B, T, Hv), dtype=f32, device=dev)
     dh0 = torch.empty((N, Hv, K, V), dtype=f32, device=dev)
+    gate_mode, A_log, dt_bias = _gate_params(A_log, dt_bias, Hv, torch)
+    dA_log = torch.empty((Hv,), dtype=f32, device=dev) if gate_mode else None
+    ddt_bias = torch.empty((Hv,), dtype=f32, device=dev) if gate_mode else None
     a = backward_args(q, k, v, g, beta, do, dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0,
-                      dht=dht, scale=scale, initial_state=initial_state, cu_seqlens=cu_seqlens)
+                      dht=dht, scale=scale, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, A_log=A_log,
+                      dt_bias=dt_bias, dA_log=dA_log, ddt_bias=ddt_bias)
     need = int(lib.gdr_backward_workspace_bytes(a))
     if workspace is None:
         # 256-byte alignment: the caching allocator hands out 512-byte aligned blocks
@@ -464,6 +481,8 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
     a.workspace_bytes = workspace.numel()
     _raise(lib.gdr_chunk_gated_delta_rule_backward(a, _stream(stream)),
            "gdr_chunk_gated_delta_rule_backward")
+    if gate_mode:
+        return dq, dk, dv, dg, dbeta, dh0, dA_log, ddt_bias
     return dq, dk, dv, dg, dbeta, dh0
 
 

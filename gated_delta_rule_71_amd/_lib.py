@@ -156,6 +156,9 @@ class BackwardArgs(ctypes.Structure):
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
         ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("d_initial_state", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("use_qk_l2norm", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dA_log", ctypes.c_void_p), ("ddt_bias", ctypes.c_void_p),
     ]
 
 

@@ -242,7 +242,7 @@ __global__ void bwd_table_kernel(const BackwardParams p) {
 
 // Per (chunk, value head): Araw = strict_lower((K K^T) * Gamma), P, T = (I + A)^-1
 // with A = diag(beta) Araw, and D = T R, R = diag(beta) (V - diag(e^G) K H0).
-template <typename TIn, int D>
+template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   constexpr int LDD = D + 1;
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
@@ -264,8 +264,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
   const int hk = h / (p.Hv / p.Hk);
 
-  load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
   row_factors(rf, p, h, ts, rows, tid);
   __syncthreads();
 
@@ -387,7 +387,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 // dH (D x 32 columns): store dH_n, then dD = P^T dO + diag(e^{G_n - G}) K dH,
 // dR = T^T dD (kept for bwd_grads_kernel), dV = diag(beta) dR, and
 // dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
-template <typename TIn, int D>
+template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   constexpr int LDD = D + 1, LDV = 33;
   constexpr int TPH = (D / 16) * 2 / NW;   // D x 32 tiles per wave
@@ -427,14 +427,14 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   const TIn *dO = static_cast<const TIn *>(p.d_out);
   // the inputs of the chunk after next in the sweep are fetched into registers
   // while the current chunk's products run
-  RowsRegs<TIn, D, D> fk, fq;
+  RowsRegs<TQK, D, D> fk, fq;
   RowsRegs<TIn, D, 32> fo;
   MatRegs<BC, BC> fp, ft;
   auto fetch = [&](int jc) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
     const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
-    fk.fetch(static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-    fq.fetch(static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+    fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+    fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
     fo.fetch(dO, p.Hv, h, ts, rows, col0, tid);
     fp.fetch(p.pmat + cc * BC * BC, BC, tid);
     ft.fetch(p.tmat + cc * BC * BC, BC, tid);
@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 //            dG_r = rowsum(E + F) - colsum(E + F) + scale e^{G_r} q_r . U1_r
 //                   - beta_r e^{G_r} k_r . Ua_r - w_r,  w_r = e^{G_n - G_r} k_r . Ub_r,
 //            plus e^{G_n} <dH_n, H0> + sum w on the last row; dg = reverse cumsum.
-template <typename TIn, int D>
+template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   constexpr int LDD = D + 1, LDV = 33;
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
@@ -636,8 +636,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         sM2[r * LDC + q] = a * ar;
       }
   }
-  load_rows<TIn, D, D>(sK, LDD, static_cast<const TIn *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
   if (tid < BC) srv[tid] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
@@ -794,17 +794,132 @@ __global__ void bwd_group_sum_kernel(const BackwardParams p, long total) {
   p.dk[i] = sk;
 }
 
+// ---- in-kernel L2 norm and gates from raw projections ------------------------------
+
+// one wave per (token, q/k head) row of D: x / sqrt(sum x^2 + 1e-6) into fp32 copies
+template <typename TIn, int D>
+__global__ void bwd_l2norm_kernel(const BackwardParams p, float *qn, float *kn, long rows) {
+  const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int E = D / 64;
+  for (int w = 0; w < 2; ++w) {
+    const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
+    float *dst = (w ? kn : qn) + row * D;
+    float x[E], ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x[e] = load_f32<TIn>(src + lane + 64 * e);
+      ss = fmaf(x[e], x[e], ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float rn = 1.0f / sqrtf(ss + 1e-6f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[lane + 64 * e] = x[e] * rn;
+  }
+}
+
+// g = -exp(A_log) softplus(alpha + dt_bias), beta = sigmoid(b) per (token, value head)
+__global__ void bwd_gates_kernel(const BackwardParams p, float *g, float *beta, long n) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int h = static_cast<int>(i % p.Hv);
+  g[i] = gate_decay(p.alpha_raw[i], expf(p.A_log[h]), p.dt_bias[h]);
+  beta[i] = gate_beta(p.b_raw[i]);
+}
+
+// dx = (dx^ - x^ (x^ . dx^)) / n with n = sqrt(sum x^2 + 1e-6), x^ = x / n, in place
+// on dq and dk (one wave per row)
+template <typename TIn, int D>
+__global__ void bwd_l2norm_grad_kernel(const BackwardParams p, long rows) {
+  const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int E = D / 64;
+  for (int w = 0; w < 2; ++w) {
+    const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
+    float *dx = (w ? p.dk : p.dq) + row * D;
+    float x[E], d[E], ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x[e] = load_f32<TIn>(src + lane + 64 * e);
+      d[e] = dx[lane + 64 * e];
+      ss = fmaf(x[e], x[e], ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float rn = 1.0f / sqrtf(ss + 1e-6f);
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dot = fmaf(x[e] * rn, d[e], dot);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+#pragma unroll
+    for (int e = 0; e < E; ++e) dx[lane + 64 * e] = (d[e] - x[e] * rn * dot) * rn;
+  }
+}
+
+// Chain rule through the gates, one workgroup per value head (a fixed-order sum over
+// tokens): dalpha = dg * dg/dalpha = -dg A sigmoid(alpha + dt_bias), db = dbeta
+// beta (1 - beta), both in place; dA_log = sum_t dg g (dg/dA_log = g) and
+// ddt_bias = sum_t dalpha.
+__global__ void __launch_bounds__(256) bwd_gates_grad_kernel(const BackwardParams p) {
+  __shared__ float red[2][256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float A = expf(p.A_log[h]), dtb = p.dt_bias[h];
+  float sa = 0.0f, sd = 0.0f;
+  for (long t = tid; t < p.tokens; t += 256) {
+    const size_t i = static_cast<size_t>(t) * p.Hv + h;
+    const float x = p.alpha_raw[i] + dtb;
+    const float dg = p.dg[i];
+    const float g = -A * softplus_f32(x);
+    const float da = -dg * A / (1.0f + expf(-x));
+    p.dg[i] = da;
+    const float b = gate_beta(p.b_raw[i]);
+    p.dbeta[i] *= b * (1.0f - b);
+    sa = fmaf(dg, g, sa);
+    sd += da;
+  }
+  red[0][tid] = sa;
+  red[1][tid] = sd;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      red[0][tid] += red[0][tid + o];
+      red[1][tid] += red[1][tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.dA_log[h] = red[0][0];
+    p.ddt_bias[h] = red[1][0];
+  }
+}
+
 namespace {
+
+template <typename TIn, typename TQK, int D>
+hipError_t launch_bwd_qk(const BackwardParams &p, int max_chunks, hipStream_t s) {
+  if (max_chunks > 0)
+    hipLaunchKernelGGL((bwd_local_kernel<TIn, TQK, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s,
+                       p);
+  // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0
+  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D>), dim3(p.num_seqs * p.Hv * (D / 32)),
+                     dim3(BT), 0, s, p);
+  if (max_chunks > 0)
+    hipLaunchKernelGGL((bwd_grads_kernel<TIn, TQK, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s,
+                       p);
+  return hipSuccess;
+}
 
 template <typename TIn, int D>
 hipError_t launch_bwd_d(const BackwardParams &p, int max_chunks, long tokens, hipStream_t s) {
-  if (max_chunks > 0)
-    hipLaunchKernelGGL((bwd_local_kernel<TIn, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s, p);
-  // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0
-  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, D>), dim3(p.num_seqs * p.Hv * (D / 32)), dim3(BT), 0,
-                     s, p);
-  if (max_chunks > 0)
-    hipLaunchKernelGGL((bwd_grads_kernel<TIn, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s, p);
+  // with the in-kernel L2 norm the kernels read the normalised fp32 copies of q, k
+  if (p.q_raw)
+    launch_bwd_qk<TIn, float, D>(p, max_chunks, s);
+  else
+    launch_bwd_qk<TIn, TIn, D>(p, max_chunks, s);
   if (p.Hv != p.Hk && tokens > 0) {
     const long total = tokens * p.Hk * D;
     hipLaunchKernelGGL((bwd_group_sum_kernel<D>), dim3((total + 255) / 256), dim3(256), 0, s, p,
@@ -818,6 +933,52 @@ hipError_t launch_bwd_d(const BackwardParams &p, int max_chunks, long tokens, hi
 hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_table_kernel, dim3(1), dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename TIn, int D>
+hipError_t launch_pro_d(const BackwardParams &p, hipStream_t s) {
+  if (p.q_raw) {
+    const long rows = p.tokens * p.Hk;
+    hipLaunchKernelGGL((bwd_l2norm_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s, p,
+                       const_cast<float *>(static_cast<const float *>(p.q)),
+                       const_cast<float *>(static_cast<const float *>(p.k)), rows);
+  }
+  if (p.alpha_raw) {
+    const long n = p.tokens * p.Hv;
+    hipLaunchKernelGGL(bwd_gates_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p,
+                       const_cast<float *>(p.g), const_cast<float *>(p.beta), n);
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn, int D>
+hipError_t launch_epi_d(const BackwardParams &p, hipStream_t s) {
+  const long rows = p.tokens * p.Hk;
+  if (p.q_raw && rows > 0)
+    hipLaunchKernelGGL((bwd_l2norm_grad_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s,
+                       p, rows);
+  if (p.alpha_raw) hipLaunchKernelGGL(bwd_gates_grad_kernel, dim3(p.Hv), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_prologue(const BackwardParams &p, int qkv_f32, int head,
+                                    hipStream_t stream) {
+  if (p.tokens == 0) return hipSuccess;
+  if (head == 64) return qkv_f32 ? launch_pro_d<float, 64>(p, stream)
+                                 : launch_pro_d<uint16_t, 64>(p, stream);
+  if (head == 128) return qkv_f32 ? launch_pro_d<float, 128>(p, stream)
+                                  : launch_pro_d<uint16_t, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_epilogue(const BackwardParams &p, int qkv_f32, int head,
+                                    hipStream_t stream) {
+  if (p.alpha_raw == nullptr && p.q_raw == nullptr) return hipSuccess;
+  if (head == 64) return qkv_f32 ? launch_epi_d<float, 64>(p, stream)
+                                 : launch_epi_d<uint16_t, 64>(p, stream);
+  if (head == 128) return qkv_f32 ? launch_epi_d<float, 128>(p, stream)
+                                  : launch_epi_d<uint16_t, 128>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_backward(const BackwardParams &p, int qkv_f32, int head, int max_chunks,

@@ -195,7 +195,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up of the backward (byte offsets from the base, each aligned).
 struct BwdLayout {
-  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, total;
+  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, qn, kn, gg, gb, total;
   int max_chunks;
 };
 
@@ -229,6 +229,11 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   const bool grouped = a->num_v_heads != a->num_qk_heads;
   L.dqh = take(grouped ? tokens * Hv * D * 4 : 0);
   L.dkh = take(grouped ? tokens * Hv * D * 4 : 0);
+  const size_t Hk = static_cast<size_t>(a->num_qk_heads);
+  L.qn = take(a->use_qk_l2norm ? tokens * Hk * D * 4 : 0);
+  L.kn = take(a->use_qk_l2norm ? tokens * Hk * D * 4 : 0);
+  L.gg = take(a->gate_mode ? tokens * Hv * 4 : 0);
+  L.gb = take(a->gate_mode ? tokens * Hv * 4 : 0);
   L.total = off;
   return L;
 }
@@ -243,6 +248,10 @@ int gdr_validate_backward(const gdr_backward_args *a) {
   if (a->head_k <= 0 || a->head_v <= 0) return GDR_ERR_INVALID_ARG;
   if (!dtype_ok(a->qkv_dtype)) return GDR_ERR_INVALID_ARG;
   if (isinf(a->scale)) return GDR_ERR_INVALID_ARG;
+  if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return GDR_ERR_INVALID_ARG;
+  if (a->gate_mode != 0 && a->gate_mode != 1) return GDR_ERR_INVALID_ARG;
+  if (a->gate_mode == 1 && (!a->A_log || !a->dt_bias || !a->dA_log || !a->ddt_bias))
+    return GDR_ERR_INVALID_ARG;
   if (a->cu_seqlens) {
     if (a->batch != 1) return GDR_ERR_INVALID_ARG;
   } else if (a->num_seqs != a->batch) {
@@ -323,8 +332,29 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
   p.drmat = reinterpret_cast<float *>(ws + L.drmat);
   p.dq_h = reinterpret_cast<float *>(ws + L.dqh);
   p.dk_h = reinterpret_cast<float *>(ws + L.dkh);
+  p.tokens = tokens;
+  if (a->use_qk_l2norm) {
+    // the backward kernels read the normalised copies; the raw inputs serve the
+    // chain rule through the norm
+    p.q_raw = a->q;
+    p.k_raw = a->k;
+    p.q = ws + L.qn;
+    p.k = ws + L.kn;
+  }
+  if (a->gate_mode) {
+    p.alpha_raw = a->g;
+    p.b_raw = a->beta;
+    p.A_log = a->A_log;
+    p.dt_bias = a->dt_bias;
+    p.dA_log = a->dA_log;
+    p.ddt_bias = a->ddt_bias;
+    p.g = reinterpret_cast<const float *>(ws + L.gg);
+    p.beta = reinterpret_cast<const float *>(ws + L.gb);
+  }
+  const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
 
   if (gdr::launch_backward_table(p, s) != hipSuccess) return GDR_ERR_HIP;
+  if (gdr::launch_backward_prologue(p, f32, a->head_k, s) != hipSuccess) return GDR_ERR_HIP;
   if (tokens > 0) {
     // forward recompute: the state after every 64 tokens of each sequence
     gdr_prefill_args f{};
@@ -339,8 +369,11 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
     f.chunk_size = 64;
     f.qkv_dtype = a->qkv_dtype;
     f.out_dtype = a->qkv_dtype;
-    f.use_qk_l2norm = 0;
+    f.use_qk_l2norm = a->use_qk_l2norm;
     f.scale = a->scale;
+    f.gate_mode = a->gate_mode;
+    f.A_log = a->A_log;
+    f.dt_bias = a->dt_bias;
     f.q = a->q;
     f.k = a->k;
     f.v = a->v;
@@ -354,8 +387,9 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
     const int fs = gdr_chunk_gated_delta_rule(&f, stream);
     if (fs != GDR_OK) return fs;
   }
-  const hipError_t e = gdr::launch_backward(p, a->qkv_dtype == GDR_DTYPE_F32, a->head_k,
-                                            L.max_chunks, tokens, s);
+  if (gdr::launch_backward(p, f32, a->head_k, L.max_chunks, tokens, s) != hipSuccess)
+    return GDR_ERR_HIP;
+  const hipError_t e = gdr::launch_backward_epilogue(p, f32, a->head_k, s);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 

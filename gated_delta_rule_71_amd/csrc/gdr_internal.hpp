@@ -120,6 +120,19 @@ struct BackwardParams {
   float *drmat;                  // [chunks, Hv, 64, D] dR = T^T dD
   float *dq_h;                   // [Tt, Hv, D] per value head (grouped heads only)
   float *dk_h;                   // [Tt, Hv, D]
+  // in-kernel L2 norm: q, k above point at the normalised fp32 copies, these at the
+  // raw inputs (NULL without the norm)
+  const void *q_raw;
+  const void *k_raw;
+  // gates formed from raw projections: g, beta above point at the formed gates,
+  // these at the projections and per-head parameters (NULL in gate mode 0)
+  const float *alpha_raw;        // [Tt, Hv]
+  const float *b_raw;            // [Tt, Hv]
+  const float *A_log;            // [Hv]
+  const float *dt_bias;          // [Hv]
+  float *dA_log;                 // [Hv]
+  float *ddt_bias;               // [Hv]
+  long tokens;
 };
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
@@ -138,5 +151,11 @@ hipError_t launch_gated_rmsnorm(const NormParams &p, int f32, hipStream_t stream
 hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream);
 hipError_t launch_backward(const BackwardParams &p, int qkv_f32, int head, int max_chunks,
                            long tokens, hipStream_t stream);
+// the normalised q, k and the formed gates the backward kernels read (before the
+// forward recompute), and the chain rule through both (after the backward kernels)
+hipError_t launch_backward_prologue(const BackwardParams &p, int qkv_f32, int head,
+                                    hipStream_t stream);
+hipError_t launch_backward_epilogue(const BackwardParams &p, int qkv_f32, int head,
+                                    hipStream_t stream);
 
 }  // namespace gdr

@@ -295,13 +295,20 @@ typedef struct {
  *   outputs, all float32: dq, dk [Tt, Hk, D] (a q/k head receives the sum over
  *   the value heads that read it), dv [Tt, Hv, D], dg, dbeta [Tt, Hv],
  *   d_initial_state [N, Hv, D, D] or NULL (not written).
- * Gates are taken as given (gate_mode 0) and q, k without the L2 norm; dg and
- *   dbeta are the gradients with respect to those gate values.
+ * use_qk_l2norm = 1: the forward divided q and k by sqrt(sum x^2 + 1e-6) (the
+ *   in-kernel norm of the prefill); dq, dk are the gradients of the raw q, k.
+ * gate_mode = 1: g and beta hold the raw projections alpha and b, and A_log,
+ *   dt_bias [Hv] the per-head parameters, as in the prefill (gates formed in the
+ *   kernels); dg and dbeta then receive dL/dalpha and dL/db, and dA_log, ddt_bias
+ *   ([Hv] float32, required) receive dL/dA_log and dL/ddt_bias (sums over all
+ *   tokens in a fixed order).  gate_mode = 0: dg, dbeta are the gradients of the
+ *   gate values given.
  * Workspace: gdr_backward_workspace_bytes(args) bytes of device memory, 256-byte
  *   aligned, owned by the caller; its contents on entry do not matter.  It holds
  *   per 64-token chunk and value head the entering state, the gradient of the
  *   leaving state and five 64 x 64 or 64 x D float32 matrices (about
- *   2 D^2 + 3 * 64^2 + 2 * 64 D floats, 200 KiB at D = 128).
+ *   2 D^2 + 3 * 64^2 + 2 * 64 D floats, 200 KiB at D = 128), plus float32 copies
+ *   of the normalised q, k (use_qk_l2norm) and of the formed gates (gate_mode 1).
  * Supported: head_k == head_v = D in {64, 128}; q/k/v/d_out F32 or BF16.
  * The outputs must not alias the inputs or the workspace.
  */
@@ -332,6 +339,12 @@ typedef struct {
   float *d_initial_state;
   void *workspace;
   size_t workspace_bytes;
+  int32_t use_qk_l2norm;    /* 0 or 1                                               */
+  int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections         */
+  const float *A_log;       /* [Hv], gate_mode 1                                    */
+  const float *dt_bias;     /* [Hv], gate_mode 1                                    */
+  float *dA_log;            /* [Hv] output, gate_mode 1                             */
+  float *ddt_bias;          /* [Hv] output, gate_mode 1                             */
 } gdr_backward_args;
 
 /* Version of this ABI (GDR_ABI_VERSION). */

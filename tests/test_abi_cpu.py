@@ -197,3 +197,23 @@ def test_backward_validation(lib, kw, code):
     assert lib.gdr_validate_backward(ctypes.byref(_backward(**kw))) == code
     # the enqueue entry point runs the same checks and launches nothing on error
     assert lib.gdr_chunk_gated_delta_rule_backward(ctypes.byref(_backward(**kw)), None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(use_qk_l2norm=2), _lib.GDR_ERR_INVALID_ARG),
+    (dict(gate_mode=2), _lib.GDR_ERR_INVALID_ARG),
+    (dict(gate_mode=1), _lib.GDR_ERR_INVALID_ARG),                      # no A_log etc.
+    (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE, dA_log=FAKE), _lib.GDR_ERR_INVALID_ARG),
+    (dict(gate_mode=1, A_log=FAKE, dt_bias=FAKE, dA_log=FAKE, ddt_bias=FAKE), _lib.GDR_OK),
+    (dict(use_qk_l2norm=1), _lib.GDR_OK),
+])
+def test_backward_validation_norm_and_gates(lib, kw, code):
+    assert lib.gdr_validate_backward(ctypes.byref(_backward(**kw))) == code
+
+
+def test_backward_workspace_grows_with_norm_and_gates(lib):
+    base = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward()))
+    norm = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(use_qk_l2norm=1)))
+    gates = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(gate_mode=1)))
+    assert norm >= base + 2 * 200 * 2 * 128 * 4          # fp32 normalised q and k
+    assert gates >= base + 2 * 200 * 4 * 4               # fp32 g and beta

@@ -128,3 +128,66 @@ def test_backward_full_B4_T4096_H16_sampled():
         xs = {"dq": x["dq"][sl], "dk": x["dk"][sl], "dv": x["dv"][sl], "dg": x["dg"][sl],
               "dbeta": x["dbeta"][sl], "dh0": x["dh0"][b:b + 1, h:h + 1]}
         compare(xs, r, False, f"full sample b={b} h={h}")
+
+
+def _raw_inputs(bw: W.BackwardWorkload, seed):
+    """Rows of q, k rescaled away from unit norm, and raw gate projections with
+    per-head A_log, dt_bias (the recipe of workloads.with_raw_gates)."""
+    r = np.random.default_rng([seed, 0x12])
+    f = bw.fwd
+    q = W.as_f64(f.q, f.dtype) * r.uniform(0.3, 3.0, f.q.shape[:-1] + (1,))
+    k = W.as_f64(f.k, f.dtype) * r.uniform(0.3, 3.0, f.k.shape[:-1] + (1,))
+    q = W.store(q.astype(np.float32), f.dtype)
+    k = W.store(k.astype(np.float32), f.dtype)
+    Hv = f.g.shape[-1]
+    A_log = np.log(r.uniform(1.0, 16.0, size=Hv)).astype(np.float32)
+    dt_bias = np.log(np.expm1(r.uniform(0.001, 0.1, size=Hv))).astype(np.float32)
+    alpha = r.standard_normal(f.g.shape).astype(np.float32)
+    b = r.standard_normal(f.beta.shape).astype(np.float32)
+    return q, k, alpha, b, A_log, dt_bias
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_backward_l2norm_and_raw_gates(dtype):
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    from oracle.backward import prefill_backward
+    bw = W.backward_workload("bwd_raw", 18, Hk=2, Hv=4, D=128 if dtype == W.BF16 else 64,
+                             dtype=dtype, lengths=[70, 1, 130], decay="slow")
+    f = bw.fwd
+    q, k, alpha, b, A_log, dt_bias = _raw_inputs(bw, 18)
+    cu = torch.from_numpy(f.cu_seqlens).cuda()
+    out = gdr.chunk_gated_delta_rule_backward(
+        to_dev(q), to_dev(k), to_dev(f.v), to_dev(alpha), to_dev(b), to_dev(bw.do),
+        dht=to_dev(bw.dht), initial_state=to_dev(f.initial_state), cu_seqlens=cu,
+        use_qk_l2norm_in_kernel=True, A_log=to_dev(A_log), dt_bias=to_dev(dt_bias))
+    torch.cuda.synchronize()
+    names = NAMES + ("dA_log", "ddt_bias")
+    x = {n: t.cpu().numpy().astype(np.float64) for n, t in zip(names, out)}
+    r = prefill_backward(W.as_f64(q, dtype), W.as_f64(k, dtype), W.as_f64(f.v, dtype),
+                         alpha.astype(np.float64), b.astype(np.float64),
+                         W.as_f64(bw.do, dtype), bw.dht.astype(np.float64),
+                         cu_seqlens=f.cu_seqlens, initial_state=f.initial_state.astype(np.float64),
+                         use_qk_l2norm=True, A_log=A_log.astype(np.float64),
+                         dt_bias=dt_bias.astype(np.float64))
+    compare(x, r, dtype == W.F32, f"l2norm + raw gates {dtype}", names=names)
+
+
+def test_backward_l2norm_only_fp32():
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    from oracle.backward import prefill_backward
+    bw = W.backward_workload("bwd_l2", 19, Hk=1, Hv=1, D=128, dtype=W.F32, B=1, T=100,
+                             decay="config")
+    f = bw.fwd
+    q, k, _, _, _, _ = _raw_inputs(bw, 19)
+    out = gdr.chunk_gated_delta_rule_backward(
+        to_dev(q), to_dev(k), to_dev(f.v), to_dev(f.g), to_dev(f.beta), to_dev(bw.do),
+        dht=to_dev(bw.dht), initial_state=to_dev(f.initial_state), use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    x = {n: t.cpu().numpy().astype(np.float64) for n, t in zip(NAMES, out)}
+    r = prefill_backward(q.astype(np.float64), k.astype(np.float64), f.v.astype(np.float64),
+                         f.g.astype(np.float64), f.beta.astype(np.float64),
+                         bw.do.astype(np.float64), bw.dht.astype(np.float64),
+                         initial_state=f.initial_state.astype(np.float64), use_qk_l2norm=True)
+    compare(x, r, True, "l2norm only fp32")
