@@ -191,3 +191,53 @@ def test_backward_l2norm_only_fp32():
                          bw.do.astype(np.float64), bw.dht.astype(np.float64),
                          initial_state=f.initial_state.astype(np.float64), use_qk_l2norm=True)
     compare(x, r, True, "l2norm only fp32")
+
+
+def test_backward_graph_replay():
+    """The backward call (forward recompute included) captured in a HIP graph: it
+    allocates nothing and launches on host-known grids, so every replay equals the
+    eager call bitwise."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    bw = W.backward_workload("bwd_graph", 20, Hk=2, Hv=4, D=128, dtype=W.BF16,
+                             lengths=[150, 9, 64], decay="config")
+    f = bw.fwd
+    d = {n: to_dev(getattr(f, n)) for n in ("q", "k", "v", "g", "beta")}
+    do, dht, h0 = to_dev(bw.do), to_dev(bw.dht), to_dev(f.initial_state)
+    cu = torch.from_numpy(f.cu_seqlens).cuda()
+    T, N = f.q.shape[1], len(f.cu_seqlens) - 1
+    shapes = ((1, T, 2, 128), (1, T, 2, 128), (1, T, 4, 128), (1, T, 4), (1, T, 4),
+              (N, 4, 128, 128))
+
+    def outs():
+        return [torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes]
+
+    def args(o):
+        return gdr.backward_args(d["q"], d["k"], d["v"], d["g"], d["beta"], do, dq=o[0],
+                                 dk=o[1], dv=o[2], dg=o[3], dbeta=o[4], dh0=o[5], dht=dht,
+                                 initial_state=h0, cu_seqlens=cu)
+
+    lib = gdr.library()
+    eo = outs()
+    a = args(eo)
+    ws = torch.empty(int(lib.gdr_backward_workspace_bytes(a)), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    assert lib.gdr_chunk_gated_delta_rule_backward(a, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+
+    go = outs()
+    ga = args(go)
+    gws = torch.empty_like(ws)
+    ga.workspace, ga.workspace_bytes = gws.data_ptr(), gws.numel()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rc = lib.gdr_chunk_gated_delta_rule_backward(ga, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    for r in range(3):
+        for t in go:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(go, eo)):
+            assert torch.equal(x, y), f"replay {r}: output {i} differs"
+        _ = torch.ones(1, device="cuda").sum().item()   # eager work between replays
