@@ -60,23 +60,30 @@ def _spans(B, T, cu_seqlens):
 def forward_torch(q, k, v, g, beta, scale, H0):
     """The per-token recurrence on torch tensors for one sequence, all value heads.
 
-    q, k [L,Hk,K]; v [L,Hv,V]; g, beta [L,Hv]; H0 [Hv,K,V] (state S^T per head).
-    Value head h reads q/k head h // (Hv // Hk).  Returns (o [L,Hv,V], H_L).
+    q [L,Hk,K]; k [L,Hk,K] or [L,n_h,Hk,K]; v [L,Hv,V] or [L,n_h,Hv,V]; g [L,Hv];
+    beta [L,Hv] or [L,n_h,Hv]; H0 [Hv,K,V] (state S^T per head).  Value head h reads
+    q/k head h // (Hv // Hk).  With n_h Householder sub-steps per token (the gated
+    delta product) the decay exp(g_t) is applied once, before the first sub-step,
+    each sub-step j writes beta_j (v_j - H^T k_j) along k_j, and o_t is read after
+    the last one.  Returns (o [L,Hv,V], H_L).
     """
     import torch
+    if k.dim() == 3:
+        k, v, beta = k[:, None], v[:, None], beta[:, None]
     L, Hk, _ = q.shape
-    Hv = v.shape[1]
+    n_h, Hv = k.shape[1], v.shape[2]
     hk = torch.arange(Hv) // (Hv // Hk)
     H = H0
     outs = []
     for t in range(L):
-        qt, kt = q[t, hk], k[t, hk]                      # [Hv, K]
-        a = torch.exp(g[t])                              # [Hv]
-        u = torch.einsum("hkv,hk->hv", H, kt)            # H^T k
-        d = beta[t][:, None] * (v[t] - a[:, None] * u)   # delta
-        H = a[:, None, None] * H + kt[:, :, None] * d[:, None, :]
-        outs.append(scale * torch.einsum("hkv,hk->hv", H, qt))
-    o = torch.stack(outs) if outs else torch.zeros((0,) + v.shape[1:], dtype=v.dtype)
+        H = torch.exp(g[t])[:, None, None] * H           # decay once per token
+        for j in range(n_h):
+            kt = k[t, j, hk]                             # [Hv, K]
+            u = torch.einsum("hkv,hk->hv", H, kt)        # H^T k
+            d = beta[t, j][:, None] * (v[t, j] - u)      # delta
+            H = H + kt[:, :, None] * d[:, None, :]
+        outs.append(scale * torch.einsum("hkv,hk->hv", H, q[t, hk]))
+    o = torch.stack(outs) if outs else torch.zeros((0, Hv, v.shape[-1]), dtype=v.dtype)
     return o, H
 
 
@@ -101,8 +108,10 @@ def prefill_backward(q, k, v, g, beta, do, dht=None, *, scale=None, cu_seqlens=N
                      A_log=None, dt_bias=None):
     """fp64 gradients of  L = <o, do> + <H_final, dht>  for the GDN recurrence.
 
-    Batched layout as in :func:`oracle.prefill` (n_h = 1): q, k [B,T,Hk,K];
-    v, do [B,T,Hv,V]; g, beta [B,T,Hv]; initial_state, dht [N,Hv,K,V] or None.
+    Batched layout as in :func:`oracle.prefill`: q [B,T,Hk,K]; k [B,T,Hk,K] or
+    [B,T,n_h,Hk,K]; v [B,T,Hv,V] or [B,T,n_h,Hv,V]; do [B,T,Hv,V]; g [B,T,Hv]; beta
+    [B,T,Hv] or [B,T,n_h,Hv]; initial_state, dht [N,Hv,K,V] or None.  The gradients
+    of k, v, beta have the shapes of k, v, beta.
     With ``use_qk_l2norm`` the recurrence reads q, k divided by their L2 norm and
     dq, dk are the gradients of the raw q, k.  With ``A_log`` and ``dt_bias`` ([Hv])
     g and beta hold the raw projections alpha and b, the gates are formed from them,
@@ -118,9 +127,10 @@ def prefill_backward(q, k, v, g, beta, do, dht=None, *, scale=None, cu_seqlens=N
         scale = 1.0 / np.sqrt(K)
     spans = _spans(B, T, cu_seqlens)
     N = len(spans)
-    res = {"dq": np.zeros((B, T, Hk, K)), "dk": np.zeros((B, T, Hk, K)),
-           "dv": np.zeros((B, T, Hv, V)), "dg": np.zeros((B, T, Hv)),
-           "dbeta": np.zeros((B, T, Hv)), "dh0": np.zeros((N, Hv, K, V))}
+    k, v, beta = np.asarray(k), np.asarray(v), np.asarray(beta)
+    res = {"dq": np.zeros((B, T, Hk, K)), "dk": np.zeros(k.shape),
+           "dv": np.zeros(v.shape), "dg": np.zeros((B, T, Hv)),
+           "dbeta": np.zeros(beta.shape), "dh0": np.zeros((N, Hv, K, V))}
     if return_forward:
         res["o"] = np.zeros((B, T, Hv, V))
         res["final_state"] = np.zeros((N, Hv, K, V))

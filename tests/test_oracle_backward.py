@@ -227,3 +227,68 @@ def test_l2norm_gradient_is_orthogonal_to_the_input():
     for x, dx in ((q, res["dq"]), (k, res["dk"])):
         dots = np.sum(x * dx, axis=-1)
         assert np.max(np.abs(dots)) < 1e-5 * np.max(np.abs(dx)), np.max(np.abs(dots))
+
+
+def _gdp_problem(seed, B=1, T=5, Hk=1, Hv=2, K=3, V=3, n_h=2):
+    r = np.random.default_rng(seed)
+    q = _unit(r, (B, T, Hk, K))
+    k = _unit(r, (B, T, n_h, Hk, K))
+    v = r.standard_normal((B, T, n_h, Hv, V))
+    g = -0.4 * r.uniform(0.0, 1.0, (B, T, Hv))
+    beta = r.uniform(0.05, 0.95, (B, T, n_h, Hv))
+    s0 = 0.5 * r.standard_normal((B, Hv, K, V))
+    do = r.standard_normal((B, T, Hv, V))
+    dht = r.standard_normal((B, Hv, K, V))
+    return q, k, v, g, beta, s0, do, dht
+
+
+def test_gdp_forward_equals_c_oracle():
+    q, k, v, g, beta, s0, do, dht = _gdp_problem(30, B=2, T=7, Hk=1, Hv=2, K=4, V=4)
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0, return_forward=True)
+    o, fs = oracle.prefill(q, k, v, g, beta, initial_state=s0, output_final_state=True,
+                           num_householder=2)
+    assert _maxdiff(res["o"], o) < 1e-13 and _maxdiff(res["final_state"], fs) < 1e-13
+
+
+def test_gdp_gradients_equal_finite_differences():
+    q, k, v, g, beta, s0, do, dht = _gdp_problem(31)
+    res = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0)
+    args = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "s0": s0}
+    name = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "s0": "dh0"}
+
+    def loss(a):
+        o, fs = oracle.prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], initial_state=a["s0"],
+                               output_final_state=True, num_householder=2)
+        return float(np.sum(o * do) + np.sum(fs * dht))
+
+    eps = 1e-6
+    for nm, x in args.items():
+        fd = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            fd[i] = (loss(dict(args, **{nm: xp})) - loss(dict(args, **{nm: xm}))) / (2 * eps)
+        assert _maxdiff(res[name[nm]], fd) < 1e-7, nm
+
+
+def test_gdp_gradients_equal_gdn_on_interleaved_rows():
+    # the product is the delta rule on rows t*n_h + j with the decay on each token's
+    # first row and the query (and dO) on its last row; the gradients map row by row
+    q, k, v, g, beta, s0, do, dht = _gdp_problem(32, T=6, Hk=1, Hv=2, K=4, V=4)
+    gdp = OB.prefill_backward(q, k, v, g, beta, do, dht, initial_state=s0)
+    B, T, n_h = q.shape[0], q.shape[1], 2
+    R = T * n_h
+    qr = np.zeros((B, R) + q.shape[2:])
+    qr[:, n_h - 1::n_h] = q
+    dor = np.zeros((B, R) + do.shape[2:])
+    dor[:, n_h - 1::n_h] = do
+    gr = np.zeros((B, R, g.shape[-1]))
+    gr[:, 0::n_h] = g
+    gdn = OB.prefill_backward(qr, k.reshape((B, R) + k.shape[3:]), v.reshape((B, R) + v.shape[3:]),
+                              gr, beta.reshape(B, R, -1), dor, dht, initial_state=s0)
+    assert _maxdiff(gdp["dq"], gdn["dq"][:, n_h - 1::n_h]) < 1e-13
+    assert _maxdiff(gdp["dg"], gdn["dg"][:, 0::n_h]) < 1e-13
+    for nm in ("dk", "dv", "dbeta"):
+        assert _maxdiff(gdp[nm], gdn[nm].reshape(gdp[nm].shape)) < 1e-13, nm
+    assert _maxdiff(gdp["dh0"], gdn["dh0"]) < 1e-13
