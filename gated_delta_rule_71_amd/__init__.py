@@ -420,6 +420,7 @@ def backward_args(q, k, v, g, beta, do, *, dq, dk, dv, dg, dbeta, dh0=None, dht=
     a.gate_mode = 0 if A_log is None else 1
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     a.dA_log, a.ddt_bias = _ptr(dA_log), _ptr(ddt_bias)
+    a.num_householder = k.shape[2] if k.dim() == 5 else 1
     return a
 
 
@@ -427,7 +428,8 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
                                     initial_state=None, cu_seqlens=None, *, workspace=None,
                                     stream=None, use_qk_l2norm_in_kernel=False, A_log=None,
                                     dt_bias=None):
-    """Gradients of the chunked prefill (gated delta rule, n_h = 1).
+    """Gradients of the chunked prefill (gated delta rule, or the gated delta
+    product when k, v are [B,T,n_h,H,D] and beta [B,T,n_h,Hv], n_h = 2).
 
     With ``use_qk_l2norm_in_kernel`` the forward normalised q and k, and dq, dk are
     the gradients of the raw q, k.  With ``A_log`` and ``dt_bias`` ([Hv] float32), g
@@ -444,10 +446,11 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
     torch = _torch()
     lib = library()
     _check(q, "q", ndim=4)
-    for name, t in (("k", k), ("v", v), ("do", do)):
-        _check(t, name, dtype=q.dtype, ndim=4)
+    _check(k, "k", dtype=q.dtype, ndim=(4, 5))
+    _check(v, "v", dtype=q.dtype, ndim=(4, 5))
+    _check(do, "do", dtype=q.dtype, ndim=4)
     _check(g, "g", dtype=torch.float32, ndim=3)
-    _check(beta, "beta", dtype=torch.float32, ndim=3)
+    _check(beta, "beta", dtype=torch.float32, ndim=(3, 4))
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1)
     for name, st in (("initial_state", initial_state), ("dht", dht)):
@@ -459,10 +462,10 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
     dev = q.device
     f32 = torch.float32
     dq = torch.empty((B, T, Hk, K), dtype=f32, device=dev)
-    dk = torch.empty((B, T, Hk, K), dtype=f32, device=dev)
-    dv = torch.empty((B, T, Hv, V), dtype=f32, device=dev)
+    dk = torch.empty(k.shape, dtype=f32, device=dev)
+    dv = torch.empty(v.shape, dtype=f32, device=dev)
     dg = torch.empty((B, T, Hv), dtype=f32, device=dev)
-    dbeta = torch.empty((B, T, Hv), dtype=f32, device=dev)
+    dbeta = torch.empty(beta.shape, dtype=f32, device=dev)
     dh0 = torch.empty((N, Hv, K, V), dtype=f32, device=dev)
     gate_mode, A_log, dt_bias = _gate_params(A_log, dt_bias, Hv, torch)
     dA_log = torch.empty((Hv,), dtype=f32, device=dev) if gate_mode else None
@@ -486,10 +489,11 @@ def chunk_gated_delta_rule_backward(q, k, v, g, beta, do, dht=None, scale=None,
     return dq, dk, dv, dg, dbeta, dh0
 
 
-def backward_workspace_bytes(q, v, *, num_seqs=None, num_qk_heads=None):
+def backward_workspace_bytes(q, v, *, num_seqs=None, num_qk_heads=None, num_householder=1):
     """gdr_backward_workspace_bytes for these shapes (host-only)."""
     B, T, Hk, K = q.shape
     a = _lib.BackwardArgs()
+    a.num_householder = int(num_householder)
     a.batch, a.seqlen = B, T
     a.num_seqs = B if num_seqs is None else int(num_seqs)
     a.num_qk_heads = Hk if num_qk_heads is None else int(num_qk_heads)

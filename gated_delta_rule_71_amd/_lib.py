@@ -159,6 +159,7 @@ class BackwardArgs(ctypes.Structure):
         ("use_qk_l2norm", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("dA_log", ctypes.c_void_p), ("ddt_bias", ctypes.c_void_p),
+        ("num_householder", ctypes.c_int32),
     ]
 
 

@@ -19,6 +19,9 @@
 //                  + diag(e^{G_n - G}) D dH_n^T,
 //   with dAs = dA * diag(beta) Gamma, dPs = scale dP * Gamma, and dbeta, dg from
 //   the same quantities (row sums, see bwd_grads_kernel).
+// With n_h Householder sub-steps per token (the gated delta product) the same
+// algebra runs on rows t * n_h + j: k, v, beta per row, g on each token's first row,
+// q and dO on its last row (zero on the others).
 // Only the dH0 recursion is sequential over a sequence's chunks; everything else
 // is local to a chunk once the chunk's entering state H0 and leaving gradient
 // dH_n are known.  Hence four launches after a table of chunk offsets:
@@ -98,6 +101,9 @@ __device__ __forceinline__ int chunk_seq(const int32_t *cb, int N, int c) {
   return lo;
 }
 
+// the rows [t0, t1) of sequence n: with n_h Householder sub-steps per token, row
+// t * n_h + j is sub-step j of token t (k, v, beta and their gradients are per row;
+// q, dO and dq sit on each token's last row, g and dg on its first)
 __device__ __forceinline__ void seq_span(const BackwardParams &p, int n, int &t0, int &t1) {
   if (p.cu_seqlens) {
     t0 = p.cu_seqlens[n];
@@ -106,6 +112,8 @@ __device__ __forceinline__ void seq_span(const BackwardParams &p, int n, int &t0
     t0 = n * p.seqlen;
     t1 = t0 + p.seqlen;
   }
+  t0 *= p.nh;
+  t1 *= p.nh;
 }
 
 // Per-chunk row factors in LDS: the fp64 cumulative decay G (restarting at the
@@ -118,7 +126,10 @@ struct RowFactors {
 __device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams &p, int h, int ts,
                                             int rows, int tid) {
   if (tid < BC) {
-    double x = tid < rows ? static_cast<double>(p.g[static_cast<size_t>(ts + tid) * p.Hv + h]) : 0.0;
+    const int row = ts + tid;
+    double x = (tid < rows && row % p.nh == 0)
+                   ? static_cast<double>(p.g[static_cast<size_t>(row / p.nh) * p.Hv + h])
+                   : 0.0;
 #pragma unroll
     for (int o = 1; o < BC; o <<= 1) {
       const double y = __shfl_up(x, o, 64);
@@ -140,26 +151,30 @@ template <typename TIn, int D, int NC>
 struct RowsRegs {
   static constexpr int SEGS = NC / 8, UNITS = BC * SEGS, PER = (UNITS + BT - 1) / BT;
   Seg8<TIn> buf[PER];
+  // nh > 1: a per-token input (q, dO) read on rows, token (ts + r) / nh, present
+  // only on each token's last row
   __device__ __forceinline__ void fetch(const TIn *src, int heads, int hd, int ts, int rows,
-                                        int col0, int tid) {
+                                        int col0, int tid, int nh = 1) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = tid + j * BT;
       const int r = min(u / SEGS, rows - 1), sg = u % SEGS;
       if (UNITS % BT == 0 || u < UNITS)
-        buf[j].load(src + (static_cast<size_t>(ts + r) * heads + hd) * D + col0 + 8 * sg);
+        buf[j].load(src + (static_cast<size_t>((ts + r) / nh) * heads + hd) * D + col0 + 8 * sg);
     }
   }
-  __device__ __forceinline__ void store(float *dst, int ld, int rows, int tid) const {
+  __device__ __forceinline__ void store(float *dst, int ld, int rows, int tid, int ts = 0,
+                                        int nh = 1) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = tid + j * BT;
       const int r = u / SEGS, sg = u % SEGS;
       if (UNITS % BT == 0 || u < UNITS) {
+        const bool ok = r < rows && (nh == 1 || (ts + r) % nh == nh - 1);
         float x[8];
         buf[j].get(x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[r * ld + 8 * sg + e] = r < rows ? x[e] : 0.0f;
+        for (int e = 0; e < 8; ++e) dst[r * ld + 8 * sg + e] = ok ? x[e] : 0.0f;
       }
     }
   }
@@ -167,10 +182,10 @@ struct RowsRegs {
 
 template <typename TIn, int D, int NC>
 __device__ __forceinline__ void load_rows(float *dst, int ld, const TIn *src, int heads, int hd,
-                                          int ts, int rows, int col0, int tid) {
+                                          int ts, int rows, int col0, int tid, int nh = 1) {
   RowsRegs<TIn, D, NC> r;
-  r.fetch(src, heads, hd, ts, rows, col0, tid);
-  r.store(dst, ld, rows, tid);
+  r.fetch(src, heads, hd, ts, rows, col0, tid, nh);
+  r.store(dst, ld, rows, tid, ts, nh);
 }
 
 // An NR x NC float32 matrix (global row stride gs; NULL reads as zeros) through
@@ -265,7 +280,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const int hk = h / (p.Hv / p.Hk);
 
   load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
+                       p.nh);
   row_factors(rf, p, h, ts, rows, tid);
   __syncthreads();
 
@@ -434,8 +450,8 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
     const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
     fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-    fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
-    fo.fetch(dO, p.Hv, h, ts, rows, col0, tid);
+    fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+    fo.fetch(dO, p.Hv, h, ts, rows, col0, tid, p.nh);
     fp.fetch(p.pmat + cc * BC * BC, BC, tid);
     ft.fetch(p.tmat + cc * BC * BC, BC, tid);
   };
@@ -454,8 +470,8 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
         sdH[r * LDV + q] = dh[t][v];
       }
     fk.store(sK, LDD, rows, tid);
-    fq.store(sQ, LDD, rows, tid);
-    fo.store(sO, LDV, rows, tid);
+    fq.store(sQ, LDD, rows, tid, ts, p.nh);
+    fo.store(sO, LDV, rows, tid, ts, p.nh);
     fp.store(sP, LDC, tid);
     ft.store(sT, LDC, tid);
     row_factors(rf, p, h, ts, rows, tid);
@@ -584,7 +600,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     auto fetch = [&](int vb) {
       fD.fetch(dm + vb, D, tid);
       fR.fetch(drm + vb, D, tid);
-      fO.fetch(static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, tid);
+      fO.fetch(static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, tid, p.nh);
       fV.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
       fH.fetch(h0 ? h0 + vb : nullptr, D, tid);
       fG.fetch(dhn + vb, D, tid);
@@ -594,7 +610,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       __syncthreads();
       fD.store(sDb, LDV, tid);
       fR.store(sRb, LDV, tid);
-      fO.store(sOb, LDV, rows, tid);
+      fO.store(sOb, LDV, rows, tid, ts, p.nh);
       fV.store(svb, LDV, rows, tid);
       fH.store(sHb, LDV, tid);
       fG.store(sGb, LDV, tid);
@@ -637,7 +653,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       }
   }
   load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
+                       p.nh);
   if (tid < BC) srv[tid] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
@@ -705,8 +722,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = wd.row(v, lane);
-        if (r < rows)
-          dst[static_cast<size_t>(ts + r) * rs + wd.col(t, lane)] =
+        if (r < rows && (ts + r) % p.nh == p.nh - 1)   // query rows: one per token
+          dst[static_cast<size_t>((ts + r) / p.nh) * rs + wd.col(t, lane)] =
               dq[t][v] + p.scale * rf.eG[r] * U1[t][v];
       }
   }
@@ -769,28 +786,30 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     }
     if (r < rows) {
       p.dbeta[static_cast<size_t>(ts + r) * p.Hv + h] = db;
-      p.dg[static_cast<size_t>(ts + r) * p.Hv + h] = s;
+      // g_t sits on the token's first row: dg_t = sum of dG over the rows from there
+      if ((ts + r) % p.nh == 0) p.dg[static_cast<size_t>((ts + r) / p.nh) * p.Hv + h] = s;
     }
   }
 }
 
-// grouped heads: dq[t, hk] = sum of the group's per-value-head dq (same for dk)
+// grouped heads: dq[t, hk] = sum of the group's per-value-head dq (tokens), and
+// the same for dk (rows)
 template <int D>
-__global__ void bwd_group_sum_kernel(const BackwardParams p, long total) {
+__global__ void bwd_group_sum_kernel(const BackwardParams p, long total_q, long total_k) {
   const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
+  if (i >= total_k) return;
   const int e = static_cast<int>(i % D);
-  const long th = i / D;                 // token * Hk + hk
+  const long th = i / D;                 // row * Hk + hk
   const int hk = static_cast<int>(th % p.Hk);
   const long t = th / p.Hk;
   const int grp = p.Hv / p.Hk;
   float sq = 0.0f, sk = 0.0f;
   for (int m = 0; m < grp; ++m) {
     const size_t src = (static_cast<size_t>(t) * p.Hv + hk * grp + m) * D + e;
-    sq += p.dq_h[src];
+    if (i < total_q) sq += p.dq_h[src];
     sk += p.dk_h[src];
   }
-  p.dq[i] = sq;
+  if (i < total_q) p.dq[i] = sq;
   p.dk[i] = sk;
 }
 
@@ -798,12 +817,13 @@ __global__ void bwd_group_sum_kernel(const BackwardParams p, long total) {
 
 // one wave per (token, q/k head) row of D: x / sqrt(sum x^2 + 1e-6) into fp32 copies
 template <typename TIn, int D>
-__global__ void bwd_l2norm_kernel(const BackwardParams p, float *qn, float *kn, long rows) {
+__global__ void bwd_l2norm_kernel(const BackwardParams p, float *qn, float *kn, long rows_q,
+                                  long rows) {
   const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   constexpr int E = D / 64;
-  for (int w = 0; w < 2; ++w) {
+  for (int w = row < rows_q ? 0 : 1; w < 2; ++w) {
     const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
     float *dst = (w ? kn : qn) + row * D;
     float x[E], ss = 0.0f;
@@ -820,24 +840,26 @@ __global__ void bwd_l2norm_kernel(const BackwardParams p, float *qn, float *kn, 
   }
 }
 
-// g = -exp(A_log) softplus(alpha + dt_bias), beta = sigmoid(b) per (token, value head)
-__global__ void bwd_gates_kernel(const BackwardParams p, float *g, float *beta, long n) {
+// g = -exp(A_log) softplus(alpha + dt_bias) per (token, value head) and
+// beta = sigmoid(b) per (row, value head)
+__global__ void bwd_gates_kernel(const BackwardParams p, float *g, float *beta, long n_tok,
+                                 long n_row) {
   const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  if (i >= n_row) return;
   const int h = static_cast<int>(i % p.Hv);
-  g[i] = gate_decay(p.alpha_raw[i], expf(p.A_log[h]), p.dt_bias[h]);
+  if (i < n_tok) g[i] = gate_decay(p.alpha_raw[i], expf(p.A_log[h]), p.dt_bias[h]);
   beta[i] = gate_beta(p.b_raw[i]);
 }
 
 // dx = (dx^ - x^ (x^ . dx^)) / n with n = sqrt(sum x^2 + 1e-6), x^ = x / n, in place
 // on dq and dk (one wave per row)
 template <typename TIn, int D>
-__global__ void bwd_l2norm_grad_kernel(const BackwardParams p, long rows) {
+__global__ void bwd_l2norm_grad_kernel(const BackwardParams p, long rows_q, long rows) {
   const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   constexpr int E = D / 64;
-  for (int w = 0; w < 2; ++w) {
+  for (int w = row < rows_q ? 0 : 1; w < 2; ++w) {
     const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
     float *dx = (w ? p.dk : p.dq) + row * D;
     float x[E], d[E], ss = 0.0f;
@@ -876,10 +898,13 @@ __global__ void __launch_bounds__(256) bwd_gates_grad_kernel(const BackwardParam
     const float g = -A * softplus_f32(x);
     const float da = -dg * A / (1.0f + expf(-x));
     p.dg[i] = da;
-    const float b = gate_beta(p.b_raw[i]);
-    p.dbeta[i] *= b * (1.0f - b);
     sa = fmaf(dg, g, sa);
     sd += da;
+  }
+  for (long t = tid; t < p.tokens * p.nh; t += 256) {
+    const size_t i = static_cast<size_t>(t) * p.Hv + h;
+    const float b = gate_beta(p.b_raw[i]);
+    p.dbeta[i] *= b * (1.0f - b);
   }
   red[0][tid] = sa;
   red[1][tid] = sd;
@@ -921,9 +946,9 @@ hipError_t launch_bwd_d(const BackwardParams &p, int max_chunks, long tokens, hi
   else
     launch_bwd_qk<TIn, TIn, D>(p, max_chunks, s);
   if (p.Hv != p.Hk && tokens > 0) {
-    const long total = tokens * p.Hk * D;
-    hipLaunchKernelGGL((bwd_group_sum_kernel<D>), dim3((total + 255) / 256), dim3(256), 0, s, p,
-                       total);
+    const long total_q = tokens * p.Hk * D, total_k = total_q * p.nh;
+    hipLaunchKernelGGL((bwd_group_sum_kernel<D>), dim3((total_k + 255) / 256), dim3(256), 0, s,
+                       p, total_q, total_k);
   }
   return hipGetLastError();
 }
@@ -938,25 +963,25 @@ hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream) {
 template <typename TIn, int D>
 hipError_t launch_pro_d(const BackwardParams &p, hipStream_t s) {
   if (p.q_raw) {
-    const long rows = p.tokens * p.Hk;
+    const long rows_q = p.tokens * p.Hk, rows = rows_q * p.nh;
     hipLaunchKernelGGL((bwd_l2norm_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s, p,
                        const_cast<float *>(static_cast<const float *>(p.q)),
-                       const_cast<float *>(static_cast<const float *>(p.k)), rows);
+                       const_cast<float *>(static_cast<const float *>(p.k)), rows_q, rows);
   }
   if (p.alpha_raw) {
-    const long n = p.tokens * p.Hv;
-    hipLaunchKernelGGL(bwd_gates_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p,
-                       const_cast<float *>(p.g), const_cast<float *>(p.beta), n);
+    const long n_tok = p.tokens * p.Hv, n_row = n_tok * p.nh;
+    hipLaunchKernelGGL(bwd_gates_kernel, dim3((n_row + 255) / 256), dim3(256), 0, s, p,
+                       const_cast<float *>(p.g), const_cast<float *>(p.beta), n_tok, n_row);
   }
   return hipGetLastError();
 }
 
 template <typename TIn, int D>
 hipError_t launch_epi_d(const BackwardParams &p, hipStream_t s) {
-  const long rows = p.tokens * p.Hk;
+  const long rows_q = p.tokens * p.Hk, rows = rows_q * p.nh;
   if (p.q_raw && rows > 0)
     hipLaunchKernelGGL((bwd_l2norm_grad_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s,
-                       p, rows);
+                       p, rows_q, rows);
   if (p.alpha_raw) hipLaunchKernelGGL(bwd_gates_grad_kernel, dim3(p.Hv), dim3(256), 0, s, p);
   return hipGetLastError();
 }

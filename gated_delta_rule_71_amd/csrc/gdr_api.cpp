@@ -75,8 +75,10 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
   if ((a->initial_state && !aligned16(a->initial_state)) ||
       (a->final_state && !aligned16(a->final_state)))
     return GDR_ERR_INVALID_ARG;
-  if (a->boundary_states && (!aligned16(a->boundary_states) || a->boundary_interval <= 0 ||
-                             a->boundary_interval % 64 != 0))
+  // boundary states every multiple of 64 rows (64 / n_h tokens)
+  if (a->boundary_states &&
+      (!aligned16(a->boundary_states) || a->boundary_interval <= 0 ||
+       (int64_t{a->boundary_interval} * a->num_householder) % 64 != 0))
     return GDR_ERR_INVALID_ARG;
   if (a->workspace_bytes < gdr_prefill_workspace_bytes(a)) return GDR_ERR_WORKSPACE;
   return GDR_OK;
@@ -202,13 +204,15 @@ struct BwdLayout {
 BwdLayout bwd_layout(const gdr_backward_args *a) {
   BwdLayout L{};
   const size_t tokens = static_cast<size_t>(a->batch) * a->seqlen;
+  const size_t nh = static_cast<size_t>(a->num_householder);
+  const size_t rows = tokens * nh;   // one row per Householder sub-step
   const size_t N = static_cast<size_t>(a->num_seqs);
   const size_t D = static_cast<size_t>(a->head_k);
   const size_t Hv = static_cast<size_t>(a->num_v_heads);
-  // chunks: sum of ceil(L_n / 64) <= (tokens + 63 N) / 64; boundary states:
-  // sum of floor(L_n / 64) <= tokens / 64
-  const size_t chunks = (tokens + 63 * N) / 64;
-  const size_t entries = tokens / 64;
+  // 64-row chunks: sum of ceil(R_n / 64) <= (rows + 63 N) / 64; boundary states:
+  // sum of floor(R_n / 64) <= rows / 64
+  const size_t chunks = (rows + 63 * N) / 64;
+  const size_t entries = rows / 64;
   L.max_chunks = static_cast<int>(chunks);
   const size_t elem = a->qkv_dtype == GDR_DTYPE_F32 ? 4 : 2;
   size_t off = 0;
@@ -228,12 +232,12 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   L.drmat = take(chunks * Hv * 64 * D * 4);
   const bool grouped = a->num_v_heads != a->num_qk_heads;
   L.dqh = take(grouped ? tokens * Hv * D * 4 : 0);
-  L.dkh = take(grouped ? tokens * Hv * D * 4 : 0);
+  L.dkh = take(grouped ? rows * Hv * D * 4 : 0);
   const size_t Hk = static_cast<size_t>(a->num_qk_heads);
   L.qn = take(a->use_qk_l2norm ? tokens * Hk * D * 4 : 0);
-  L.kn = take(a->use_qk_l2norm ? tokens * Hk * D * 4 : 0);
+  L.kn = take(a->use_qk_l2norm ? rows * Hk * D * 4 : 0);
   L.gg = take(a->gate_mode ? tokens * Hv * 4 : 0);
-  L.gb = take(a->gate_mode ? tokens * Hv * 4 : 0);
+  L.gb = take(a->gate_mode ? rows * Hv * 4 : 0);
   L.total = off;
   return L;
 }
@@ -257,13 +261,19 @@ int gdr_validate_backward(const gdr_backward_args *a) {
   } else if (a->num_seqs != a->batch) {
     return GDR_ERR_INVALID_ARG;
   }
+  if (a->num_householder < 1) return GDR_ERR_INVALID_ARG;
   if (a->head_k != a->head_v || !head_ok(a->head_k)) return GDR_ERR_UNSUPPORTED;
+  if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
+  // the forward recompute of the gated delta product has no float32 path at D = 128
+  if (a->num_householder == 2 && a->qkv_dtype == GDR_DTYPE_F32 && a->head_k == 128)
+    return GDR_ERR_UNSUPPORTED;
   const int64_t tokens = int64_t{a->batch} * a->seqlen;
-  if (tokens > kMaxRows) return GDR_ERR_UNSUPPORTED;
+  if (tokens * a->num_householder > kMaxRows) return GDR_ERR_UNSUPPORTED;
   {
     const int64_t kw = int64_t{a->num_qk_heads} * a->head_k;
     const int64_t vw = int64_t{a->num_v_heads} * a->head_v;
-    if (tokens * (kw > vw ? kw : vw) >= (int64_t{1} << 32)) return GDR_ERR_UNSUPPORTED;
+    if (tokens * a->num_householder * (kw > vw ? kw : vw) >= (int64_t{1} << 32))
+      return GDR_ERR_UNSUPPORTED;
   }
   if (int64_t{a->num_seqs} * a->num_v_heads * (a->head_v / 32) > kMaxRows)
     return GDR_ERR_UNSUPPORTED;
@@ -333,6 +343,7 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
   p.dq_h = reinterpret_cast<float *>(ws + L.dqh);
   p.dk_h = reinterpret_cast<float *>(ws + L.dkh);
   p.tokens = tokens;
+  p.nh = a->num_householder;
   if (a->use_qk_l2norm) {
     // the backward kernels read the normalised copies; the raw inputs serve the
     // chain rule through the norm
@@ -365,8 +376,8 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
     f.num_v_heads = a->num_v_heads;
     f.head_k = a->head_k;
     f.head_v = a->head_v;
-    f.num_householder = 1;
-    f.chunk_size = 64;
+    f.num_householder = a->num_householder;
+    f.chunk_size = 64 / a->num_householder;
     f.qkv_dtype = a->qkv_dtype;
     f.out_dtype = a->qkv_dtype;
     f.use_qk_l2norm = a->use_qk_l2norm;
@@ -383,7 +394,7 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
     f.initial_state = a->initial_state;
     f.out = ws + L.o;
     f.boundary_states = p.states;
-    f.boundary_interval = 64;
+    f.boundary_interval = 64 / a->num_householder;   // every 64 rows
     const int fs = gdr_chunk_gated_delta_rule(&f, stream);
     if (fs != GDR_OK) return fs;
   }

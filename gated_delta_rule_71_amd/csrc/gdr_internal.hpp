@@ -89,19 +89,19 @@ struct NormParams {
 
 struct BackwardParams {
   const void *q;                 // [Tt, Hk, D]
-  const void *k;                 // [Tt, Hk, D]
-  const void *v;                 // [Tt, Hv, D]
+  const void *k;                 // [Tt * n_h, Hk, D]
+  const void *v;                 // [Tt * n_h, Hv, D]
   const float *g;                // [Tt, Hv]
-  const float *beta;             // [Tt, Hv]
+  const float *beta;             // [Tt * n_h, Hv]
   const int32_t *cu_seqlens;     // NULL: batched
   const float *initial_state;    // [N, Hv, D, D] or NULL (zeros)
   const void *d_out;             // [Tt, Hv, D], q's dtype
   const float *d_final_state;    // [N, Hv, D, D] or NULL (zeros)
   float *dq;                     // [Tt, Hk, D]
-  float *dk;                     // [Tt, Hk, D]
-  float *dv;                     // [Tt, Hv, D]
+  float *dk;                     // [Tt * n_h, Hk, D]
+  float *dv;                     // [Tt * n_h, Hv, D]
   float *dg;                     // [Tt, Hv]
-  float *dbeta;                  // [Tt, Hv]
+  float *dbeta;                  // [Tt * n_h, Hv]
   float *d_initial_state;        // [N, Hv, D, D] or NULL (not written)
   int seqlen;
   int num_seqs;
@@ -119,7 +119,7 @@ struct BackwardParams {
   float *dmat;                   // [chunks, Hv, 64, D] D = T R
   float *drmat;                  // [chunks, Hv, 64, D] dR = T^T dD
   float *dq_h;                   // [Tt, Hv, D] per value head (grouped heads only)
-  float *dk_h;                   // [Tt, Hv, D]
+  float *dk_h;                   // [Tt * n_h, Hv, D]
   // in-kernel L2 norm: q, k above point at the normalised fp32 copies, these at the
   // raw inputs (NULL without the norm)
   const void *q_raw;
@@ -133,6 +133,7 @@ struct BackwardParams {
   float *dA_log;                 // [Hv]
   float *ddt_bias;               // [Hv]
   long tokens;
+  int nh;                        // Householder sub-steps per token (rows per token)
 };
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).

@@ -295,9 +295,10 @@ class BackwardWorkload:
 
 
 def backward_workload(name, seed, *, Hk, Hv, D, dtype, B=1, T=None, lengths=None,
-                      decay="config", initial_state=True, final_grad=True):
+                      decay="config", initial_state=True, final_grad=True, num_householder=1):
     """Backward inputs: batched (B, T) or packed (``lengths``, B = 1), q/k/v/g/beta as
-    in the forward recipe, initial states ~ N(0, 0.1), dO and dH_T ~ N(0, 1)."""
+    in the forward recipe (k, v, beta per Householder sub-step when
+    ``num_householder`` > 1), initial states ~ N(0, 0.1), dO and dH_T ~ N(0, 1)."""
     rng = np.random.default_rng([seed, 0xBAC])
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
@@ -307,14 +308,16 @@ def backward_workload(name, seed, *, Hk, Hv, D, dtype, B=1, T=None, lengths=None
         B, T = 1, int(cu[-1])
     else:
         N, cu = B, None
+    n_h = int(num_householder)
+    sub = () if n_h == 1 else (n_h,)
     q = store(_unit_rows(rng, (B, T, Hk, D)), dtype)
-    k = store(_unit_rows(rng, (B, T, Hk, D)), dtype)
-    v = store(rng.standard_normal((B, T, Hv, D), dtype=np.float32), dtype)
-    beta = _beta(rng, (B, T, Hv))
+    k = store(_unit_rows(rng, (B, T) + sub + (Hk, D)), dtype)
+    v = store(rng.standard_normal((B, T) + sub + (Hv, D), dtype=np.float32), dtype)
+    beta = _beta(rng, (B, T) + sub + (Hv,))
     g = _gates(rng, T, Hv, decay, batch=B)
     h0 = (0.1 * rng.standard_normal((N, Hv, D, D), dtype=np.float32)).astype(np.float32) \
         if initial_state else None
-    fwd = PrefillWorkload(name, dtype, q, k, v, g, beta, 64, 1, cu_seqlens=cu,
+    fwd = PrefillWorkload(name, dtype, q, k, v, g, beta, 64 // n_h, n_h, cu_seqlens=cu,
                           initial_state=h0, meta={"seed": seed, "decay": decay})
     do = store(rng.standard_normal((B, T, Hv, D), dtype=np.float32), dtype)
     dht = rng.standard_normal((N, Hv, D, D), dtype=np.float32) if final_grad else None

@@ -104,7 +104,8 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
  *   min(chunk_size * n_h, 32) rows (16 rows for float32 inputs with K = 128).
  * boundary_states (optional, for prefix caching; the per-chunk states of page
  *   "core.ssm.gated_delta_product", ssm_prefill): the state of every sequence
- *   after each whole multiple of boundary_interval tokens from its start.
+ *   after each whole multiple of boundary_interval tokens from its start
+ *   (boundary_interval * n_h a positive multiple of 64).
  *   Sequence n of L_n tokens writes floor(L_n / boundary_interval) entries, at
  *   rows off_n + j, off_n = sum over m < n of floor(L_m / boundary_interval);
  *   entry j holds the state after the sequence's first (j + 1) * boundary_interval
@@ -146,7 +147,7 @@ typedef struct {
   const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
   const float *dt_bias;     /* [Hv] float32, gate_mode 1 only (else ignored)        */
   float *boundary_states;   /* [E, Hv, K, V] float32 or NULL (below)                */
-  int32_t boundary_interval; /* tokens, a positive multiple of 64 (boundary_states) */
+  int32_t boundary_interval; /* tokens, times n_h a multiple of 64 (boundary_states)*/
 } gdr_prefill_args;
 
 /*
@@ -288,12 +289,15 @@ typedef struct {
  * dL/d(initial_state).  The forward states every 64 tokens are recomputed inside
  * the call (into the workspace), so nothing from the forward call is needed.
  *
- * Shapes (Tt = batch * seqlen tokens; with cu_seqlens, batch must be 1; n_h = 1):
- *   q, k [Tt, Hk, D]; v, d_out [Tt, Hv, D] (qkv_dtype, one dtype for all four);
- *   g, beta [Tt, Hv] float32; initial_state, d_final_state [N, Hv, D, D] float32
- *   (the [K, V] layout of states) or NULL (zeros);
- *   outputs, all float32: dq, dk [Tt, Hk, D] (a q/k head receives the sum over
- *   the value heads that read it), dv [Tt, Hv, D], dg, dbeta [Tt, Hv],
+ * Shapes (Tt = batch * seqlen tokens; with cu_seqlens, batch must be 1; n_h =
+ * num_householder sub-steps per token, 1 for the gated delta rule, 2 for the
+ * gated delta product as in the prefill):
+ *   q [Tt, Hk, D]; k [Tt, n_h, Hk, D]; v [Tt, n_h, Hv, D]; d_out [Tt, Hv, D]
+ *   (qkv_dtype, one dtype for all four); g [Tt, Hv] and beta [Tt, n_h, Hv]
+ *   float32; initial_state, d_final_state [N, Hv, D, D] float32 (the [K, V]
+ *   layout of states) or NULL (zeros);
+ *   outputs, all float32, shaped like their inputs: dq, dk (a q/k head receives
+ *   the sum over the value heads that read it), dv, dg, dbeta, and
  *   d_initial_state [N, Hv, D, D] or NULL (not written).
  * use_qk_l2norm = 1: the forward divided q and k by sqrt(sum x^2 + 1e-6) (the
  *   in-kernel norm of the prefill); dq, dk are the gradients of the raw q, k.
@@ -309,7 +313,8 @@ typedef struct {
  *   leaving state and five 64 x 64 or 64 x D float32 matrices (about
  *   2 D^2 + 3 * 64^2 + 2 * 64 D floats, 200 KiB at D = 128), plus float32 copies
  *   of the normalised q, k (use_qk_l2norm) and of the formed gates (gate_mode 1).
- * Supported: head_k == head_v = D in {64, 128}; q/k/v/d_out F32 or BF16.
+ * Supported: head_k == head_v = D in {64, 128}; q/k/v/d_out F32 or BF16;
+ *   n_h in {1, 2} (n_h = 2 with F32 inputs only at D = 64, as in the prefill).
  * The outputs must not alias the inputs or the workspace.
  */
 typedef struct {
@@ -345,6 +350,7 @@ typedef struct {
   const float *dt_bias;     /* [Hv], gate_mode 1                                    */
   float *dA_log;            /* [Hv] output, gate_mode 1                             */
   float *ddt_bias;          /* [Hv] output, gate_mode 1                             */
+  int32_t num_householder;  /* n_h: 1 or 2                                          */
 } gdr_backward_args;
 
 /* Version of this ABI (GDR_ABI_VERSION). */

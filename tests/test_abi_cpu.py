@@ -155,7 +155,7 @@ def _backward(**kw):
     base = dict(batch=2, seqlen=100, num_seqs=2, num_qk_heads=2, num_v_heads=4, head_k=128,
                 head_v=128, qkv_dtype=1, scale=math.nan, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
                 beta=FAKE, d_out=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE,
-                workspace=FAKE)
+                workspace=FAKE, num_householder=1)
     base.update(kw)
     for k, v in base.items():
         setattr(a, k, v)
@@ -217,3 +217,25 @@ def test_backward_workspace_grows_with_norm_and_gates(lib):
     gates = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(gate_mode=1)))
     assert norm >= base + 2 * 200 * 2 * 128 * 4          # fp32 normalised q and k
     assert gates >= base + 2 * 200 * 4 * 4               # fp32 g and beta
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_householder=0), _lib.GDR_ERR_INVALID_ARG),
+    (dict(num_householder=3), _lib.GDR_ERR_UNSUPPORTED),
+    (dict(num_householder=2, qkv_dtype=0), _lib.GDR_ERR_UNSUPPORTED),   # f32 at D = 128
+    (dict(num_householder=2, qkv_dtype=0, head_k=64, head_v=64), _lib.GDR_OK),
+    (dict(num_householder=2), _lib.GDR_OK),
+])
+def test_backward_validation_householder(lib, kw, code):
+    assert lib.gdr_validate_backward(ctypes.byref(_backward(**kw))) == code
+
+
+def test_backward_workspace_counts_rows(lib):
+    one = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward()))
+    two = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(num_householder=2)))
+    # 200 tokens, 2 sequences, Hv = 4, D = 128; n_h = 2 doubles the rows: 8 instead
+    # of 5 chunks of 64 rows (per chunk and head D^2 + 3 * 64^2 + 2 * 64 D floats),
+    # 6 instead of 3 boundary states, and the per-row dk of the grouped heads
+    per_chunk = 4 * (128 * 128 + 3 * 64 * 64 + 2 * 64 * 128) * 4
+    extra = 3 * per_chunk + 3 * 4 * 128 * 128 * 4 + 200 * 4 * 128 * 4
+    assert abs(two - one - extra) <= 8 * 256

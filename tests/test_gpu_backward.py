@@ -241,3 +241,67 @@ def test_backward_graph_replay():
         for i, (x, y) in enumerate(zip(go, eo)):
             assert torch.equal(x, y), f"replay {r}: output {i} differs"
         _ = torch.ones(1, device="cuda").sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("dtype,D", [(W.F32, 64), (W.BF16, 128)])
+def test_backward_product_packed_grouped(dtype, D):
+    """The gated delta product (two Householder sub-steps per token): ragged packed
+    sequences around the 32-token (64-row) chunk, grouped heads."""
+    bw = W.backward_workload("bwd_gdp", 21, Hk=2, Hv=4, D=D, dtype=dtype,
+                             lengths=[1, 31, 32, 33, 0, 100], decay="slow", num_householder=2)
+    compare(gpu_backward(bw), oracle_backward(bw), dtype == W.F32, f"gdp packed {dtype}")
+
+
+@pytest.mark.parametrize("decay", ["config", "zero"])
+def test_backward_product_bf16_B2_T150(decay):
+    bw = W.backward_workload("bwd_gdp_b", 22, Hk=2, Hv=2, D=128, dtype=W.BF16, B=2, T=150,
+                             decay=decay, num_householder=2)
+    compare(gpu_backward(bw), oracle_backward(bw), False, f"gdp B2 T150 {decay}")
+
+
+def test_backward_product_l2norm_and_raw_gates():
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    from oracle.backward import prefill_backward
+    bw = W.backward_workload("bwd_gdp_raw", 23, Hk=1, Hv=2, D=64, dtype=W.F32,
+                             lengths=[45, 70], decay="slow", num_householder=2)
+    f = bw.fwd
+    q, k, alpha, b, A_log, dt_bias = _raw_inputs(bw, 23)
+    cu = torch.from_numpy(f.cu_seqlens).cuda()
+    out = gdr.chunk_gated_delta_rule_backward(
+        to_dev(q), to_dev(k), to_dev(f.v), to_dev(alpha), to_dev(b), to_dev(bw.do),
+        dht=to_dev(bw.dht), initial_state=to_dev(f.initial_state), cu_seqlens=cu,
+        use_qk_l2norm_in_kernel=True, A_log=to_dev(A_log), dt_bias=to_dev(dt_bias))
+    torch.cuda.synchronize()
+    names = NAMES + ("dA_log", "ddt_bias")
+    x = {n: t.cpu().numpy().astype(np.float64) for n, t in zip(names, out)}
+    r = prefill_backward(q.astype(np.float64), k.astype(np.float64), f.v.astype(np.float64),
+                         alpha.astype(np.float64), b.astype(np.float64),
+                         bw.do.astype(np.float64), bw.dht.astype(np.float64),
+                         cu_seqlens=f.cu_seqlens, initial_state=f.initial_state.astype(np.float64),
+                         use_qk_l2norm=True, A_log=A_log.astype(np.float64),
+                         dt_bias=dt_bias.astype(np.float64))
+    compare(x, r, True, "gdp l2norm + raw gates", names=names)
+
+
+def test_backward_product_T4096_H8_sampled():
+    """A longer gated delta product (B=1, T=4096, H=8, D=128, bf16, config decay) with
+    two sampled heads against the oracle."""
+    from oracle.backward import prefill_backward
+    bw = W.backward_workload("bwd_gdp_long", 24, Hk=8, Hv=8, D=128, dtype=W.BF16, B=1, T=4096,
+                             decay="config", num_householder=2)
+    x = gpu_backward(bw)
+    f = bw.fwd
+    for h in (0, 7):
+        sl = (slice(0, 1), slice(None))
+        hs = slice(h, h + 1)
+        r = prefill_backward(W.as_f64(f.q[:, :, hs], f.dtype), W.as_f64(f.k[:, :, :, hs], f.dtype),
+                             W.as_f64(f.v[:, :, :, hs], f.dtype), f.g[:, :, hs].astype(np.float64),
+                             f.beta[:, :, :, hs].astype(np.float64),
+                             W.as_f64(bw.do[:, :, hs], f.dtype),
+                             bw.dht[:, hs].astype(np.float64),
+                             initial_state=f.initial_state[:, hs].astype(np.float64))
+        xs = {"dq": x["dq"][:, :, hs], "dk": x["dk"][:, :, :, hs], "dv": x["dv"][:, :, :, hs],
+              "dg": x["dg"][:, :, hs], "dbeta": x["dbeta"][:, :, :, hs], "dh0": x["dh0"][:, hs]}
+        compare(xs, r, False, f"gdp long head {h}")
+        del sl
