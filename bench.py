@@ -23,7 +23,8 @@ Seven legs, each timed over exactly K steps bracketed by torch.cuda.synchronize(
            and a 128-request decode step) and the gated RMS norm of its output;
            kernel times and achieved bandwidth.
   backward: the chunked backward (gradients of q, k, v, g, beta and the initial
-           state) at B=4, T=4096, H=16, D=128, bf16 inputs; one call = the forward
+           state) at B=4, T=4096, H=16, D=128, bf16 inputs, and of the gated delta
+           product (n_h = 2) at B=1, T=16384, H=32; one call = the forward
            recompute plus the backward kernels; tokens/s and the fraction of the
            fp32 matrix-core peak its dense contractions reach.
 Per-launch kernel durations come from HIP events on the launch stream.  The
@@ -350,29 +351,31 @@ def run_conv_norm_leg(wl2, steps, warmup):
     }
 
 
-def backward_flops_per_token(Hv, D, C=64):
+def backward_flops_per_token(Hv, D, C=64, n_h=1):
     """Dense-tile flops per token of the backward kernels (forward recompute excluded):
-    per chunk and value head, eleven C x C x D products (K K^T, Q K^T, T R; P^T dO,
-    T^T dD; dR D^T, dO D^T, dPs K, dAs K, dAs^T K, dPs^T Q) and seven C x D x D ones
-    (K H0; K dH, Q^T dO, K^T dR; dO H0^T, dR H0^T, D dH^T), 2 flops per multiply-add."""
-    return Hv * (22 * C * D + 14 * D * D)
+    per 64-row chunk and value head, eleven C x C x D products (K K^T, Q K^T, T R;
+    P^T dO, T^T dD; dR D^T, dO D^T, dPs K, dAs K, dAs^T K, dPs^T Q) and seven C x D x D
+    ones (K H0; K dH, Q^T dO, K^T dR; dO H0^T, dR H0^T, D dH^T), 2 flops per
+    multiply-add; n_h rows per token."""
+    return n_h * Hv * (22 * C * D + 14 * D * D)
 
 
-def run_backward_leg(steps, warmup):
+def run_backward_leg(steps, warmup, *, name="bwd_bf16_B4_T4096_H16_D128", B=4, T=4096, H=16,
+                     n_h=1):
     import torch
     import gated_delta_rule_71_amd as gdr
     from gated_delta_rule_71_amd import workloads as W
-    bw = W.backward_workload("bwd_bf16_B4_T4096_H16_D128", 1, Hk=16, Hv=16, D=128, dtype=W.BF16,
-                             B=4, T=4096, decay="config")
+    bw = W.backward_workload(name, 1, Hk=H, Hv=H, D=128, dtype=W.BF16, B=B, T=T, decay="config",
+                             num_householder=n_h)
     f = bw.fwd
     d = {n: up(getattr(f, n)) for n in ("q", "k", "v", "g", "beta")}
     do, dht, h0 = up(bw.do), up(bw.dht), up(f.initial_state)
     gdr.chunk_gated_delta_rule_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], do, dht=dht,
                                         initial_state=h0)
     B, T, Hk, D = f.q.shape
-    Hv = f.v.shape[2]
+    Hv = f.v.shape[-2]
     outs = [torch.empty(s, dtype=torch.float32, device="cuda")
-            for s in ((B, T, Hk, D), (B, T, Hk, D), (B, T, Hv, D), (B, T, Hv), (B, T, Hv),
+            for s in ((B, T, Hk, D), f.k.shape, f.v.shape, (B, T, Hv), f.beta.shape,
                       (B, Hv, D, D))]
     a = gdr.backward_args(d["q"], d["k"], d["v"], d["g"], d["beta"], do, dq=outs[0],
                           dk=outs[1], dv=outs[2], dg=outs[3], dbeta=outs[4], dh0=outs[5],
@@ -388,7 +391,7 @@ def run_backward_leg(steps, warmup):
 
     wall, kern = time_launches(launch, steps, warmup)
     tokens = B * T
-    F = backward_flops_per_token(Hv, D)
+    F = backward_flops_per_token(Hv, D, n_h=n_h)
     tf = F * tokens / (kern * 1e-3) / 1e12
     return {"workload": bw.fwd.name, "tokens": tokens, "call_ms": kern, "wall_ms": wall,
             "value": tokens / (kern * 1e-3), "unit": "tokens/s",
@@ -527,6 +530,11 @@ def main():
     if "backward" in legs:
         res["backward"] = run_backward_leg(max(2, args.steps // 4), min(args.warmup, 2))
         print(f"[bench] backward: {res['backward']['call_ms']:.3f} ms per call",
+              file=sys.stderr, flush=True)
+        res["backward"]["gated_delta_product"] = run_backward_leg(
+            2, 1, name="bwd_gdp2_bf16_B1_T16384_H32_D128", B=1, T=16384, H=32, n_h=2)
+        print(f"[bench] backward (product): "
+              f"{res['backward']['gated_delta_product']['call_ms']:.3f} ms per call",
               file=sys.stderr, flush=True)
 
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ------------
