@@ -144,7 +144,8 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            cu_seqlens=None, *, state_indices=None, out_dtype=None, out=None,
                            final_state=None, stream=None, A_log=None, dt_bias=None,
-                           boundary_states=None, boundary_interval=None, **kwargs):
+                           boundary_states=None, boundary_interval=None, workspace=None,
+                           segments=True, **kwargs):
     """Chunked prefill of the gated delta rule (packed or batched sequences).
 
     q [B,T,Hk,K]; k [B,T,Hk,K] or [B,T,n_h,Hk,K]; v [B,T,Hv,V] or [B,T,n_h,Hv,V]
@@ -158,6 +159,10 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     ``boundary_states`` float32 [E,Hv,K,V] with ``boundary_interval`` (tokens, a
     multiple of 64) receives each sequence's state after every whole multiple of
     the interval, sequences in order (E = boundary_count(lengths, interval)).
+    Long batched rows that leave compute units idle run in segments (three passes
+    of the chunked kernel and a state combine) when a workspace of
+    gdr_prefill_workspace_bytes is given; it is allocated here unless ``segments``
+    is False (then the single pass runs).
     Returns (o [B,T,Hv,V], final_state or None).
     """
     torch = _torch()
@@ -200,6 +205,13 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
                      state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias,
                      boundary_states=boundary_states, boundary_interval=boundary_interval)
+    # long batched rows may run in segments, with a workspace (single pass without)
+    need = int(lib.gdr_prefill_workspace_bytes(a))
+    if workspace is None and need > 0 and segments:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check(workspace, "workspace", dtype=torch.uint8, ndim=1)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _raise(lib.gdr_chunk_gated_delta_rule(a, _stream(stream)), "gdr_chunk_gated_delta_rule")
     ret_state = final_state if (output_final_state or state_indices is not None) else None
     return out, ret_state

@@ -11,6 +11,9 @@
 
 namespace {
 
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(int32_t d) { return d == GDR_DTYPE_F32 || d == GDR_DTYPE_BF16; }
 bool head_ok(int32_t d) { return d == 64 || d == 128; }
@@ -80,7 +83,6 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
       (!aligned16(a->boundary_states) || a->boundary_interval <= 0 ||
        (int64_t{a->boundary_interval} * a->num_householder) % 64 != 0))
     return GDR_ERR_INVALID_ARG;
-  if (a->workspace_bytes < gdr_prefill_workspace_bytes(a)) return GDR_ERR_WORKSPACE;
   return GDR_OK;
 }
 
@@ -114,9 +116,61 @@ int gdr_validate_decode(const gdr_decode_args *a) {
   return GDR_OK;
 }
 
+// ---- long batched sequences in segments ------------------------------------------
+
+namespace {
+
+constexpr int kComputeUnits = 256;
+
+// Segment plan for a prefill: S > 1 segments per batch row when the batch rows alone
+// leave most compute units idle (fewer workgroups than compute units even with 32
+// value columns each) and the rows are long enough for S segments of >= 2048 tokens.
+struct SegPlan {
+  int S = 1, seg_len = 0;
+  size_t cu = 0, ident = 0, F = 0, A = 0, H_in = 0, total = 0;
+};
+
+SegPlan seg_plan(const gdr_prefill_args *a) {
+  SegPlan sp;
+  if (!a || a->cu_seqlens || a->state_indices || a->boundary_states || a->batch < 1 ||
+      a->num_v_heads < 1 || a->head_v < 32 || a->head_k < 1)
+    return sp;
+  const long pairs = static_cast<long>(a->batch) * a->num_v_heads;
+  if (pairs * (a->head_v / 32) >= kComputeUnits) return sp;
+  int S = 1;
+  while (2 * S * pairs <= kComputeUnits && a->seqlen / (2 * S) >= 2048) S *= 2;
+  if (S < 2) return sp;
+  sp.S = S;
+  sp.seg_len = ((a->seqlen + S - 1) / S + 63) / 64 * 64;
+  if (static_cast<long>(S - 1) * sp.seg_len >= a->seqlen) {   // last segment empty
+    sp.S = 1;
+    return sp;
+  }
+  const size_t nseq = static_cast<size_t>(a->batch) * S, Hv = a->num_v_heads;
+  const size_t kk = static_cast<size_t>(a->head_k) * a->head_k;
+  const size_t kv = static_cast<size_t>(a->head_k) * a->head_v;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes);
+    return at;
+  };
+  sp.cu = take((nseq + 1) * sizeof(int32_t));
+  sp.ident = take(nseq * Hv * kk * 4);
+  sp.A = take(nseq * Hv * kk * 4);
+  sp.F = take(nseq * Hv * kv * 4);
+  sp.H_in = take(nseq * Hv * kv * 4);
+  sp.total = off;
+  return sp;
+}
+
+}  // namespace
+
 size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *a) {
-  (void)a;  // the chunked prefill keeps every intermediate on chip
-  return 0;
+  // the single-pass chunked prefill keeps every intermediate on chip; long batched
+  // sequences that leave compute units idle may also run in segments, which needs
+  // the workspace below (optional: without it the single pass runs)
+  return seg_plan(a).total;
 }
 
 int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
@@ -153,8 +207,59 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.boundary_interval = a->boundary_interval;
   const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
   const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
-  const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder, state_waves,
-                                           static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const SegPlan sp = seg_plan(a);
+  const bool aligned = (reinterpret_cast<uintptr_t>(a->workspace) & (kAlign - 1)) == 0;
+  if (sp.S > 1 && a->workspace && aligned && a->workspace_bytes >= sp.total) {
+    // long rows in segments: the passes are prefills over the segments as packed
+    // sequences (see segments.hip)
+    char *ws = static_cast<char *>(a->workspace);
+    gdr::SegmentParams g{};
+    g.batch = a->batch;
+    g.seqlen = a->seqlen;
+    g.S = sp.S;
+    g.seg_len = sp.seg_len;
+    g.Hv = a->num_v_heads;
+    g.DK = a->head_k;
+    g.DV = a->head_v;
+    g.cu = reinterpret_cast<int32_t *>(ws + sp.cu);
+    g.ident = reinterpret_cast<float *>(ws + sp.ident);
+    g.F = reinterpret_cast<float *>(ws + sp.F);
+    g.A = reinterpret_cast<float *>(ws + sp.A);
+    g.initial_state = a->initial_state;
+    g.H_in = reinterpret_cast<float *>(ws + sp.H_in);
+    g.final_state = a->final_state;
+    const int nseq = a->batch * sp.S;
+    auto run = [&](gdr::PrefillParams q, int dv) {
+      q.cu_seqlens = g.cu;
+      q.seqlen = a->batch * a->seqlen;
+      q.num_seqs = nseq;
+      q.DV = dv;
+      const int ns = gdr::prefill_state_waves(dv, nseq, a->num_v_heads);
+      q.num_vtiles = dv / (32 * ns);
+      q.group_size = q.num_vtiles * (a->num_v_heads / a->num_qk_heads);
+      q.num_groups = nseq * a->num_qk_heads;
+      return gdr::launch_prefill(q, f32, a->head_k, rows, a->num_householder, ns, s);
+    };
+    if (gdr::launch_segment_setup(g, s) != hipSuccess) return GDR_ERR_HIP;
+    gdr::PrefillParams pf = p;          // 1: from zero, final states F, no outputs
+    pf.initial_state = nullptr;
+    pf.final_state = const_cast<float *>(g.F);
+    pf.out = nullptr;
+    if (run(pf, a->head_v) != hipSuccess) return GDR_ERR_HIP;
+    gdr::PrefillParams pa = pf;         // 2: no values, from the identity: transitions
+    pa.v = nullptr;
+    pa.initial_state = g.ident;
+    pa.final_state = const_cast<float *>(g.A);
+    if (run(pa, a->head_k) != hipSuccess) return GDR_ERR_HIP;
+    if (gdr::launch_segment_combine(g, s) != hipSuccess) return GDR_ERR_HIP;   // 3
+    gdr::PrefillParams po = p;          // 4: from the entering states, outputs
+    po.initial_state = g.H_in;
+    po.final_state = nullptr;
+    return run(po, a->head_v) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+  }
+  const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder,
+                                           state_waves, s);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
@@ -191,9 +296,6 @@ int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {
 // ---- backward ------------------------------------------------------------------
 
 namespace {
-
-constexpr size_t kAlign = 256;
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up of the backward (byte offsets from the base, each aligned).
 struct BwdLayout {

@@ -9,14 +9,14 @@ namespace gdr {
 struct PrefillParams {
   const void *q;
   const void *k;
-  const void *v;
+  const void *v;                 // NULL: values read as zero
   const float *g;
   const float *beta;
   const int32_t *cu_seqlens;     // NULL: batched, sequence n = tokens [n*seqlen, (n+1)*seqlen)
   const int32_t *state_indices;  // NULL: dense states
   const float *initial_state;    // NULL: zeros
   float *final_state;            // NULL: not written
-  void *out;
+  void *out;                     // NULL: outputs not written
   int seqlen;
   int num_seqs;
   int Hk;
@@ -135,6 +135,28 @@ struct BackwardParams {
   long tokens;
   int nh;                        // Householder sub-steps per token (rows per token)
 };
+
+// Segments of long batched sequences (the prefill's workspace).  Segment s of batch
+// row b covers tokens [s * seg_len, min((s + 1) * seg_len, seqlen)) and is packed
+// sequence b * S + s of the internal passes.
+struct SegmentParams {
+  int batch;
+  int seqlen;
+  int S;                         // segments per batch row
+  int seg_len;                   // tokens per segment (a multiple of 64)
+  int Hv;
+  int DK;
+  int DV;
+  int32_t *cu;                   // [batch * S + 1]
+  float *ident;                  // [batch * S, Hv, DK, DK] identity states
+  const float *F;                // [batch * S, Hv, DK, DV] final states from zero
+  const float *A;                // [batch * S, Hv, DK, DK] transitions
+  const float *initial_state;    // [batch, Hv, DK, DV] or NULL
+  float *H_in;                   // [batch * S, Hv, DK, DV] entering states
+  float *final_state;            // [batch, Hv, DK, DV] or NULL
+};
+hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream);
+hipError_t launch_segment_combine(const SegmentParams &p, hipStream_t stream);
 
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k);

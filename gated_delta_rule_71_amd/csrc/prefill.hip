@@ -479,7 +479,8 @@ prefill_kernel(const PrefillParams p) {
   // uniform bases; every element offset below fits in 32 bits (checked on the host)
   const TIn *__restrict__ kb = static_cast<const TIn *>(p.k) + hk * DK;
   const TIn *__restrict__ qb = static_cast<const TIn *>(p.q) + hk * DK;
-  const TIn *__restrict__ vrow = static_cast<const TIn *>(p.v) + h * p.DV + vt * DVT;
+  const TIn *__restrict__ vrow =
+      p.v ? static_cast<const TIn *>(p.v) + h * p.DV + vt * DVT : nullptr;
   const float *__restrict__ gb = p.g + h;
   const float *__restrict__ bb = p.beta + h;
   // gate parameters of this value head when g and beta hold raw projections
@@ -488,7 +489,8 @@ prefill_kernel(const PrefillParams p) {
     gate_A = expf(p.A_log[h]);
     gate_dt = p.dt_bias[h];
   }
-  TOut *__restrict__ ob = static_cast<TOut *>(p.out) + h * p.DV + col0;   // + token, lane
+  TOut *__restrict__ ob =
+      p.out ? static_cast<TOut *>(p.out) + h * p.DV + col0 : nullptr;   // + token, lane
   const uint32_t kstride = p.Hk * DK;        // elements between key rows (and query rows)
   const uint32_t vstride = p.Hv * p.DV;      // elements between value / output rows
   const size_t state_stride = static_cast<size_t>(DK) * p.DV;
@@ -589,8 +591,13 @@ prefill_kernel(const PrefillParams p) {
       const int u = stid + j * ST;
       const int rp = u % (CR / 2), sg = min(u / (CR / 2), Tr::VSEG - 1);
       const int ra = min(c + 2 * rp, last), rb = min(c + 2 * rp + 1, last);
-      cr.v[j][0].load(vrow + (static_cast<uint32_t>(ra) * vstride + sg * 8));
-      cr.v[j][1].load(vrow + (static_cast<uint32_t>(rb) * vstride + sg * 8));
+      if (p.v) {
+        cr.v[j][0].load(vrow + (static_cast<uint32_t>(ra) * vstride + sg * 8));
+        cr.v[j][1].load(vrow + (static_cast<uint32_t>(rb) * vstride + sg * 8));
+      } else {   // no values: the state's own evolution (a transition operator)
+        cr.v[j][0].zero();
+        cr.v[j][1].zero();
+      }
     }
     if (pw == 3) {
       const int row = min(c + lane, last);
@@ -844,7 +851,7 @@ prefill_kernel(const PrefillParams p) {
           o1[i] = sx[mq] * xo[mq][1][i] + yo[mq][1][i];
         }
         const int tok = tq0 + 16 * mq + l16;
-        if (full || tok < t1) {
+        if (p.out && (full || tok < t1)) {
           TOut *o = ob + (static_cast<uint32_t>(tok) * vstride + 4 * g4);
           store4(o, o0);
           store4(o + 16, o1);

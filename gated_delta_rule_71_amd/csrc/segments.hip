@@ -1,0 +1,123 @@
+// Long batched sequences split into segments that run in parallel.
+//
+// The recurrence is linear in the state: a segment entering with state H_in (the
+// [K, V] matrix S^T) leaves with
+//     H_out = A H_in + F,
+// where F is what the segment leaves from a zero state and A (K x K) is the
+// segment's transition: the same recurrence run with zero values from the identity
+// (each step maps H to exp(g) (I - beta k k^T) H, applied to the left of the stored
+// [K, V] state).  So a sequence of S segments needs
+//   1. every segment from a zero state (F, no outputs),
+//   2. every segment with zero values from the identity (A, no outputs),
+//   3. the entering states H_in, one segment after another (this file: a K x K by
+//      K x V product per segment), and
+//   4. every segment from its true entering state, writing the outputs,
+// where 1, 2 and 4 are ordinary chunked prefills over the segments as packed
+// sequences.  The chain of dependent chunk steps per workgroup shortens by the
+// factor S at the cost of three passes instead of one; the host takes this path
+// only when the sequences alone leave most compute units idle.
+
+#include "common.hpp"
+#include "gdr_internal.hpp"
+
+namespace gdr {
+
+// cu_seqlens of the packed segments, and identity states [B*S, Hv, DK, DK]
+__global__ void segment_setup_kernel(const SegmentParams p, long n_ident) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nseq = p.batch * p.S;
+  if (i <= nseq) {
+    const int b = static_cast<int>(i / p.S), s = static_cast<int>(i % p.S);
+    p.cu[i] = i == nseq ? p.batch * p.seqlen : b * p.seqlen + min(s * p.seg_len, p.seqlen);
+  }
+  if (i < n_ident) {
+    const int e = static_cast<int>(i % (static_cast<long>(p.DK) * p.DK));
+    p.ident[i] = (e / p.DK == e % p.DK) ? 1.0f : 0.0f;
+  }
+}
+
+// One workgroup per (batch row, value head, 32 state columns): H starts from the
+// initial state (or zero); for each segment s, H_in[s] = H, then H <- A_s H + F_s;
+// the last H is the final state.  A_s is staged 32 columns at a time.
+template <int DK>
+__global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParams p) {
+  constexpr int LD = 33;
+  __shared__ float sH[DK * LD];
+  __shared__ float sA[DK * LD];
+  const int tid = threadIdx.x;
+  const int ntile = p.DV / 32;
+  const int vt = blockIdx.x % ntile;
+  const int h = (blockIdx.x / ntile) % p.Hv;
+  const int b = blockIdx.x / ntile / p.Hv;
+  const int c = tid & 31, kr = tid >> 5;   // column of the tile, first row (8 row groups)
+  constexpr int RPT = DK / 8;              // rows per thread: kr + 8 i
+  const size_t sv = static_cast<size_t>(DK) * p.DV, sa = static_cast<size_t>(DK) * DK;
+  float H[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int k = kr + 8 * i;
+    H[i] = p.initial_state
+               ? p.initial_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+                                 static_cast<size_t>(k) * p.DV + 32 * vt + c]
+               : 0.0f;
+  }
+  for (int s = 0; s < p.S; ++s) {
+    const size_t seq = static_cast<size_t>(b) * p.S + s;
+    float *hin = p.H_in + (seq * p.Hv + h) * sv + 32 * vt + c;
+    const float *F = p.F + (seq * p.Hv + h) * sv + 32 * vt + c;
+    const float *A = p.A + (seq * p.Hv + h) * sa;
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int k = kr + 8 * i;
+      hin[static_cast<size_t>(k) * p.DV] = H[i];
+      sH[k * LD + c] = H[i];
+      acc[i] = F[static_cast<size_t>(k) * p.DV];
+    }
+    for (int kb = 0; kb < DK; kb += 32) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int k = kr + 8 * i;
+        sA[k * LD + c] = A[static_cast<size_t>(k) * DK + kb + c];
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < 32; ++kk) {
+        const float hv = sH[(kb + kk) * LD + c];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) acc[i] = fmaf(sA[(kr + 8 * i) * LD + kk], hv, acc[i]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) H[i] = acc[i];
+  }
+  if (p.final_state) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      p.final_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+                    static_cast<size_t>(kr + 8 * i) * p.DV + 32 * vt + c] = H[i];
+  }
+}
+
+hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream) {
+  const long n_ident = static_cast<long>(p.batch) * p.S * p.Hv * p.DK * p.DK;
+  const long n = n_ident > p.batch * p.S + 1 ? n_ident : p.batch * p.S + 1;
+  hipLaunchKernelGGL(segment_setup_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p,
+                     n_ident);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_combine(const SegmentParams &p, hipStream_t stream) {
+  const dim3 grid(p.batch * p.Hv * (p.DV / 32));
+  if (p.DK == 64)
+    hipLaunchKernelGGL(segment_combine_kernel<64>, grid, dim3(256), 0, stream, p);
+  else if (p.DK == 128)
+    hipLaunchKernelGGL(segment_combine_kernel<128>, grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace gdr

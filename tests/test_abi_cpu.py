@@ -105,7 +105,32 @@ def _decode(**kw):
 def test_validate_prefill(lib, kw, code):
     a = _prefill(**kw)
     assert lib.gdr_validate_prefill(ctypes.byref(a)) == code
-    assert lib.gdr_prefill_workspace_bytes(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("kw,segments", [
+    ({}, 1),                                                  # short rows: one pass
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32), 8),
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=16,
+          num_householder=2), 8),
+    (dict(batch=1, num_seqs=1, seqlen=8192, num_v_heads=4, num_qk_heads=4), 4),
+    (dict(batch=4, num_seqs=4, seqlen=4096, num_v_heads=16, num_qk_heads=16), 1),  # full GPU
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
+          cu_seqlens=FAKE), 1),                               # packed: lengths on the device
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
+          boundary_states=FAKE, boundary_interval=64), 1),
+])
+def test_prefill_segment_workspace(lib, kw, segments):
+    """Long batched rows that leave compute units idle may run in segments; the
+    optional workspace holds, per segment and head, the identity and transition
+    (K x K) and the zero-start and entering states (K x V), all float32."""
+    a = _prefill(**kw)
+    need = lib.gdr_prefill_workspace_bytes(ctypes.byref(a))
+    if segments == 1:
+        assert need == 0
+    else:
+        nseq = a.batch * segments
+        floats = nseq * a.num_v_heads * (2 * a.head_k * a.head_k + 2 * a.head_k * a.head_v)
+        assert floats * 4 <= need <= floats * 4 + 5 * 256 + 4 * (nseq + 1)
 
 
 @pytest.mark.parametrize("kw,code", [
