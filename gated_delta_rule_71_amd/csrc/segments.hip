@@ -36,60 +36,72 @@ __global__ void segment_setup_kernel(const SegmentParams p, long n_ident) {
   }
 }
 
-// One workgroup per (batch row, value head, 32 state columns): H starts from the
+// One workgroup per (batch row, value head, 16 state columns): H starts from the
 // initial state (or zero); for each segment s, H_in[s] = H, then H <- A_s H + F_s;
-// the last H is the final state.  A_s is staged 32 columns at a time.
+// the last H is the final state.  The whole K x K transition of a segment sits in
+// LDS; the next segment's is fetched into registers (16-byte loads) while the
+// current product runs, so each segment exposes at most one load latency.
+constexpr int kCombineCols = 16;
+
 template <int DK>
 __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParams p) {
-  constexpr int LD = 33;
-  __shared__ float sH[DK * LD];
-  __shared__ float sA[DK * LD];
+  constexpr int TC = kCombineCols, LDA = DK + 1, LDH = TC + 1;
+  constexpr int RPT = DK * TC / 256;            // rows per thread: kr + (256 / TC) i
+  constexpr int RS = 256 / TC;
+  constexpr int A4 = DK * DK / 4 / 256;         // 16-byte pieces of A per thread
+  __shared__ float sA[DK * LDA];
+  __shared__ float sH[DK * LDH];
   const int tid = threadIdx.x;
-  const int ntile = p.DV / 32;
+  const int ntile = p.DV / TC;
   const int vt = blockIdx.x % ntile;
   const int h = (blockIdx.x / ntile) % p.Hv;
   const int b = blockIdx.x / ntile / p.Hv;
-  const int c = tid & 31, kr = tid >> 5;   // column of the tile, first row (8 row groups)
-  constexpr int RPT = DK / 8;              // rows per thread: kr + 8 i
+  const int c = tid % TC, kr = tid / TC;
   const size_t sv = static_cast<size_t>(DK) * p.DV, sa = static_cast<size_t>(DK) * DK;
   float H[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int k = kr + 8 * i;
+  for (int i = 0; i < RPT; ++i)
     H[i] = p.initial_state
                ? p.initial_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
-                                 static_cast<size_t>(k) * p.DV + 32 * vt + c]
+                                 static_cast<size_t>(kr + RS * i) * p.DV + TC * vt + c]
                : 0.0f;
-  }
+  float4 ra[A4];
+  auto fetchA = [&](const float *A) {
+#pragma unroll
+    for (int j = 0; j < A4; ++j) ra[j] = reinterpret_cast<const float4 *>(A)[tid + 256 * j];
+  };
+  fetchA(p.A + (static_cast<size_t>(b) * p.S * p.Hv + h) * sa);
   for (int s = 0; s < p.S; ++s) {
     const size_t seq = static_cast<size_t>(b) * p.S + s;
-    float *hin = p.H_in + (seq * p.Hv + h) * sv + 32 * vt + c;
-    const float *F = p.F + (seq * p.Hv + h) * sv + 32 * vt + c;
-    const float *A = p.A + (seq * p.Hv + h) * sa;
+    float *hin = p.H_in + (seq * p.Hv + h) * sv + TC * vt + c;
+    const float *F = p.F + (seq * p.Hv + h) * sv + TC * vt + c;
     float acc[RPT];
 #pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = F[static_cast<size_t>(kr + RS * i) * p.DV];
+    __syncthreads();   // the previous segment's product has read sA and sH
+#pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int k = kr + 8 * i;
+      const int k = kr + RS * i;
       hin[static_cast<size_t>(k) * p.DV] = H[i];
-      sH[k * LD + c] = H[i];
-      acc[i] = F[static_cast<size_t>(k) * p.DV];
+      sH[k * LDH + c] = H[i];
     }
-    for (int kb = 0; kb < DK; kb += 32) {
-      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int k = kr + 8 * i;
-        sA[k * LD + c] = A[static_cast<size_t>(k) * DK + kb + c];
-      }
-      __syncthreads();
-#pragma unroll 8
-      for (int kk = 0; kk < 32; ++kk) {
-        const float hv = sH[(kb + kk) * LD + c];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) acc[i] = fmaf(sA[(kr + 8 * i) * LD + kk], hv, acc[i]);
-      }
+    for (int j = 0; j < A4; ++j) {
+      const int e = 4 * (tid + 256 * j), r = e / DK, q = e % DK;
+      float *d = sA + r * LDA + q;
+      d[0] = ra[j].x;
+      d[1] = ra[j].y;
+      d[2] = ra[j].z;
+      d[3] = ra[j].w;
     }
     __syncthreads();
+    if (s + 1 < p.S) fetchA(p.A + ((seq + 1) * p.Hv + h) * sa);
+#pragma unroll 8
+    for (int kk = 0; kk < DK; ++kk) {
+      const float hv = sH[kk * LDH + c];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) acc[i] = fmaf(sA[(kr + RS * i) * LDA + kk], hv, acc[i]);
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) H[i] = acc[i];
   }
@@ -97,7 +109,7 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       p.final_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
-                    static_cast<size_t>(kr + 8 * i) * p.DV + 32 * vt + c] = H[i];
+                    static_cast<size_t>(kr + RS * i) * p.DV + TC * vt + c] = H[i];
   }
 }
 
@@ -110,7 +122,7 @@ hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_segment_combine(const SegmentParams &p, hipStream_t stream) {
-  const dim3 grid(p.batch * p.Hv * (p.DV / 32));
+  const dim3 grid(p.batch * p.Hv * (p.DV / kCombineCols));
   if (p.DK == 64)
     hipLaunchKernelGGL(segment_combine_kernel<64>, grid, dim3(256), 0, stream, p);
   else if (p.DK == 128)
