@@ -68,6 +68,8 @@ def parse():
                          "launches plus a device copy of known size (counter calibration)")
     ap.add_argument("--summarize-db", metavar="DB",
                     help="print a text summary of a rocprofv3 results database and exit")
+    ap.add_argument("--mfma-from", metavar="DB",
+                    help="matrix-core flops and utilisation per kernel from a counter pass")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="derive HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE "
                          "profile of --profile-run, write profiles/traffic.json and exit")
@@ -154,6 +156,40 @@ def traffic_from(fetch_db, write_db):
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(data, indent=1))
+
+
+def mfma_from(db):
+    """Matrix-core work per kernel from one counter pass (SQ_INSTS_VALU_MFMA_MOPS_F16,
+    SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE): flops =
+    MOPS x 512 (the counters count multiply or add operations / 512), achieved
+    TFLOP/s over the dispatch's traced duration, and the utilisation
+    sum(MFMA busy cycles) / (max(GUI active cycles) x 1024 SIMDs)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select dispatch_id, name, counter_name, sum(counter_value), max(counter_value) "
+        "from pmc_events group by dispatch_id, counter_name").fetchall()
+    per = {}
+    for d, name, cn, total, peak in rows:
+        per.setdefault(d, {"name": name})[cn] = peak if cn == "GRBM_GUI_ACTIVE" else total
+    dur = {}
+    tabs = {r[0] for r in con.execute("select name from sqlite_master")}
+    if "kernels" in tabs:
+        for d, t0, t1 in con.execute("select dispatch_id, start, end from kernels"):
+            dur[d] = (t1 - t0) * 1e-9
+    print("dispatch | kernel | MFMA flops (f16, f32) | duration us | TFLOP/s | MFMA busy %")
+    for d in sorted(per):
+        r = per[d]
+        f16 = r.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512
+        f32 = r.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512
+        if f16 + f32 == 0:
+            continue
+        busy, active = r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), r.get("GRBM_GUI_ACTIVE", 0.0)
+        util = 100.0 * busy / (active * 1024) if active else float("nan")
+        t = dur.get(d)
+        tf = (f16 + f32) / t / 1e12 if t else float("nan")
+        print(f"  {d} | {r['name'][:70]} | {f16:.4g}, {f32:.4g} | "
+              f"{t * 1e6 if t else float('nan'):.1f} | {tf:.1f} | {util:.1f}")
 
 
 def up(a):
@@ -439,6 +475,9 @@ def main():
         return
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.mfma_from:
+        mfma_from(args.mfma_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
