@@ -132,8 +132,8 @@ struct SegPlan {
 
 SegPlan seg_plan(const gdr_prefill_args *a) {
   SegPlan sp;
-  if (!a || a->cu_seqlens || a->state_indices || a->boundary_states || a->batch < 1 ||
-      a->num_v_heads < 1 || a->head_v < 32 || a->head_k < 1)
+  if (!a || a->cu_seqlens || a->state_indices || a->batch < 1 || a->num_v_heads < 1 ||
+      a->head_v < 32 || a->head_k < 1)
     return sp;
   const long pairs = static_cast<long>(a->batch) * a->num_v_heads;
   if (pairs * (a->head_v / 32) >= kComputeUnits) return sp;
@@ -143,6 +143,13 @@ SegPlan seg_plan(const gdr_prefill_args *a) {
   sp.S = S;
   sp.seg_len = ((a->seqlen + S - 1) / S + 63) / 64 * 64;
   if (static_cast<long>(S - 1) * sp.seg_len >= a->seqlen) {   // last segment empty
+    sp.S = 1;
+    return sp;
+  }
+  // boundary states (written by the last pass) keep their order when every
+  // segment but a row's last is a whole number of intervals
+  if (a->boundary_states &&
+      (a->boundary_interval <= 0 || sp.seg_len % a->boundary_interval != 0)) {
     sp.S = 1;
     return sp;
   }
@@ -246,6 +253,7 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
     pf.initial_state = nullptr;
     pf.final_state = const_cast<float *>(g.F);
     pf.out = nullptr;
+    pf.boundary_states = nullptr;       // boundary states come from the last pass
     if (run(pf, a->head_v) != hipSuccess) return GDR_ERR_HIP;
     gdr::PrefillParams pa = pf;         // 2: no values, from the identity: transitions
     pa.v = nullptr;
@@ -253,8 +261,8 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
     pa.final_state = const_cast<float *>(g.A);
     if (run(pa, a->head_k) != hipSuccess) return GDR_ERR_HIP;
     if (gdr::launch_segment_combine(g, s) != hipSuccess) return GDR_ERR_HIP;   // 3
-    gdr::PrefillParams po = p;          // 4: from the entering states, outputs
-    po.initial_state = g.H_in;
+    gdr::PrefillParams po = p;          // 4: from the entering states, outputs (and
+    po.initial_state = g.H_in;          //    boundary states)
     po.final_state = nullptr;
     return run(po, a->head_v) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
   }
@@ -299,9 +307,37 @@ namespace {
 
 // Workspace carve-up of the backward (byte offsets from the base, each aligned).
 struct BwdLayout {
-  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, qn, kn, gg, gb, total;
+  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, qn, kn, gg, gb, fwd, total;
+  size_t fwd_bytes;   // workspace of the forward recompute (long rows in segments)
   int max_chunks;
 };
+
+// the forward recompute's prefill arguments (boundary state every 64 rows); the
+// pointers are left NULL except a stand-in for boundary_states, as only the sizes
+// matter to the segment plan
+gdr_prefill_args bwd_forward_args(const gdr_backward_args *a) {
+  gdr_prefill_args f{};
+  f.batch = a->batch;
+  f.seqlen = a->seqlen;
+  f.num_seqs = a->num_seqs;
+  f.num_qk_heads = a->num_qk_heads;
+  f.num_v_heads = a->num_v_heads;
+  f.head_k = a->head_k;
+  f.head_v = a->head_v;
+  f.num_householder = a->num_householder;
+  f.chunk_size = 64 / (a->num_householder > 0 ? a->num_householder : 1);
+  f.qkv_dtype = a->qkv_dtype;
+  f.out_dtype = a->qkv_dtype;
+  f.use_qk_l2norm = a->use_qk_l2norm;
+  f.scale = a->scale;
+  f.cu_seqlens = a->cu_seqlens;
+  f.gate_mode = a->gate_mode;
+  f.A_log = a->A_log;
+  f.dt_bias = a->dt_bias;
+  f.boundary_states = reinterpret_cast<float *>(kAlign);   // stand-in, replaced at the call
+  f.boundary_interval = f.chunk_size;
+  return f;
+}
 
 BwdLayout bwd_layout(const gdr_backward_args *a) {
   BwdLayout L{};
@@ -340,6 +376,9 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   L.kn = take(a->use_qk_l2norm ? rows * Hk * D * 4 : 0);
   L.gg = take(a->gate_mode ? tokens * Hv * 4 : 0);
   L.gb = take(a->gate_mode ? rows * Hv * 4 : 0);
+  const gdr_prefill_args f = bwd_forward_args(a);
+  L.fwd_bytes = gdr_prefill_workspace_bytes(&f);
+  L.fwd = take(L.fwd_bytes);
   L.total = off;
   return L;
 }
@@ -469,34 +508,19 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
   if (gdr::launch_backward_table(p, s) != hipSuccess) return GDR_ERR_HIP;
   if (gdr::launch_backward_prologue(p, f32, a->head_k, s) != hipSuccess) return GDR_ERR_HIP;
   if (tokens > 0) {
-    // forward recompute: the state after every 64 tokens of each sequence
-    gdr_prefill_args f{};
-    f.batch = a->batch;
-    f.seqlen = a->seqlen;
-    f.num_seqs = a->num_seqs;
-    f.num_qk_heads = a->num_qk_heads;
-    f.num_v_heads = a->num_v_heads;
-    f.head_k = a->head_k;
-    f.head_v = a->head_v;
-    f.num_householder = a->num_householder;
-    f.chunk_size = 64 / a->num_householder;
-    f.qkv_dtype = a->qkv_dtype;
-    f.out_dtype = a->qkv_dtype;
-    f.use_qk_l2norm = a->use_qk_l2norm;
-    f.scale = a->scale;
-    f.gate_mode = a->gate_mode;
-    f.A_log = a->A_log;
-    f.dt_bias = a->dt_bias;
+    // forward recompute: the state after every 64 rows of each sequence (long
+    // batched rows run in segments with their workspace)
+    gdr_prefill_args f = bwd_forward_args(a);
     f.q = a->q;
     f.k = a->k;
     f.v = a->v;
     f.g = a->g;
     f.beta = a->beta;
-    f.cu_seqlens = a->cu_seqlens;
     f.initial_state = a->initial_state;
     f.out = ws + L.o;
     f.boundary_states = p.states;
-    f.boundary_interval = 64 / a->num_householder;   // every 64 rows
+    f.workspace = L.fwd_bytes ? ws + L.fwd : nullptr;
+    f.workspace_bytes = L.fwd_bytes;
     const int fs = gdr_chunk_gated_delta_rule(&f, stream);
     if (fs != GDR_OK) return fs;
   }

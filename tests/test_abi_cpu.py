@@ -116,8 +116,11 @@ def test_validate_prefill(lib, kw, code):
     (dict(batch=4, num_seqs=4, seqlen=4096, num_v_heads=16, num_qk_heads=16), 1),  # full GPU
     (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
           cu_seqlens=FAKE), 1),                               # packed: lengths on the device
+    # boundary states stay in order when they fall on segment ends (8192 tokens)
     (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
-          boundary_states=FAKE, boundary_interval=64), 1),
+          boundary_states=FAKE, boundary_interval=64), 8),
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
+          boundary_states=FAKE, boundary_interval=3072), 1),
 ])
 def test_prefill_segment_workspace(lib, kw, segments):
     """Long batched rows that leave compute units idle may run in segments; the

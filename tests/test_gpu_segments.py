@@ -82,3 +82,42 @@ def test_segments_deterministic():
                          initial_state="random")
     a, b = _run(wl, True), _run(wl, True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_segments_with_boundary_states():
+    """Boundary states (prefix caching) written by the last pass of the segment path,
+    in the order of the unsplit call, against the single pass and the oracle."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    import oracle
+    wl = W.prefill_dense("seg_bnd", 45, 2, 8192, 2, 2, 128, 128, W.BF16, 64, decay="slow",
+                         initial_state="random")
+    d = {n: to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")}
+    iv = 1024
+    res = {}
+    for seg in (True, False):
+        bs = torch.empty((2 * 8192 // iv, 2, 128, 128), dtype=torch.float32, device="cuda")
+        o, fs = gdr.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                           initial_state=to_dev(wl.initial_state),
+                                           output_final_state=True, segments=seg,
+                                           boundary_states=bs, boundary_interval=iv)
+        torch.cuda.synchronize()
+        res[seg] = (to_host(o), fs.cpu().numpy().astype(np.float64),
+                    bs.cpu().numpy().astype(np.float64))
+    assert _segments_used(wl)
+    # entry j of row b is the state after (j + 1) * iv tokens: the oracle's final state
+    # of that prefix
+    for b in range(2):
+        for j in (0, 3, 7):
+            L = (j + 1) * iv
+            _, ref = oracle.prefill(W.as_f64(wl.q[b:b + 1, :L]), W.as_f64(wl.k[b:b + 1, :L]),
+                                    W.as_f64(wl.v[b:b + 1, :L]), wl.g[b:b + 1, :L],
+                                    wl.beta[b:b + 1, :L],
+                                    initial_state=wl.initial_state[b:b + 1].astype(np.float64),
+                                    output_final_state=True)
+            for seg in (True, False):
+                check(res[seg][2][b * (8192 // iv) + j], ref[0], f32_inputs=False,
+                      out_bf16=False, what=f"boundary b={b} j={j} segments={seg}")
+    ro, rs = _oracle(wl)
+    check(res[True][0], ro, f32_inputs=False, out_bf16=True, what="segments outputs")
+    check(res[True][1], rs, f32_inputs=False, out_bf16=False, what="segments final states")
