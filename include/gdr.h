@@ -62,7 +62,7 @@ typedef enum {
   GDR_OK = 0,
   GDR_ERR_INVALID_ARG = 1, /* NULL where a pointer is required, bad size, misaligned */
   GDR_ERR_UNSUPPORTED = 2, /* valid but not implemented (head size, dtype, n_h, ...) */
-  GDR_ERR_WORKSPACE = 3,   /* workspace smaller than gdr_prefill_workspace_bytes()   */
+  GDR_ERR_WORKSPACE = 3,   /* workspace smaller than gdr_backward_workspace_bytes()  */
   GDR_ERR_HIP = 4          /* the HIP runtime reported a launch error                 */
 } gdr_status;
 
@@ -141,7 +141,7 @@ typedef struct {
   const float *initial_state;
   float *final_state;
   void *out;
-  void *workspace;          /* device memory of workspace_bytes (may be NULL if 0)  */
+  void *workspace;          /* optional device memory (segment path, below) or NULL */
   size_t workspace_bytes;
   int32_t gate_mode;        /* 0: g, beta are the gates; 1: raw projections (above) */
   const float *A_log;       /* [Hv] float32, gate_mode 1 only (else ignored)        */
@@ -363,7 +363,18 @@ const char *gdr_status_string(int status);
 int gdr_validate_prefill(const gdr_prefill_args *args);
 int gdr_validate_decode(const gdr_decode_args *args);
 
-/* Device workspace the prefill needs, in bytes (a host-only function of the sizes). */
+/*
+ * Optional device workspace of a prefill, in bytes (a host-only function of the
+ * sizes; 256-byte aligned memory owned by the caller, contents irrelevant).  It is
+ * nonzero only for long batched rows (no cu_seqlens, dense states) whose
+ * (sequence, value head) pairs leave compute units idle: given the workspace, such
+ * a call splits every row into S segments and runs three chunked passes over them
+ * (from zero, the transition from the identity with zero values, and from the true
+ * entering states, combined in between), which shortens the dependent chain S
+ * times.  Without it (NULL or smaller) the single pass runs; both give the same
+ * result up to rounding.  Boundary states are allowed on the segment path when
+ * boundary_interval divides the segment length (checked here: 0 otherwise).
+ */
 size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *args);
 
 /* Enqueue a prefill / a decode step on `stream` (hipStream_t). */
