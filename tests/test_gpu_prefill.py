@@ -237,24 +237,33 @@ def _sample_pairs(wl, per_seq, seed):
     return pairs
 
 
-def test_prefill_full_B4_T4096_H16():
-    wl = W.config1()
+# The measured workloads at full size, with the config decay and the two extra decay
+# variants (slow: g ~ -U(0, 0.05), long memory across chunks; zero: no decay).
+FULL_DECAYS = ["config", "slow", "zero"]
+
+
+@pytest.mark.parametrize("decay", FULL_DECAYS)
+def test_prefill_full_B4_T4096_H16(decay):
+    wl = W.config1(decay=decay)
     o, st, _ = gpu_prefill(wl)
-    _compare(wl, o, st, _sample_pairs(wl, 2, 1), out_bf16=True, what="B4 T4096 H16")
+    _compare(wl, o, st, _sample_pairs(wl, 2, 1), out_bf16=True, what=f"B4 T4096 H16 {decay}")
 
 
-def test_prefill_full_varlen_Hk16_Hv32():
-    wl = W.config2()
+@pytest.mark.parametrize("decay", FULL_DECAYS)
+def test_prefill_full_varlen_Hk16_Hv32(decay):
+    wl = W.config2(decay=decay)
     before = wl.initial_state.copy()
     o, st, _ = gpu_prefill(wl)
-    _compare(wl, o, st, _sample_pairs(wl, 2, 2), out_bf16=True, what="varlen 8 seqs")
+    _compare(wl, o, st, _sample_pairs(wl, 2, 2), out_bf16=True, what=f"varlen 8 seqs {decay}")
     written = [int(s) for s in wl.state_indices]
     untouched = np.setdiff1d(np.arange(before.shape[0]), written)
     after = st.cpu().numpy()
     assert np.array_equal(after[untouched].view(np.uint32), before[untouched].view(np.uint32))
 
 
-def test_prefill_full_product_T65536_H32():
-    wl = W.config4()
+@pytest.mark.parametrize("decay", FULL_DECAYS)
+def test_prefill_full_product_T65536_H32(decay):
+    """Runs in segments (the binding allocates the workspace)."""
+    wl = W.config4(decay=decay)
     o, st, _ = gpu_prefill(wl)
-    _compare(wl, o, st, [(0, 3), (0, 17)], out_bf16=True, what="gdp T65536 H32")
+    _compare(wl, o, st, [(0, 3), (0, 17)], out_bf16=True, what=f"gdp T65536 H32 {decay}")
