@@ -29,7 +29,7 @@
 //      chunk after the first) into the workspace;
 //   2. bwd_local_kernel, one workgroup per (chunk, value head): Gamma, A, P,
 //      T = (I + A)^-1 (by 16 x 16 blocks) and D = T R;
-//   3. bwd_sweep_kernel, one workgroup per (sequence, value head, 32 value
+//   3. bwd_sweep_kernel, one workgroup per (sequence, value head, 32 or 16 value
 //      columns), last chunk to first: dH_n of every chunk, dR, dV and dH0;
 //   4. bwd_grads_kernel, one workgroup per (chunk, value head): dQ, dK, dbeta, dg;
 //   5. with grouped heads (Hv > Hk), a sum of dQ, dK over each group.
@@ -45,6 +45,7 @@ namespace {
 
 constexpr int BC = 64;        // tokens per backward chunk
 constexpr int BT = 512;       // threads per workgroup (two waves per SIMD)
+constexpr int kCUs = 256;     // compute units
 constexpr int NW = BT / 64;   // waves per workgroup
 constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
 
@@ -399,15 +400,21 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
     for (int v = 0; v < 4; ++v) dm[wd.row(v, lane) * D + wd.col(t, lane)] = d[t][v];
 }
 
-// Per (sequence, value head, 32 value columns), last chunk to first, carrying
-// dH (D x 32 columns): store dH_n, then dD = P^T dO + diag(e^{G_n - G}) K dH,
+// Per (sequence, value head, CW value columns), last chunk to first, carrying
+// dH (D x CW columns): store dH_n, then dD = P^T dO + diag(e^{G_n - G}) K dH,
 // dR = T^T dD (kept for bwd_grads_kernel), dV = diag(beta) dR, and
 // dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
-template <typename TIn, typename TQK, int D>
+// (CW = 32, or 16 when 32-column workgroups would leave compute units idle: the
+// chain per workgroup stays the same, its products halve)
+template <typename TIn, typename TQK, int D, int CW>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = 33;
-  constexpr int TPH = (D / 16) * 2 / NW;   // D x 32 tiles per wave
-  constexpr int TPS = (BC / 16) * 2 / NW;  // 64 x 32 tiles per wave
+  constexpr int LDD = D + 1, LDV = CW + 1;
+  constexpr int TPH = (D / 16) * (CW / 16) / NW;   // D x CW tiles per wave
+  // 64 x CW tiles: one per wave, on the first NACT waves
+  constexpr int NACT = (BC / 16) * (CW / 16) < NW ? (BC / 16) * (CW / 16) : NW;
+  constexpr int TPS = (BC / 16) * (CW / 16) / NACT;
+  static_assert(TPH >= 1 && TPS >= 1, "column tile");
+  const bool sact = (threadIdx.x >> 6) < NACT;   // wave-uniform
   __shared__ float sK[BC * LDD];
   __shared__ float sQ[BC * LDD];
   __shared__ float sP[BC * LDC];
@@ -418,19 +425,19 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   __shared__ RowFactors rf;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NVT = D / 32;
+  constexpr int NVT = D / CW;
   const int vt = blockIdx.x % NVT;
   const int h = (blockIdx.x / NVT) % p.Hv;
   const int n = blockIdx.x / NVT / p.Hv;
-  const int col0 = 32 * vt;
+  const int col0 = CW * vt;
   const int hk = h / (p.Hv / p.Hk);
   int t0, t1;
   seq_span(p, n, t0, t1);
   const int nch = (t1 - t0 + BC - 1) / BC;
   const size_t ss = static_cast<size_t>(D) * D;
 
-  const WTile<32, TPH> wh(wave);
-  const WTile<32, TPS> ws(wave);
+  const WTile<CW, TPH> wh(wave);
+  const WTile<CW, TPS> ws(wave);
   f32x4 dh[TPH];
   zero(dh);
   if (p.d_final_state) {
@@ -444,7 +451,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   // the inputs of the chunk after next in the sweep are fetched into registers
   // while the current chunk's products run
   RowsRegs<TQK, D, D> fk, fq;
-  RowsRegs<TIn, D, 32> fo;
+  RowsRegs<TIn, D, CW> fo;
   MatRegs<BC, BC> fp, ft;
   auto fetch = [&](int jc) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
@@ -479,7 +486,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     __syncthreads();
 
     // dD = P^T dO + diag(e^{G_n - G}) (K dH)
-    {
+    if (sact) {
       f32x4 a1[TPS], a2[TPS];
       zero(a1);
       zero(a2);
@@ -497,22 +504,25 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     // dR = T^T dD
     f32x4 dr[TPS];
     zero(dr);
-    mmf(dr, ws, sT, 1, LDC, sD, LDV, 1, BC, lane);
+    if (sact) mmf(dr, ws, sT, 1, LDC, sD, LDV, 1, BC, lane);
     __syncthreads();
     {
       float *drm = p.drmat + cc * BC * D;
+      if (sact) {
 #pragma unroll
-      for (int t = 0; t < TPS; ++t)
+        for (int t = 0; t < TPS; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = ws.row(v, lane), q = ws.col(t, lane);
-          drm[r * D + col0 + q] = dr[t][v];
-          if (r < rows)
-            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] = rf.beta[r] * dr[t][v];
-          sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[t][v];
-        }
-      for (int idx = tid; idx < BC * 32; idx += BT) {
-        const int r = idx / 32, q = idx % 32;
+          for (int v = 0; v < 4; ++v) {
+            const int r = ws.row(v, lane), q = ws.col(t, lane);
+            drm[r * D + col0 + q] = dr[t][v];
+            if (r < rows)
+              p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
+                  rf.beta[r] * dr[t][v];
+            sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[t][v];
+          }
+      }
+      for (int idx = tid; idx < BC * CW; idx += BT) {
+        const int r = idx / CW, q = idx % CW;
         sO[r * LDV + q] *= p.scale * rf.eG[r];
       }
     }
@@ -929,9 +939,18 @@ hipError_t launch_bwd_qk(const BackwardParams &p, int max_chunks, hipStream_t s)
   if (max_chunks > 0)
     hipLaunchKernelGGL((bwd_local_kernel<TIn, TQK, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s,
                        p);
-  // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0
-  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D>), dim3(p.num_seqs * p.Hv * (D / 32)),
-                     dim3(BT), 0, s, p);
+  // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0;
+  // 16-column tiles when 32-column ones leave compute units idle
+  bool narrow = false;
+  if constexpr (D == 128) {
+    narrow = static_cast<long>(p.num_seqs) * p.Hv * (D / 32) < kCUs;
+    if (narrow)
+      hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 16>),
+                         dim3(p.num_seqs * p.Hv * (D / 16)), dim3(BT), 0, s, p);
+  }
+  if (!narrow)
+    hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 32>), dim3(p.num_seqs * p.Hv * (D / 32)),
+                       dim3(BT), 0, s, p);
   if (max_chunks > 0)
     hipLaunchKernelGGL((bwd_grads_kernel<TIn, TQK, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s,
                        p);
