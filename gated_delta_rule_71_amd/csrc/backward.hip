@@ -47,7 +47,21 @@ constexpr int BC = 64;        // tokens per backward chunk
 constexpr int BT = 512;       // threads per workgroup (two waves per SIMD)
 constexpr int kCUs = 256;     // compute units
 constexpr int NW = BT / 64;   // waves per workgroup
-constexpr int LDC = BC + 1;   // leading dimension of 64 x 64 tiles in LDS
+constexpr int LDC = BC + 1;   // 64 x 64 tiles read one row or one column per thread
+
+// LDS row strides (floats) for matrix-core operands, against the 64 four-byte LDS
+// banks.  An operand read in mmf has 16 lanes along one index of the matrix and 4
+// along the other.  With the 16 lanes on 16 rows (4 along a row) the read is
+// conflict-free at a stride of 4 x odd (mod 64); with the 16 lanes along a row (4
+// rows) at 16 x odd (mod 64); a matrix read both ways takes 17 (mod 64), where only
+// 3 lane pairs share a bank.  (A stride of n + 1 makes such reads up to 4-way.)
+constexpr int ld_up(int n, int m, int r) { return n + ((r - n) % m + m) % m; }
+constexpr int ld_row_read(int n) { return ld_up(n, 8, 4); }
+constexpr int ld_col_read(int n) { return ld_up(n, 32, 16); }
+constexpr int ld_any_read(int n) { return ld_up(n, 64, 17); }
+static_assert(ld_row_read(32) == 36 && ld_row_read(128) == 132 && ld_col_read(16) == 16 &&
+                  ld_col_read(32) == 48 && ld_col_read(64) == 80 && ld_any_read(128) == 145,
+              "LDS strides");
 
 // Wave-tiled fp32 matrix-core products.  An M x N output is cut into 16 x 16
 // tiles, numbered row by row; wave w owns the TPW consecutive tiles w*TPW ..
@@ -260,14 +274,18 @@ __global__ void bwd_table_kernel(const BackwardParams p) {
 // with A = diag(beta) Araw, and D = T R, R = diag(beta) (V - diag(e^G) K H0).
 template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1;
+  constexpr int LDK = ld_row_read(D);    // K: by rows
+  constexpr int LDQ = ld_any_read(D);    // Q by rows, R by columns
+  constexpr int LDA = ld_row_read(BC);   // A: by rows
+  constexpr int LDT = ld_row_read(BC);   // T: by rows (by columns only in the block steps)
+  constexpr int LDH = ld_col_read(D);    // H0: by columns
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
   constexpr int TPD = (BC / 16) * (D / 16) / NW;    // 64 x D tiles per wave
-  __shared__ float sK[BC * LDD];
-  __shared__ float sQ[BC * LDD];    // later V, then R
-  __shared__ float sA[BC * LDC];
-  __shared__ float sT[BC * LDC];
-  __shared__ float sH[32 * LDD];    // 32 rows of H0 at a time; also the solve's 16 x 16 blocks
+  __shared__ float sK[BC * LDK];
+  __shared__ float sQ[BC * LDQ];    // later V, then R
+  __shared__ float sA[BC * LDA];
+  __shared__ float sT[BC * LDT];
+  __shared__ float sH[32 * LDH];    // 32 rows of H0 at a time; also the solve's 16 x 16 blocks
   __shared__ RowFactors rf;
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -280,8 +298,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
   const int hk = h / (p.Hv / p.Hk);
 
-  load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
+  load_rows<TQK, D, D>(sK, LDK, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  load_rows<TQK, D, D>(sQ, LDQ, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
                        p.nh);
   row_factors(rf, p, h, ts, rows, tid);
   __syncthreads();
@@ -292,8 +310,8 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
     f32x4 kk[TPC], qk[TPC];
     zero(kk);
     zero(qk);
-    mmf(kk, w, sK, LDD, 1, sK, 1, LDD, D, lane);
-    mmf(qk, w, sQ, LDD, 1, sK, 1, LDD, D, lane);
+    mmf(kk, w, sK, LDK, 1, sK, 1, LDK, D, lane);
+    mmf(qk, w, sQ, LDQ, 1, sK, 1, LDK, D, lane);
     float *araw = p.araw + cc * BC * BC;
     float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
@@ -306,7 +324,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
         const float a = q < r ? kk[t][v] * gam : 0.0f;
         araw[r * BC + q] = a;
         pm[r * BC + q] = q <= r ? p.scale * qk[t][v] * gam : 0.0f;
-        sA[r * LDC + q] = rf.beta[r] * a;
+        sA[r * LDA + q] = rf.beta[r] * a;
       }
   }
   __syncthreads();
@@ -317,7 +335,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   //   off-diagonal blocks, block row by block row: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
   //   (16 x 16 matrix-core products, wave j takes block column j).
   {
-    for (int idx = tid; idx < BC * BC; idx += BT) sT[(idx / BC) * LDC + idx % BC] = 0.0f;
+    for (int idx = tid; idx < BC * BC; idx += BT) sT[(idx / BC) * LDT + idx % BC] = 0.0f;
     __syncthreads();
     if (wave < BC / 16 && lane < 16) {
       const int b = 16 * wave, jc = lane;
@@ -326,11 +344,11 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
       for (int r = 0; r < 16; ++r) {
         float x = r == jc ? 1.0f : 0.0f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) x = fmaf(-sA[(b + r) * LDC + b + i], t[i], x);
+        for (int i = 0; i < r; ++i) x = fmaf(-sA[(b + r) * LDA + b + i], t[i], x);
         t[r] = x;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sT[(b + r) * LDC + b + jc] = t[r];
+      for (int r = 0; r < 16; ++r) sT[(b + r) * LDT + b + jc] = t[r];
     }
     __syncthreads();
     constexpr int LDM = 17;
@@ -342,7 +360,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
         f32x4 m[1];
         zero(m);
         for (int k = jb; k < i; ++k)
-          mmf(m, w0, sA + (16 * i) * LDC + 16 * k, LDC, 1, sT + (16 * k) * LDC + 16 * jb, LDC, 1,
+          mmf(m, w0, sA + (16 * i) * LDA + 16 * k, LDA, 1, sT + (16 * k) * LDT + 16 * jb, LDT, 1,
               16, lane);
 #pragma unroll
         for (int v = 0; v < 4; ++v) sM[jb * 16 * LDM + w0.row(v, lane) * LDM + w0.col(0, lane)] = m[0][v];
@@ -352,15 +370,15 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
         const int jb = wave;
         f32x4 m[1];
         zero(m);
-        mmf(m, w0, sT + (16 * i) * LDC + 16 * i, LDC, 1, sM + jb * 16 * LDM, LDM, 1, 16, lane);
+        mmf(m, w0, sT + (16 * i) * LDT + 16 * i, LDT, 1, sM + jb * 16 * LDM, LDM, 1, 16, lane);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          sT[(16 * i + w0.row(v, lane)) * LDC + 16 * jb + w0.col(0, lane)] = -m[0][v];
+          sT[(16 * i + w0.row(v, lane)) * LDT + 16 * jb + w0.col(0, lane)] = -m[0][v];
       }
       __syncthreads();
     }
     float *tm = p.tmat + cc * BC * BC;
-    for (int idx = tid; idx < BC * BC; idx += BT) tm[idx] = sT[(idx / BC) * LDC + idx % BC];
+    for (int idx = tid; idx < BC * BC; idx += BT) tm[idx] = sT[(idx / BC) * LDT + idx % BC];
   }
 
   // X = K H0, H0 streamed 32 rows at a time
@@ -371,28 +389,28 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   if (h0) {
     for (int kb = 0; kb < D; kb += 32) {
       __syncthreads();
-      load_mat<32, D>(sH, LDD, h0 + static_cast<size_t>(kb) * D, D, tid);
+      load_mat<32, D>(sH, LDH, h0 + static_cast<size_t>(kb) * D, D, tid);
       __syncthreads();
-      mmf(x, wd, sK + kb, LDD, 1, sH, LDD, 1, 32, lane);
+      mmf(x, wd, sK + kb, LDK, 1, sH, LDH, 1, 32, lane);
     }
   }
   // R = diag(beta) (V - diag(e^G) X) -> sQ (V is staged there first)
   __syncthreads();
-  load_rows<TIn, D, D>(sQ, LDD, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
+  load_rows<TIn, D, D>(sQ, LDQ, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TPD; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = wd.row(v, lane);
-      float &y = sQ[r * LDD + wd.col(t, lane)];
+      float &y = sQ[r * LDQ + wd.col(t, lane)];
       y = rf.beta[r] * (y - rf.eG[r] * x[t][v]);
     }
   __syncthreads();
   // D = T R
   f32x4 d[TPD];
   zero(d);
-  mmf(d, wd, sT, LDC, 1, sQ, LDD, 1, BC, lane);
+  mmf(d, wd, sT, LDT, 1, sQ, LDQ, 1, BC, lane);
   float *dm = p.dmat + cc * BC * D;
 #pragma unroll
   for (int t = 0; t < TPD; ++t)
@@ -408,20 +426,24 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 // chain per workgroup stays the same, its products halve)
 template <typename TIn, typename TQK, int D, int CW>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = CW + 1;
+  constexpr int LDK = ld_any_read(D);    // K: by rows (K dH) and by columns (K^T)
+  constexpr int LDQ = ld_col_read(D);    // Q: by columns
+  constexpr int LDP = ld_col_read(BC);   // P, T: by columns
+  constexpr int LDV = ld_col_read(CW);   // dO, dD: by columns
+  constexpr int LDH = ld_row_read(D);    // dH, stored transposed (CW x D): by rows
   constexpr int TPH = (D / 16) * (CW / 16) / NW;   // D x CW tiles per wave
   // 64 x CW tiles: one per wave, on the first NACT waves
   constexpr int NACT = (BC / 16) * (CW / 16) < NW ? (BC / 16) * (CW / 16) : NW;
   constexpr int TPS = (BC / 16) * (CW / 16) / NACT;
   static_assert(TPH >= 1 && TPS >= 1, "column tile");
   const bool sact = (threadIdx.x >> 6) < NACT;   // wave-uniform
-  __shared__ float sK[BC * LDD];
-  __shared__ float sQ[BC * LDD];
-  __shared__ float sP[BC * LDC];
-  __shared__ float sT[BC * LDC];
+  __shared__ float sK[BC * LDK];
+  __shared__ float sQ[BC * LDQ];
+  __shared__ float sP[BC * LDP];
+  __shared__ float sT[BC * LDP];
   __shared__ float sO[BC * LDV];    // dO columns, later diag(scale e^G) dO
   __shared__ float sD[BC * LDV];    // dD, later -diag(beta e^G) dR
-  __shared__ float sdH[D * LDV];
+  __shared__ float sdH[CW * LDH];   // dH^T
   __shared__ RowFactors rf;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -474,13 +496,13 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
       for (int v = 0; v < 4; ++v) {
         const int r = wh.row(v, lane), q = wh.col(t, lane);
         dhn[r * D + col0 + q] = dh[t][v];
-        sdH[r * LDV + q] = dh[t][v];
+        sdH[q * LDH + r] = dh[t][v];
       }
-    fk.store(sK, LDD, rows, tid);
-    fq.store(sQ, LDD, rows, tid, ts, p.nh);
+    fk.store(sK, LDK, rows, tid);
+    fq.store(sQ, LDQ, rows, tid, ts, p.nh);
     fo.store(sO, LDV, rows, tid, ts, p.nh);
-    fp.store(sP, LDC, tid);
-    ft.store(sT, LDC, tid);
+    fp.store(sP, LDP, tid);
+    ft.store(sT, LDP, tid);
     row_factors(rf, p, h, ts, rows, tid);
     if (jc > 0) fetch(jc - 1);
     __syncthreads();
@@ -490,8 +512,8 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
       f32x4 a1[TPS], a2[TPS];
       zero(a1);
       zero(a2);
-      mmf(a1, ws, sP, 1, LDC, sO, LDV, 1, BC, lane);
-      mmf(a2, ws, sK, LDD, 1, sdH, LDV, 1, D, lane);
+      mmf(a1, ws, sP, 1, LDP, sO, LDV, 1, BC, lane);
+      mmf(a2, ws, sK, LDK, 1, sdH, 1, LDH, D, lane);
 #pragma unroll
       for (int t = 0; t < TPS; ++t)
 #pragma unroll
@@ -504,7 +526,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     // dR = T^T dD
     f32x4 dr[TPS];
     zero(dr);
-    if (sact) mmf(dr, ws, sT, 1, LDC, sD, LDV, 1, BC, lane);
+    if (sact) mmf(dr, ws, sT, 1, LDP, sD, LDV, 1, BC, lane);
     __syncthreads();
     {
       float *drm = p.drmat + cc * BC * D;
@@ -532,8 +554,8 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
       const float en = rf.eG[BC - 1];
 #pragma unroll
       for (int t = 0; t < TPH; ++t) dh[t] *= en;
-      mmf(dh, wh, sQ, 1, LDD, sO, LDV, 1, BC, lane);
-      mmf(dh, wh, sK, 1, LDD, sD, LDV, 1, BC, lane);
+      mmf(dh, wh, sQ, 1, LDQ, sO, LDV, 1, BC, lane);
+      mmf(dh, wh, sK, 1, LDK, sD, LDV, 1, BC, lane);
     }
     __syncthreads();
   }
@@ -558,13 +580,15 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 //            plus e^{G_n} <dH_n, H0> + sum w on the last row; dg = reverse cumsum.
 template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
-  constexpr int LDD = D + 1, LDV = 33;
+  constexpr int LDV = ld_row_read(32);   // phase 1 slices: by rows
+  constexpr int LDG = ld_any_read(BC);   // dAs, dPs: by rows and by columns
+  constexpr int LDD = ld_col_read(D);    // K, Q: by columns
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
   constexpr int TPD = (BC / 16) * (D / 16) / NW;    // 64 x D tiles per wave
   constexpr int HALVES = NW / (BC / 16);            // waves sharing one tile row of 64 x D
   // phase 1 and phases 2-3 share one LDS arena
   constexpr int P1 = 4 * BC * LDV + 2 * D * LDV;
-  constexpr int P23 = 4 * BC * LDC + 2 * BC * LDD;
+  constexpr int P23 = 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
   constexpr int ARENA = P1 > P23 ? P1 : P23;
   __shared__ float arena[ARENA];
   __shared__ RowFactors rf;
@@ -642,7 +666,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   }
   __syncthreads();
 
-  float *sdAs = arena, *sdPs = sdAs + BC * LDC, *sM1 = sdPs + BC * LDC, *sM2 = sM1 + BC * LDC;
+  float *sdAs = arena, *sdPs = sdAs + BC * LDG, *sM1 = sdPs + BC * LDG, *sM2 = sM1 + BC * LDC;
   float *sK = sM2 + BC * LDC, *sQ = sK + BC * LDD;
   {
     const float *araw = p.araw + cc * BC * BC;
@@ -656,8 +680,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         const float a = q < r ? -dA[t][v] : 0.0f;
         const float pp = q <= r ? dP[t][v] : 0.0f;
         const float ar = araw[r * BC + q];
-        sdAs[r * LDC + q] = a * rf.beta[r] * gam;
-        sdPs[r * LDC + q] = p.scale * pp * gam;
+        sdAs[r * LDG + q] = a * rf.beta[r] * gam;
+        sdPs[r * LDG + q] = p.scale * pp * gam;
         sM1[r * LDC + q] = a * rf.beta[r] * ar + pp * pm[r * BC + q];
         sM2[r * LDC + q] = a * ar;
       }
@@ -717,7 +741,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   {
     f32x4 dq[TPD];
     zero(dq);
-    mmf(dq, wd, sdPs, LDC, 1, sK, LDD, 1, BC, lane);
+    mmf(dq, wd, sdPs, LDG, 1, sK, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
@@ -741,9 +765,9 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   {
     f32x4 dk[TPD];
     zero(dk);
-    mmf(dk, wd, sdAs, LDC, 1, sK, LDD, 1, BC, lane);
-    mmf(dk, wd, sdAs, 1, LDC, sK, LDD, 1, BC, lane);
-    mmf(dk, wd, sdPs, 1, LDC, sQ, LDD, 1, BC, lane);
+    mmf(dk, wd, sdAs, LDG, 1, sK, LDD, 1, BC, lane);
+    mmf(dk, wd, sdAs, 1, LDG, sK, LDD, 1, BC, lane);
+    mmf(dk, wd, sdPs, 1, LDG, sQ, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
