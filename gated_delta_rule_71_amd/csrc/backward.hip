@@ -138,13 +138,24 @@ struct RowFactors {
   double G[BC];
   float beta[BC], eG[BC], eGl[BC];
 };
-__device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams &p, int h, int ts,
-                                            int rows, int tid) {
+// g and beta of one chunk's rows in registers (thread r < 64 holds row r), so that
+// a sweep can fetch them one chunk ahead
+struct RowInputs {
+  float g, beta;
+  __device__ __forceinline__ void fetch(const BackwardParams &p, int h, int ts, int rows,
+                                        int tid) {
+    g = 0.0f;
+    beta = 0.0f;
+    if (tid < rows) {
+      const int row = ts + tid;
+      beta = p.beta[static_cast<size_t>(row) * p.Hv + h];
+      if (row % p.nh == 0) g = p.g[static_cast<size_t>(row / p.nh) * p.Hv + h];
+    }
+  }
+};
+__device__ __forceinline__ void row_factors(RowFactors &rf, const RowInputs &ri, int tid) {
   if (tid < BC) {
-    const int row = ts + tid;
-    double x = (tid < rows && row % p.nh == 0)
-                   ? static_cast<double>(p.g[static_cast<size_t>(row / p.nh) * p.Hv + h])
-                   : 0.0;
+    double x = static_cast<double>(ri.g);
 #pragma unroll
     for (int o = 1; o < BC; o <<= 1) {
       const double y = __shfl_up(x, o, 64);
@@ -152,10 +163,16 @@ __device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams
     }
     const double last = __shfl(x, BC - 1, 64);
     rf.G[tid] = x;
-    rf.beta[tid] = tid < rows ? p.beta[static_cast<size_t>(ts + tid) * p.Hv + h] : 0.0f;
+    rf.beta[tid] = ri.beta;
     rf.eG[tid] = expf(static_cast<float>(x));
     rf.eGl[tid] = expf(static_cast<float>(last - x));
   }
+}
+__device__ __forceinline__ void row_factors(RowFactors &rf, const BackwardParams &p, int h, int ts,
+                                            int rows, int tid) {
+  RowInputs ri;
+  ri.fetch(p, h, ts, rows, tid);
+  row_factors(rf, ri, tid);
 }
 
 // Rows [0, 64) x NC columns (from col0) of a [tokens, heads, D] input (head `hd`),
@@ -475,9 +492,11 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   RowsRegs<TQK, D, D> fk, fq;
   RowsRegs<TIn, D, CW> fo;
   MatRegs<BC, BC> fp, ft;
+  RowInputs fr;
   auto fetch = [&](int jc) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
     const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
+    fr.fetch(p, h, ts, rows, tid);
     fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
     fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
     fo.fetch(dO, p.Hv, h, ts, rows, col0, tid, p.nh);
@@ -503,7 +522,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     fo.store(sO, LDV, rows, tid, ts, p.nh);
     fp.store(sP, LDP, tid);
     ft.store(sT, LDP, tid);
-    row_factors(rf, p, h, ts, rows, tid);
+    row_factors(rf, fr, tid);
     if (jc > 0) fetch(jc - 1);
     __syncthreads();
 
