@@ -315,10 +315,23 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
   const int hk = h / (p.Hv / p.Hk);
 
-  load_rows<TQK, D, D>(sK, LDK, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TQK, D, D>(sQ, LDQ, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
-                       p.nh);
-  row_factors(rf, p, h, ts, rows, tid);
+  // every global input is fetched into registers up front: K, Q, g, beta first
+  // (needed at once), then H0 and V, whose loads run under the K K^T products and
+  // the inverse
+  RowsRegs<TQK, D, D> fk, fq;
+  RowInputs fr;
+  fr.fetch(p, h, ts, rows, tid);
+  fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+  const float *h0 = entry_state(p, n, j, h, D);
+  MatRegs<32, D> fh[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) fh[b].fetch(h0 ? h0 + static_cast<size_t>(32 * b) * D : nullptr, D, tid);
+  RowsRegs<TIn, D, D> fv;
+  fv.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
+  fk.store(sK, LDK, rows, tid);
+  fq.store(sQ, LDQ, rows, tid, ts, p.nh);
+  row_factors(rf, fr, tid);
   __syncthreads();
 
   const size_t cc = static_cast<size_t>(c) * p.Hv + h;
@@ -402,18 +415,18 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   const WTile<D, TPD> wd(wave);
   f32x4 x[TPD];
   zero(x);
-  const float *h0 = entry_state(p, n, j, h, D);
   if (h0) {
-    for (int kb = 0; kb < D; kb += 32) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
       __syncthreads();
-      load_mat<32, D>(sH, LDH, h0 + static_cast<size_t>(kb) * D, D, tid);
+      fh[b].store(sH, LDH, tid);
       __syncthreads();
-      mmf(x, wd, sK + kb, LDK, 1, sH, LDH, 1, 32, lane);
+      mmf(x, wd, sK + 32 * b, LDK, 1, sH, LDH, 1, 32, lane);
     }
   }
   // R = diag(beta) (V - diag(e^G) X) -> sQ (V is staged there first)
   __syncthreads();
-  load_rows<TIn, D, D>(sQ, LDQ, static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
+  fv.store(sQ, LDQ, rows, tid);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TPD; ++t)
@@ -643,6 +656,12 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   zero(Ua);
   zero(Ub);
   float hh = 0.0f, rv = 0.0f;
+  // phase 2's inputs (K, Q rows and the chunk's Araw, P entries of this thread's
+  // tiles) are fetched during the last slice of phase 1; fp32 K, Q rows at D = 128
+  // would not fit the registers and are loaded when needed
+  constexpr bool kPreKQ = sizeof(TQK) == 2 || D <= 64;
+  RowsRegs<TQK, D, D> fk, fq;
+  float ar[TPC][4], pv[TPC][4];
   {
     float *sDb = arena, *sRb = sDb + BC * LDV, *sOb = sRb + BC * LDV, *svb = sOb + BC * LDV;
     float *sHb = svb + BC * LDV, *sGb = sHb + D * LDV;
@@ -667,7 +686,24 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       fV.store(svb, LDV, rows, tid);
       fH.store(sHb, LDV, tid);
       fG.store(sGb, LDV, tid);
-      if (vb + 32 < D) fetch(vb + 32);
+      if (vb + 32 < D) {
+        fetch(vb + 32);
+      } else {
+        if constexpr (kPreKQ) {
+          fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+          fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+        }
+        const float *araw = p.araw + cc * BC * BC;
+        const float *pm = p.pmat + cc * BC * BC;
+#pragma unroll
+        for (int t = 0; t < TPC; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = wc.row(v, lane), q = wc.col(t, lane);
+            ar[t][v] = araw[r * BC + q];
+            pv[t][v] = pm[r * BC + q];
+          }
+      }
       __syncthreads();
       // <dH_n, H0> over this slice (each thread its share of the elements)
       for (int idx = tid; idx < D * 32; idx += BT) {
@@ -687,27 +723,27 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 
   float *sdAs = arena, *sdPs = sdAs + BC * LDG, *sM1 = sdPs + BC * LDG, *sM2 = sM1 + BC * LDC;
   float *sK = sM2 + BC * LDC, *sQ = sK + BC * LDD;
-  {
-    const float *araw = p.araw + cc * BC * BC;
-    const float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
-    for (int t = 0; t < TPC; ++t)
+  for (int t = 0; t < TPC; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = wc.row(v, lane), q = wc.col(t, lane);
-        const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
-        const float a = q < r ? -dA[t][v] : 0.0f;
-        const float pp = q <= r ? dP[t][v] : 0.0f;
-        const float ar = araw[r * BC + q];
-        sdAs[r * LDG + q] = a * rf.beta[r] * gam;
-        sdPs[r * LDG + q] = p.scale * pp * gam;
-        sM1[r * LDC + q] = a * rf.beta[r] * ar + pp * pm[r * BC + q];
-        sM2[r * LDC + q] = a * ar;
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int r = wc.row(v, lane), q = wc.col(t, lane);
+      const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
+      const float a = q < r ? -dA[t][v] : 0.0f;
+      const float pp = q <= r ? dP[t][v] : 0.0f;
+      sdAs[r * LDG + q] = a * rf.beta[r] * gam;
+      sdPs[r * LDG + q] = p.scale * pp * gam;
+      sM1[r * LDC + q] = a * rf.beta[r] * ar[t][v] + pp * pv[t][v];
+      sM2[r * LDC + q] = a * ar[t][v];
+    }
+  if constexpr (kPreKQ) {
+    fk.store(sK, LDD, rows, tid);
+    fq.store(sQ, LDD, rows, tid, ts, p.nh);
+  } else {
+    load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+    load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
+                         p.nh);
   }
-  load_rows<TQK, D, D>(sK, LDD, static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
-  load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
-                       p.nh);
   if (tid < BC) srv[tid] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
