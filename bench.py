@@ -112,6 +112,13 @@ def summarize_db(db):
                 "select name, total_calls, total_duration, average, percentage "
                 "from top_kernels order by total_duration desc"):
             print(f"  {name[:110]} | {calls} | {tot:.0f} | {avg:.1f} | {pct:.2f}")
+    if "kernels" in tabs and con.execute("select count(*) from kernels").fetchone()[0]:
+        # the same kernel on different workloads differs in its grid
+        print("by launch grid (us): name | grid (threads) | calls | average")
+        for name, gx, gy, calls, avg in con.execute(
+                "select name, grid_x, grid_y, count(*), avg(end - start) / 1000.0 from kernels "
+                "group by name, grid_x, grid_y order by sum(end - start) desc"):
+            print(f"  {name[:100]} | {gx}x{gy} | {calls} | {avg:.1f}")
     if "pmc_events" in tabs and con.execute("select count(*) from pmc_events").fetchone()[0]:
         print("counters per dispatch (summed over instances): dispatch | kernel | counter | value")
         rows = con.execute(
