@@ -70,6 +70,8 @@ def parse():
                     help="print a text summary of a rocprofv3 results database and exit")
     ap.add_argument("--mfma-from", metavar="DB",
                     help="matrix-core flops and utilisation per kernel from a counter pass")
+    ap.add_argument("--lds-from", metavar="DB",
+                    help="print LDS bank-conflict counters per kernel from a rocprofv3 database")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="derive HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE "
                          "profile of --profile-run, write profiles/traffic.json and exit")
@@ -197,6 +199,33 @@ def mfma_from(db):
         tf = (f16 + f32) / t / 1e12 if t else float("nan")
         print(f"  {d} | {r['name'][:70]} | {f16:.4g}, {f32:.4g} | "
               f"{t * 1e6 if t else float('nan'):.1f} | {tf:.1f} | {util:.1f}")
+
+
+def lds_from(db):
+    """LDS bank conflicts per kernel from one counter pass (SQ_LDS_BANK_CONFLICT,
+    SQ_LDS_IDX_ACTIVE, SQ_INSTS_LDS, GRBM_GUI_ACTIVE), dispatches of one kernel
+    summed: conflict cycles / LDS-active cycles, and per-dispatch means."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select dispatch_id, name, counter_name, sum(counter_value), max(counter_value) "
+        "from pmc_events group by dispatch_id, counter_name").fetchall()
+    per = {}
+    for d, name, cn, total, peak in rows:
+        per.setdefault(d, {"name": name})[cn] = peak if cn == "GRBM_GUI_ACTIVE" else total
+    agg = {}
+    for r in per.values():
+        a = agg.setdefault(r["name"][:90], [0, 0.0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        for i, cn in enumerate(("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+                                "GRBM_GUI_ACTIVE"), 1):
+            a[i] += r.get(cn, 0.0)
+    print("kernel | dispatches | conflict / LDS-active | LDS-active per dispatch | "
+          "LDS instructions per dispatch | GUI-active per dispatch")
+    for name, (n, conf, act, insts, gui) in sorted(agg.items(), key=lambda x: -x[1][2]):
+        if act:
+            print(f"  {name} | {n} | {conf / act:.3f} | {act / n:.3g} | {insts / n:.3g} | "
+                  f"{gui / n:.3g}")
 
 
 def up(a):
@@ -485,6 +514,9 @@ def main():
         return
     if args.mfma_from:
         mfma_from(args.mfma_from)
+        return
+    if args.lds_from:
+        lds_from(args.lds_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
