@@ -618,6 +618,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;   // 64 x 64 tiles per wave
   constexpr int TPD = (BC / 16) * (D / 16) / NW;    // 64 x D tiles per wave
   constexpr int HALVES = NW / (BC / 16);            // waves sharing one tile row of 64 x D
+  static_assert(BT == 8 * BC, "row sums and dots: eight threads per row");
   // phase 1 and phases 2-3 share one LDS arena
   constexpr int P1 = 4 * BC * LDV + 2 * D * LDV;
   constexpr int P23 = 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
@@ -715,10 +716,17 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       mmf(U1, wd, sOb, LDV, 1, sHb, 1, LDV, 32, lane);
       mmf(Ua, wd, sRb, LDV, 1, sHb, 1, LDV, 32, lane);
       mmf(Ub, wd, sDb, LDV, 1, sGb, 1, LDV, 32, lane);
-      if (tid < BC)
-        for (int q = 0; q < 32; ++q) rv = fmaf(sRb[tid * LDV + q], svb[tid * LDV + q], rv);
+      {
+        // dR . v of row tid / 8, this thread's 4 columns of the slice
+        const int r = tid >> 3, q0 = 4 * (tid & 7);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv = fmaf(sRb[r * LDV + q0 + e], svb[r * LDV + q0 + e], rv);
+      }
     }
   }
+  // the 8 partial row dots of a row sit in 8 consecutive lanes
+#pragma unroll
+  for (int o = 4; o > 0; o >>= 1) rv += __shfl_xor(rv, o, 64);
   __syncthreads();
 
   float *sdAs = arena, *sdPs = sdAs + BC * LDG, *sM1 = sdPs + BC * LDG, *sM2 = sM1 + BC * LDC;
@@ -744,7 +752,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     load_rows<TQK, D, D>(sQ, LDD, static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid,
                          p.nh);
   }
-  if (tid < BC) srv[tid] = rv;
+  if ((tid & 7) == 0) srv[tid >> 3] = rv;
   // <dH_n, H0>: wave sums, then across waves
   {
     float s = hh;
@@ -754,16 +762,28 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   }
   __syncthreads();
 
-  if (tid < BC) {
+  {
+    // row and column sums of E + F and row sums of dA * Araw: row (column) tid / 8,
+    // 8 of its entries per thread, then a sum over the 8 consecutive lanes
+    const int r = tid >> 3, q0 = 8 * (tid & 7);
     float rs = 0.0f, cs = 0.0f, r2 = 0.0f;
-    for (int q = 0; q < BC; ++q) {
-      rs += sM1[tid * LDC + q];
-      cs += sM1[q * LDC + tid];
-      r2 += sM2[tid * LDC + q];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      rs += sM1[r * LDC + q0 + e];
+      cs += sM1[(q0 + e) * LDC + r];
+      r2 += sM2[r * LDC + q0 + e];
     }
-    srow[0][tid] = rs;
-    srow[1][tid] = cs;
-    srow[2][tid] = r2;
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) {
+      rs += __shfl_xor(rs, o, 64);
+      cs += __shfl_xor(cs, o, 64);
+      r2 += __shfl_xor(r2, o, 64);
+    }
+    if ((tid & 7) == 0) {
+      srow[0][r] = rs;
+      srow[1][r] = cs;
+      srow[2][r] = r2;
+    }
   }
   // row dots of U1, Ua, Ub with the rows of Q and K: the 16 lanes of a lane group
   // hold one row's columns of a tile; the HALVES waves of a tile row add in LDS
