@@ -100,6 +100,51 @@ __device__ __forceinline__ void mmf(f32x4 (&acc)[TPW], const WTile<N, TPW> &w, c
   }
 }
 
+// Two or three products sharing the B operand, each B fragment read from LDS once:
+// acc1 += A1 B, acc2 += A2 B (, acc3 += A3 B); the accumulators may be one array
+template <int N, int TPW>
+__device__ __forceinline__ void mmf2(f32x4 (&acc1)[TPW], f32x4 (&acc2)[TPW],
+                                     const WTile<N, TPW> &w, const float *A1, int ars1, int acs1,
+                                     const float *A2, int ars2, int acs2, const float *B, int brs,
+                                     int bcs, int P, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const float *a1 = A1 + (w.r0 + i) * ars1 + g * acs1;
+  const float *a2 = A2 + (w.r0 + i) * ars2 + g * acs2;
+  const float *b = B + g * brs + (w.c0 + i) * bcs;
+#pragma unroll 4
+  for (int p = 0; p < P; p += 4) {
+    const float x1 = a1[p * acs1], x2 = a2[p * acs2];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float y = b[p * brs + 16 * t * bcs];
+      acc1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, y, acc1[t], 0, 0, 0);
+      acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, y, acc2[t], 0, 0, 0);
+    }
+  }
+}
+template <int N, int TPW>
+__device__ __forceinline__ void mmf3(f32x4 (&acc1)[TPW], f32x4 (&acc2)[TPW], f32x4 (&acc3)[TPW],
+                                     const WTile<N, TPW> &w, const float *A1, int ars1, int acs1,
+                                     const float *A2, int ars2, int acs2, const float *A3, int ars3,
+                                     int acs3, const float *B, int brs, int bcs, int P, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const float *a1 = A1 + (w.r0 + i) * ars1 + g * acs1;
+  const float *a2 = A2 + (w.r0 + i) * ars2 + g * acs2;
+  const float *a3 = A3 + (w.r0 + i) * ars3 + g * acs3;
+  const float *b = B + g * brs + (w.c0 + i) * bcs;
+#pragma unroll 4
+  for (int p = 0; p < P; p += 4) {
+    const float x1 = a1[p * acs1], x2 = a2[p * acs2], x3 = a3[p * acs3];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float y = b[p * brs + 16 * t * bcs];
+      acc1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, y, acc1[t], 0, 0, 0);
+      acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, y, acc2[t], 0, 0, 0);
+      acc3[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x3, y, acc3[t], 0, 0, 0);
+    }
+  }
+}
+
 template <int TPW>
 __device__ __forceinline__ void zero(f32x4 (&acc)[TPW]) {
 #pragma unroll
@@ -340,8 +385,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
     f32x4 kk[TPC], qk[TPC];
     zero(kk);
     zero(qk);
-    mmf(kk, w, sK, LDK, 1, sK, 1, LDK, D, lane);
-    mmf(qk, w, sQ, LDQ, 1, sK, 1, LDK, D, lane);
+    mmf2(kk, qk, w, sK, LDK, 1, sQ, LDQ, 1, sK, 1, LDK, D, lane);
     float *araw = p.araw + cc * BC * BC;
     float *pm = p.pmat + cc * BC * BC;
 #pragma unroll
@@ -711,10 +755,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         const int r = idx / 32, q = idx % 32;
         hh = fmaf(sHb[r * LDV + q], sGb[r * LDV + q], hh);
       }
-      mmf(dA, wc, sRb, LDV, 1, sDb, 1, LDV, 32, lane);
-      mmf(dP, wc, sOb, LDV, 1, sDb, 1, LDV, 32, lane);
-      mmf(U1, wd, sOb, LDV, 1, sHb, 1, LDV, 32, lane);
-      mmf(Ua, wd, sRb, LDV, 1, sHb, 1, LDV, 32, lane);
+      mmf2(dA, dP, wc, sRb, LDV, 1, sOb, LDV, 1, sDb, 1, LDV, 32, lane);
+      mmf2(U1, Ua, wd, sOb, LDV, 1, sRb, LDV, 1, sHb, 1, LDV, 32, lane);
       mmf(Ub, wd, sDb, LDV, 1, sGb, 1, LDV, 32, lane);
       {
         // dR . v of row tid / 8, this thread's 4 columns of the slice
@@ -812,11 +854,14 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     }
   }
 
-  // dQ = dPs K + diag(scale e^G) U1
+  // dQ = dPs K + diag(scale e^G) U1,
+  // dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub
+  f32x4 dq[TPD], dk[TPD];
+  zero(dq);
+  zero(dk);
+  mmf3(dq, dk, dk, wd, sdPs, LDG, 1, sdAs, LDG, 1, sdAs, 1, LDG, sK, LDD, 1, BC, lane);
+  mmf(dk, wd, sdPs, 1, LDG, sQ, LDD, 1, BC, lane);
   {
-    f32x4 dq[TPD];
-    zero(dq);
-    mmf(dq, wd, sdPs, LDG, 1, sK, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
@@ -836,13 +881,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
               dq[t][v] + p.scale * rf.eG[r] * U1[t][v];
       }
   }
-  // dK = dAs K + dAs^T K + dPs^T Q - diag(beta e^G) Ua + diag(e^{G_n - G}) Ub
   {
-    f32x4 dk[TPD];
-    zero(dk);
-    mmf(dk, wd, sdAs, LDG, 1, sK, LDD, 1, BC, lane);
-    mmf(dk, wd, sdAs, 1, LDG, sK, LDD, 1, BC, lane);
-    mmf(dk, wd, sdPs, 1, LDG, sQ, LDD, 1, BC, lane);
     float *dst;
     size_t rs;
     if (p.Hk == p.Hv) {
