@@ -505,6 +505,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
   constexpr int LDP = ld_col_read(BC);   // P, T: by columns
   constexpr int LDV = ld_col_read(CW);   // dO, dD: by columns
   constexpr int LDH = ld_row_read(D);    // dH, stored transposed (CW x D): by rows
+  static_assert(LDV <= LDP, "-diag(beta e^G) dR reuses the LDS of P");
   constexpr int TPH = (D / 16) * (CW / 16) / NW;   // D x CW tiles per wave
   // 64 x CW tiles: one per wave, on the first NACT waves
   constexpr int NACT = (BC / 16) * (CW / 16) < NW ? (BC / 16) * (CW / 16) : NW;
@@ -599,30 +600,30 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
         }
     }
     __syncthreads();
-    // dR = T^T dD
-    f32x4 dr[TPS];
-    zero(dr);
-    if (sact) mmf(dr, ws, sT, 1, LDP, sD, LDV, 1, BC, lane);
-    __syncthreads();
-    {
+    // dR = T^T dD; then, in the same interval, dR is stored, dV = diag(beta) dR,
+    // -diag(beta e^G) dR goes to the LDS of P (read only by dD, which is done) and
+    // dO is scaled by diag(scale e^G) (dO is read next by the dH products)
+    float *sR = sP;
+    if (sact) {
+      f32x4 dr[TPS];
+      zero(dr);
+      mmf(dr, ws, sT, 1, LDP, sD, LDV, 1, BC, lane);
       float *drm = p.drmat + cc * BC * D;
-      if (sact) {
 #pragma unroll
-        for (int t = 0; t < TPS; ++t)
+      for (int t = 0; t < TPS; ++t)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = ws.row(v, lane), q = ws.col(t, lane);
-            drm[r * D + col0 + q] = dr[t][v];
-            if (r < rows)
-              p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
-                  rf.beta[r] * dr[t][v];
-            sD[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[t][v];
-          }
-      }
-      for (int idx = tid; idx < BC * CW; idx += BT) {
-        const int r = idx / CW, q = idx % CW;
-        sO[r * LDV + q] *= p.scale * rf.eG[r];
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int r = ws.row(v, lane), q = ws.col(t, lane);
+          drm[r * D + col0 + q] = dr[t][v];
+          if (r < rows)
+            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
+                rf.beta[r] * dr[t][v];
+          sR[r * LDV + q] = -rf.beta[r] * rf.eG[r] * dr[t][v];
+        }
+    }
+    for (int idx = tid; idx < BC * CW; idx += BT) {
+      const int r = idx / CW, q = idx % CW;
+      sO[r * LDV + q] *= p.scale * rf.eG[r];
     }
     __syncthreads();
     // dH <- e^{G_n} dH + Q^T (diag(scale e^G) dO) + K^T (-diag(beta e^G) dR)
@@ -631,7 +632,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 #pragma unroll
       for (int t = 0; t < TPH; ++t) dh[t] *= en;
       mmf(dh, wh, sQ, 1, LDQ, sO, LDV, 1, BC, lane);
-      mmf(dh, wh, sK, 1, LDK, sD, LDV, 1, BC, lane);
+      mmf(dh, wh, sK, 1, LDK, sR, LDV, 1, BC, lane);
     }
     __syncthreads();
   }
