@@ -523,9 +523,13 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NVT = D / CW;
-  const int vt = blockIdx.x % NVT;
-  const int h = (blockIdx.x / NVT) % p.Hv;
-  const int n = blockIdx.x / NVT / p.Hv;
+  // the NVT column tiles of one (sequence, head) read the same K, Q, P and T: they
+  // go to one XCD, whose L2 then serves the re-reads
+  const int item = xcd_work_item(blockIdx.x, NVT, p.num_seqs * p.Hv);
+  if (item < 0) return;
+  const int vt = item % NVT;
+  const int h = (item / NVT) % p.Hv;
+  const int n = item / NVT / p.Hv;
   const int col0 = CW * vt;
   const int hk = h / (p.Hv / p.Hk);
   int t0, t1;
@@ -1080,15 +1084,16 @@ hipError_t launch_bwd_qk(const BackwardParams &p, int max_chunks, hipStream_t s)
                        p);
   // every (sequence, head) runs the sweep: an empty sequence passes dH_T to dH0;
   // 16-column tiles when 32-column ones leave compute units idle
+  const int rounds = (p.num_seqs * p.Hv + 7) / 8;   // XCD rounds of (sequence, head) groups
   bool narrow = false;
   if constexpr (D == 128) {
     narrow = static_cast<long>(p.num_seqs) * p.Hv * (D / 32) < kCUs;
     if (narrow)
-      hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 16>),
-                         dim3(p.num_seqs * p.Hv * (D / 16)), dim3(BT), 0, s, p);
+      hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 16>), dim3(8 * (D / 16) * rounds),
+                         dim3(BT), 0, s, p);
   }
   if (!narrow)
-    hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 32>), dim3(p.num_seqs * p.Hv * (D / 32)),
+    hipLaunchKernelGGL((bwd_sweep_kernel<TIn, TQK, D, 32>), dim3(8 * (D / 32) * rounds),
                        dim3(BT), 0, s, p);
   if (max_chunks > 0)
     hipLaunchKernelGGL((bwd_grads_kernel<TIn, TQK, D>), dim3(max_chunks, p.Hv), dim3(BT), 0, s,
