@@ -82,67 +82,105 @@ struct WTile {
   __device__ __forceinline__ int col(int t, int lane) const { return c0 + 16 * t + (lane & 15); }
 };
 
-// acc[t] += A(rows of the tile row, p) B(p, columns of tile t) over p in [0, P),
-// A(r, p) = A[r * ars + p * acs], B(p, c) = B[p * brs + c * bcs] in LDS, P % 4 == 0
+// The products acc_j[t] += A_j(rows of the tile row, p) B(p, columns of tile t)
+// over p in [0, P), j < NA, sharing the B fragments (each read from LDS once), with
+// A_j(r, p) = A_j[r * ars_j + p * acs_j] and B(p, c) = B[p * brs + c * bcs] in LDS,
+// P % 16 == 0.  The operands are read in batches of four k-steps, each batch issued
+// before the matrix-core instructions of the previous one, so that the reads are in
+// flight while the previous batch multiplies (read and multiply one k-step at a time,
+// every instruction waited for its own LDS round trip).  mul(j, t, a, b) applies one
+// instruction to product j, tile t.
+constexpr int KB = 4;   // k-steps per batch
+template <int NA, int TPW>
+struct OperandBatch {
+  float a[KB][NA], b[KB][TPW];
+};
+template <int NA, int N, int TPW, typename Mul>
+__device__ __forceinline__ void mmf_batched(const WTile<N, TPW> &w, const float *const (&A)[NA],
+                                            const int (&ars)[NA], const int (&acs)[NA],
+                                            const float *B, int brs, int bcs, int P, int lane,
+                                            Mul mul) {
+  const int i = lane & 15, g = lane >> 4;
+  const float *a[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) a[j] = A[j] + (w.r0 + i) * ars[j] + g * acs[j];
+  const float *b = B + g * brs + (w.c0 + i) * bcs;
+  auto load = [&](OperandBatch<NA, TPW> &x, int p) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int q = p + 4 * u;
+#pragma unroll
+      for (int j = 0; j < NA; ++j) x.a[u][j] = a[j][q * acs[j]];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) x.b[u][t] = b[q * brs + 16 * t * bcs];
+    }
+  };
+  auto multiply = [&](const OperandBatch<NA, TPW> &x) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int j = 0; j < NA; ++j) mul(j, t, x.a[u][j], x.b[u][t]);
+  };
+  OperandBatch<NA, TPW> x0, x1;
+  load(x0, 0);
+#pragma unroll
+  for (int p = 0; p < P; p += 8 * KB) {
+    if (p + 4 * KB < P) load(x1, p + 4 * KB);
+    multiply(x0);
+    if (p + 4 * KB < P) {
+      if (p + 8 * KB < P) load(x0, p + 8 * KB);
+      multiply(x1);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A B (one product)
 template <int N, int TPW>
 __device__ __forceinline__ void mmf(f32x4 (&acc)[TPW], const WTile<N, TPW> &w, const float *A,
                                     int ars, int acs, const float *B, int brs, int bcs, int P,
                                     int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const float *a = A + (w.r0 + i) * ars + g * acs;
-  const float *b = B + g * brs + (w.c0 + i) * bcs;
-#pragma unroll 4
-  for (int p = 0; p < P; p += 4) {
-    const float av = a[p * acs];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[p * brs + 16 * t * bcs], acc[t], 0, 0, 0);
-  }
+  const float *const As[1] = {A};
+  const int r[1] = {ars}, c[1] = {acs};
+  mmf_batched<1>(w, As, r, c, B, brs, bcs, P, lane,
+                 [&](int, int t, float x, float y) { acc[t] = mfma4(x, y, acc[t]); });
 }
 
-// Two or three products sharing the B operand, each B fragment read from LDS once:
 // acc1 += A1 B, acc2 += A2 B (, acc3 += A3 B); the accumulators may be one array
 template <int N, int TPW>
 __device__ __forceinline__ void mmf2(f32x4 (&acc1)[TPW], f32x4 (&acc2)[TPW],
                                      const WTile<N, TPW> &w, const float *A1, int ars1, int acs1,
                                      const float *A2, int ars2, int acs2, const float *B, int brs,
                                      int bcs, int P, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const float *a1 = A1 + (w.r0 + i) * ars1 + g * acs1;
-  const float *a2 = A2 + (w.r0 + i) * ars2 + g * acs2;
-  const float *b = B + g * brs + (w.c0 + i) * bcs;
-#pragma unroll 4
-  for (int p = 0; p < P; p += 4) {
-    const float x1 = a1[p * acs1], x2 = a2[p * acs2];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const float y = b[p * brs + 16 * t * bcs];
-      acc1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, y, acc1[t], 0, 0, 0);
-      acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, y, acc2[t], 0, 0, 0);
-    }
-  }
+  const float *const As[2] = {A1, A2};
+  const int r[2] = {ars1, ars2}, c[2] = {acs1, acs2};
+  mmf_batched<2>(w, As, r, c, B, brs, bcs, P, lane, [&](int j, int t, float x, float y) {
+    if (j == 0)
+      acc1[t] = mfma4(x, y, acc1[t]);
+    else
+      acc2[t] = mfma4(x, y, acc2[t]);
+  });
 }
 template <int N, int TPW>
 __device__ __forceinline__ void mmf3(f32x4 (&acc1)[TPW], f32x4 (&acc2)[TPW], f32x4 (&acc3)[TPW],
                                      const WTile<N, TPW> &w, const float *A1, int ars1, int acs1,
                                      const float *A2, int ars2, int acs2, const float *A3, int ars3,
                                      int acs3, const float *B, int brs, int bcs, int P, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const float *a1 = A1 + (w.r0 + i) * ars1 + g * acs1;
-  const float *a2 = A2 + (w.r0 + i) * ars2 + g * acs2;
-  const float *a3 = A3 + (w.r0 + i) * ars3 + g * acs3;
-  const float *b = B + g * brs + (w.c0 + i) * bcs;
-#pragma unroll 4
-  for (int p = 0; p < P; p += 4) {
-    const float x1 = a1[p * acs1], x2 = a2[p * acs2], x3 = a3[p * acs3];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const float y = b[p * brs + 16 * t * bcs];
-      acc1[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x1, y, acc1[t], 0, 0, 0);
-      acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x2, y, acc2[t], 0, 0, 0);
-      acc3[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x3, y, acc3[t], 0, 0, 0);
-    }
-  }
+  const float *const As[3] = {A1, A2, A3};
+  const int r[3] = {ars1, ars2, ars3}, c[3] = {acs1, acs2, acs3};
+  mmf_batched<3>(w, As, r, c, B, brs, bcs, P, lane, [&](int j, int t, float x, float y) {
+    if (j == 0)
+      acc1[t] = mfma4(x, y, acc1[t]);
+    else if (j == 1)
+      acc2[t] = mfma4(x, y, acc2[t]);
+    else
+      acc3[t] = mfma4(x, y, acc3[t]);
+  });
 }
 
 template <int TPW>
