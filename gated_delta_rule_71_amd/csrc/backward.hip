@@ -85,10 +85,11 @@ struct WTile {
 // The products acc_j[t] += A_j(rows of the tile row, p) B(p, columns of tile t)
 // over p in [0, P), j < NA, sharing the B fragments (each read from LDS once), with
 // A_j(r, p) = A_j[r * ars_j + p * acs_j] and B(p, c) = B[p * brs + c * bcs] in LDS,
-// P % 16 == 0.  The operands are read in batches of four k-steps, each batch issued
-// before the matrix-core instructions of the previous one, so that the reads are in
-// flight while the previous batch multiplies (read and multiply one k-step at a time,
-// every instruction waited for its own LDS round trip).  mul(j, t, a, b) applies one
+// P % 16 == 0 (every caller passes 16, 32, 64 or 128).  The operands are read in
+// batches of four k-steps, each batch issued before the matrix-core instructions of
+// the previous one, so that the reads are in flight while the previous batch
+// multiplies (reading and multiplying one k-step at a time would make every
+// instruction wait out its own LDS round trip).  mul(j, t, a, b) applies one
 // instruction to product j, tile t.
 constexpr int KB = 4;   // k-steps per batch
 template <int NA, int TPW>
