@@ -291,7 +291,13 @@ def prefill_bytes(wl, out_bytes_per_elem=2):
 
 
 def prefill_flops_per_token(wl, chunk_tokens):
-    """Dense-tile flops per token of the chunked form (measurement)."""
+    """Dense-tile flops per token of the chunked form with chunks of C tokens.
+
+    The delta rule: per q/k head the chunk's K K^T and Q K^T (2 C K each), per value
+    head W = T diag(beta e^G) K and U = T diag(beta) V (2 C K + 2 C V), the
+    intra-chunk P D (2 C V) and the state products K H, Q H and K^T D (2 K V each).
+    The product with n_h sub-steps per token runs the same steps on n_h C rows per
+    chunk, with queries on one row per token."""
     B, T, Hk, Hv, K, V = wl.shape
     n_h = wl.num_householder
     C = chunk_tokens
