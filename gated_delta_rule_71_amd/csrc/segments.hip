@@ -40,31 +40,44 @@ __global__ void segment_setup_kernel(const SegmentParams p, long n_ident) {
 // initial state (or zero); for each segment s, H_in[s] = H, then H <- A_s H + F_s;
 // the last H is the final state.  The whole K x K transition of a segment sits in
 // LDS; the next segment's is fetched into registers (16-byte loads) while the
-// current product runs, so each segment exposes at most one load latency.
+// current product runs, so each segment exposes at most one load latency.  The
+// product A_s H runs on the fp32 matrix cores (v_mfma_f32_16x16x4f32): each of the
+// four waves owns DK / 64 tiles of 16 rows x 16 columns of H in accumulator
+// layout (lane l: column l % 16, rows 4 (l / 16) + v).
 constexpr int kCombineCols = 16;
 
 template <int DK>
 __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParams p) {
-  constexpr int TC = kCombineCols, LDA = DK + 1, LDH = TC + 1;
-  constexpr int RPT = DK * TC / 256;            // rows per thread: kr + (256 / TC) i
-  constexpr int RS = 256 / TC;
+  constexpr int TC = kCombineCols;
+  // LDS strides against the 64 four-byte banks: A is read with 16 lanes on 16
+  // rows and 4 along a row (stride 4 mod 64 words), H with 16 lanes along a row
+  // and 4 rows (stride 16)
+  constexpr int LDA = DK + 4, LDH = TC;
+  constexpr int NT = DK / 64;                   // 16-row tiles per wave
   constexpr int A4 = DK * DK / 4 / 256;         // 16-byte pieces of A per thread
+  constexpr int KB = 4;                         // k-steps per batch of operand reads
+  static_assert(TC == 16 && NT >= 1, "combine tiling");
   __shared__ float sA[DK * LDA];
   __shared__ float sH[DK * LDH];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
   const int ntile = p.DV / TC;
   const int vt = blockIdx.x % ntile;
   const int h = (blockIdx.x / ntile) % p.Hv;
   const int b = blockIdx.x / ntile / p.Hv;
-  const int c = tid % TC, kr = tid / TC;
   const size_t sv = static_cast<size_t>(DK) * p.DV, sa = static_cast<size_t>(DK) * DK;
-  float H[RPT];
+  // row of this lane's element v of tile t
+  auto row = [&](int t, int v) { return 16 * (wave * NT + t) + 4 * g + v; };
+  const size_t col = static_cast<size_t>(TC) * vt + i;
+  f32x4 H[NT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    H[i] = p.initial_state
-               ? p.initial_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
-                                 static_cast<size_t>(kr + RS * i) * p.DV + TC * vt + c]
-               : 0.0f;
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      H[t][v] = p.initial_state
+                    ? p.initial_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+                                      static_cast<size_t>(row(t, v)) * p.DV + col]
+                    : 0.0f;
   float4 ra[A4];
   auto fetchA = [&](const float *A) {
 #pragma unroll
@@ -73,18 +86,21 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
   fetchA(p.A + (static_cast<size_t>(b) * p.S * p.Hv + h) * sa);
   for (int s = 0; s < p.S; ++s) {
     const size_t seq = static_cast<size_t>(b) * p.S + s;
-    float *hin = p.H_in + (seq * p.Hv + h) * sv + TC * vt + c;
-    const float *F = p.F + (seq * p.Hv + h) * sv + TC * vt + c;
-    float acc[RPT];
+    float *hin = p.H_in + (seq * p.Hv + h) * sv + col;
+    const float *F = p.F + (seq * p.Hv + h) * sv + col;
+    f32x4 acc[NT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) acc[i] = F[static_cast<size_t>(kr + RS * i) * p.DV];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[t][v] = F[static_cast<size_t>(row(t, v)) * p.DV];
     __syncthreads();   // the previous segment's product has read sA and sH
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int k = kr + RS * i;
-      hin[static_cast<size_t>(k) * p.DV] = H[i];
-      sH[k * LDH + c] = H[i];
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        hin[static_cast<size_t>(row(t, v)) * p.DV] = H[t][v];
+        sH[row(t, v) * LDH + i] = H[t][v];
+      }
 #pragma unroll
     for (int j = 0; j < A4; ++j) {
       const int e = 4 * (tid + 256 * j), r = e / DK, q = e % DK;
@@ -96,20 +112,34 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
     }
     __syncthreads();
     if (s + 1 < p.S) fetchA(p.A + ((seq + 1) * p.Hv + h) * sa);
-#pragma unroll 8
-    for (int kk = 0; kk < DK; ++kk) {
-      const float hv = sH[kk * LDH + c];
+    // acc += A_s H over k, the operands of KB k-steps read before their products
+    const float *a0 = sA + (16 * wave * NT + i) * LDA + g;
+    const float *b0 = sH + g * LDH + i;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) acc[i] = fmaf(sA[(kr + RS * i) * LDA + kk], hv, acc[i]);
+    for (int k = 0; k < DK; k += 4 * KB) {
+      float xa[KB][NT], xb[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        xb[u] = b0[(k + 4 * u) * LDH];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xa[u][t] = a0[16 * t * LDA + k + 4 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[u][t], xb[u], acc[t], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) H[i] = acc[i];
+    for (int t = 0; t < NT; ++t) H[t] = acc[t];
   }
   if (p.final_state) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      p.final_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
-                    static_cast<size_t>(kr + RS * i) * p.DV + TC * vt + c] = H[i];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        p.final_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+                      static_cast<size_t>(row(t, v)) * p.DV + col] = H[t][v];
   }
 }
 
