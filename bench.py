@@ -1,13 +1,17 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs prefill,decode,gdp,gates,boundary,conv_norm,backward]
+                    [--legs prefill,prefill_b4,decode,gdp,gates,boundary,conv_norm,backward]
 
-Seven legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Eight legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
            the headline `value`.
+  prefill_b4: the batched gated delta rule, B=4, T=4096, H=16, K = V = 128, bf16
+           q/k/v, fp32 g/beta, a random N(0, 0.1) initial state and the final
+           state written, chunk 64; tokens/s with its HBM and matrix-core
+           fractions.
   decode:  one token for each of 128 requests (16 padding) over a
            [256, 32, 128, 128] fp32 slot cache; reported as state GB/s.  The
            256 MB last-level cache is flushed (1 GiB read) before every launch,
@@ -57,7 +61,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,gdp,gates,boundary,conv_norm,backward")
+    ap.add_argument("--legs",
+                    default="prefill,prefill_b4,decode,gdp,gates,boundary,conv_norm,backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -556,6 +561,18 @@ def main():
         print(f"[bench] prefill: {wall:.3f} ms/step, kernel {kern:.3f} ms", file=sys.stderr,
               flush=True)
 
+    # ---- batched prefill, B = 4, T = 4096, H = 16 --------------------------------------
+    if "prefill_b4" in legs:
+        wl1 = W.config1()
+        wall, kern = run_prefill_leg(wl1, args.steps, args.warmup)
+        byt = prefill_bytes(wl1)
+        F = prefill_flops_per_token(wl1, wl1.chunk_size)
+        res["prefill_b4"] = dict(wall_ms=wall, kernel_ms=kern, tokens=wl1.tokens, bytes=byt,
+                                 flops=F * wl1.tokens, flops_per_token=F, workload=wl1.name)
+        print(f"[bench] prefill B4 T4096 H16: kernel {kern:.3f} ms", file=sys.stderr,
+              flush=True)
+        del wl1
+
     # ---- decode ------------------------------------------------------------------------
     if "decode" in legs:
         wl3 = W.config3()
@@ -698,19 +715,33 @@ def main():
                                        "traffic": stored_traffic("decode", "decode.hip")}}
         if "prefill" not in res:
             line.update(value=gbs, unit="GB/s", ms_per_step=dd["wall_ms"])
+    if "prefill_b4" in res:
+        pb = res["prefill_b4"]
+        gbs = pb["bytes"] / (pb["kernel_ms"] * 1e-3) / 1e9
+        tf = pb["flops"] / (pb["kernel_ms"] * 1e-3) / 1e12
+        line["prefill_b4"] = {
+            "workload": pb["workload"], "value": pb["tokens"] / (pb["wall_ms"] * 1e-3),
+            "unit": "tokens/s", "kernel_ms": pb["kernel_ms"], "tokens": pb["tokens"],
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": pb["bytes"]},
+            "mfma": {"flops_per_token": pb["flops_per_token"], "achieved_tflops": tf,
+                     "peak_tflops": MFMA_PEAK_TFLOPS, "frac": tf / MFMA_PEAK_TFLOPS}}
     if "gdp" in res:
         gg = res["gdp"]
         tps = gg["tokens"] / (gg["wall_ms"] * 1e-3)
         gbs = gg["bytes"] / (gg["kernel_ms"] * 1e-3) / 1e9
         tf = gg["flops"] / (gg["kernel_ms"] * 1e-3) / 1e12
+        # the product's arithmetic intensity (~444 flop/B) is past the ridge (~315):
+        # its roofline is the matrix cores'
         line["gdp"] = {"workload": gg["workload"], "value": tps, "unit": "tokens/s",
                        "kernel_ms": gg["kernel_ms"], "single_pass_ms": gg["single_pass_ms"],
                        "note": "in 8 segments of 8192 tokens: three chunked passes and a "
                                "state combine; single_pass_ms is the one-pass kernel",
-                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
-                       "mfma": {"flops_per_token": gg["flops_per_token"],
-                                "achieved_tflops": tf, "frac": tf / MFMA_PEAK_TFLOPS}}
+                       "roofline": {"bound": "mfma", "achieved": tf,
+                                    "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": tf / MFMA_PEAK_TFLOPS,
+                                    "flops_per_token": gg["flops_per_token"]},
+                       "hbm": {"achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS}}
     if "gates" in res:
         line["fused_gates"] = res["gates"]
     if "boundary" in res:

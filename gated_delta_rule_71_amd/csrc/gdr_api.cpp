@@ -69,6 +69,14 @@ int gdr_validate_prefill(const gdr_prefill_args *a) {
   if (a->num_householder > 2) return GDR_ERR_UNSUPPORTED;
   if (!pow2(a->chunk_size) || a->chunk_size < 16 || a->chunk_size > 256)
     return GDR_ERR_UNSUPPORTED;
+  // the chunk shape the kernels would run must be instantiated (float32 inputs with
+  // K = 128 fit only 16-row chunks in LDS, which the two-sub-step rows do not use)
+  {
+    const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
+    const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
+    if (!gdr::prefill_variant_exists(f32, a->head_k, rows, a->num_householder, 1))
+      return GDR_ERR_UNSUPPORTED;
+  }
   if (tokens > 0) {
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out) return GDR_ERR_INVALID_ARG;
     if (a->gate_mode == 1 && (!a->A_log || !a->dt_bias)) return GDR_ERR_INVALID_ARG;
@@ -180,9 +188,11 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *a) {
   return seg_plan(a).total;
 }
 
-int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
-  const int st = gdr_validate_prefill(a);
-  if (st != GDR_OK) return st;
+namespace {
+
+// Enqueue a validated prefill.  ws, ws_bytes: device memory for the segment path of
+// long batched rows (NULL: the single pass runs).
+int enqueue_prefill(const gdr_prefill_args *a, hipStream_t s, void *ws_base, size_t ws_bytes) {
   if (a->num_seqs == 0) return GDR_OK;
   gdr::PrefillParams p;
   p.q = a->q;
@@ -214,13 +224,12 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   p.boundary_interval = a->boundary_interval;
   const int f32 = a->qkv_dtype == GDR_DTYPE_F32;
   const int rows = gdr::prefill_chunk_rows(a->chunk_size, a->num_householder, f32, a->head_k);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   const SegPlan sp = seg_plan(a);
-  const bool aligned = (reinterpret_cast<uintptr_t>(a->workspace) & (kAlign - 1)) == 0;
-  if (sp.S > 1 && a->workspace && aligned && a->workspace_bytes >= sp.total) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(ws_base) & (kAlign - 1)) == 0;
+  if (sp.S > 1 && ws_base && aligned && ws_bytes >= sp.total) {
     // long rows in segments: the passes are prefills over the segments as packed
     // sequences (see segments.hip)
-    char *ws = static_cast<char *>(a->workspace);
+    char *ws = static_cast<char *>(ws_base);
     gdr::SegmentParams g{};
     g.batch = a->batch;
     g.seqlen = a->seqlen;
@@ -248,6 +257,11 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
       q.num_groups = nseq * a->num_qk_heads;
       return gdr::launch_prefill(q, f32, a->head_k, rows, a->num_householder, ns, s);
     };
+    // every pass's launch shape exists before anything is enqueued
+    for (const int dv : {a->head_v, a->head_k})
+      if (!gdr::prefill_variant_exists(f32, a->head_k, rows, a->num_householder,
+                                       gdr::prefill_state_waves(dv, nseq, a->num_v_heads)))
+        return GDR_ERR_UNSUPPORTED;
     if (gdr::launch_segment_setup(g, s) != hipSuccess) return GDR_ERR_HIP;
     gdr::PrefillParams pf = p;          // 1: from zero, final states F, no outputs
     pf.initial_state = nullptr;
@@ -266,9 +280,19 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
     po.final_state = nullptr;
     return run(po, a->head_v) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
   }
+  if (!gdr::prefill_variant_exists(f32, a->head_k, rows, a->num_householder, state_waves))
+    return GDR_ERR_UNSUPPORTED;
   const hipError_t e = gdr::launch_prefill(p, f32, a->head_k, rows, a->num_householder,
                                            state_waves, s);
   return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace
+
+int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
+  const int st = gdr_validate_prefill(a);
+  if (st != GDR_OK) return st;
+  return enqueue_prefill(a, static_cast<hipStream_t>(stream), a->workspace, a->workspace_bytes);
 }
 
 int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {

@@ -158,6 +158,8 @@ struct SegmentParams {
 hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream);
 hipError_t launch_segment_combine(const SegmentParams &p, hipStream_t stream);
 
+// Whether a prefill kernel is instantiated for this launch shape (host only).
+bool prefill_variant_exists(int qkv_f32, int head_k, int rows, int nh, int ns);
 // Rows per chunk the prefill kernels run for a requested chunk size (tokens).
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k);
 // State waves (32 value columns each) per prefill workgroup.

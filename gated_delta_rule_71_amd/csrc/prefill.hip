@@ -39,9 +39,13 @@
 // column tile (the tiles of one head share them through L2), o once and the state
 // once in each direction.
 //
-// Operand precision: bf16 inputs run with fp16 operands (bf16 values convert
-// exactly; T, P, H and D are rounded to fp16, 11 significant bits) and fp32
-// accumulation; fp32 inputs run every product with fp32 operands.
+// Operand precision: bf16 inputs run with fp16 operands and fp32 accumulation;
+// fp32 inputs run every product with fp32 operands.  On the fp16 path q, k and v
+// (after the optional L2 norm), and the in-kernel T, P, H and D, are rounded to
+// fp16 (11 significant bits).  bf16 values of magnitude in [2^-14, 65504) convert
+// exactly; smaller ones become fp16 subnormals and lose low bits (negligible
+// against the unit-norm rows they sit in), and entries of magnitude >= 65504
+// (inputs, the state, or the in-kernel deltas) overflow to infinity.
 
 #include <type_traits>
 
@@ -941,6 +945,16 @@ hipError_t launch_ns(const PrefillParams &p, int head_k, int rows, int nh, int n
 }
 
 }  // namespace
+
+bool prefill_variant_exists(int qkv_f32, int head_k, int rows, int nh, int ns) {
+  // mirrors launch_ns / launch_dk / launch_rows above
+  if (ns != 1 && ns != 2 && ns != 4) return false;
+  if (head_k != 64 && head_k != 128) return false;
+  const bool rows32 = !(qkv_f32 && head_k > 64);
+  if (nh == 1) return rows == 16 || (rows32 && rows == 32);
+  if (nh == 2) return rows32 && rows == 32;
+  return false;
+}
 
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k) {
   // fp32 operands with K = 128 only fit 16-row chunks in LDS

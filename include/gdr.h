@@ -41,9 +41,18 @@
  *  - Errors: arguments are checked on the host before anything is launched; on
  *    any error nothing is enqueued and no buffer is touched.  Preconditions on
  *    device-resident data (monotone cu_seqlens, 0 <= index < num_slots, unique
- *    non-negative indices, |q|,|k| entries below 65504 for bf16 inputs without the
- *    L2 norm) are documented, not checked: checking them would need a device
- *    synchronisation.  Violating them gives undefined results.
+ *    non-negative indices, value ranges below) are documented, not checked:
+ *    checking them would need a device synchronisation.  Violating them gives
+ *    undefined results.
+ *  - Value range of bf16 inputs: the prefill's matrix-core products take fp16
+ *    operands.  q, k (after the optional L2 norm) and v, the state, and the
+ *    in-kernel per-chunk values (the inverse T, the decayed scores P and the
+ *    deltas D = T beta (v - exp(G) k^T S)) are rounded to fp16 there, so every
+ *    such entry must stay below 65504 in magnitude (larger ones overflow to
+ *    infinity); bf16 entries below 2^-14 become fp16 subnormals and keep fewer
+ *    significant bits.  Unit-norm keys, states of moderate size and values of
+ *    order one are far inside this range.  F32 inputs use fp32 operands
+ *    throughout and have no such limit.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -112,7 +121,8 @@ typedef enum { GDR_DTYPE_F32 = 0, GDR_DTYPE_BF16 = 1 } gdr_dtype;
  *   tokens, in the [K, V] layout of final states.  E = sum of the counts.  Every
  *   sequence writes its entries, padding sequences (state index -1) included.
  * Supported: K in {64, 128}, V in {64, 128}, n_h in {1, 2}, q/k/v F32 or BF16,
- *   out F32 or BF16, Tt * n_h < 2^31 - 1024 rows and
+ *   except n_h = 2 with F32 inputs and K = 128 (GDR_ERR_UNSUPPORTED: its chunks do
+ *   not fit on chip), out F32 or BF16, Tt * n_h < 2^31 - 1024 rows and
  *   Tt * n_h * max(Hk * K, Hv * V) < 2^32 (element offsets within q, k, v and out
  *   are 32-bit); larger inputs return GDR_ERR_UNSUPPORTED.
  */

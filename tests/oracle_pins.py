@@ -200,6 +200,30 @@ def pin_l2norm_flag(lib):
     assert np.max(np.abs(o3 - o1)) > 1e-2, "without the flag, rescaled rows must matter"
 
 
+def pin_l2norm_epsilon(lib):
+    """Where the norm's epsilon sits.  A row x = a e_0 with a^2 = 1e-6 normalises to
+    e_0 a / sqrt(a^2 + 1e-6) = e_0 / sqrt(2) when the epsilon is added under the
+    square root; with it outside (a / (|a| + 1e-6)) or left out the component is
+    ~0.999 or 1.  One token from a zero state then gives the closed form
+    o = scale beta (k^ . q^) v = scale beta v / 2 and H = beta k^ v^T."""
+    D = 4
+    a = 1e-3
+    q = np.zeros((1, 1, 1, D))
+    k = np.zeros((1, 1, 1, 1, D))
+    q[..., 0] = a
+    k[..., 0] = -a                      # sign kept: k^ = -e_0 / sqrt(2)
+    v = np.array([1.0, -2.0, 0.5, 3.0]).reshape(1, 1, 1, 1, D)
+    g = np.array([-0.7]).reshape(1, 1, 1)
+    beta = np.array([0.6]).reshape(1, 1, 1, 1)
+    scale = 0.25
+    o, fs = oracle.prefill(q, k, v, g, beta, scale=scale, output_final_state=True,
+                           use_qk_l2norm=True, lib=lib)
+    _close(o[0, 0, 0], scale * 0.6 * (-0.5) * v[0, 0, 0, 0], 1e-12, "l2norm epsilon output")
+    h = np.zeros((D, D))
+    h[0] = 0.6 * (-1.0 / np.sqrt(2.0)) * v[0, 0, 0, 0]
+    _close(fs[0, 0], h, 1e-12, "l2norm epsilon state")
+
+
 def pin_grouped_heads(lib):
     """Hk = 2, Hv = 4: value head h reads q/k head h // 2 (contiguous groups)."""
     q, k, v, g, beta, s0 = _problem(12, T=9, Hk=2, Hv=4, D=5)
@@ -364,6 +388,7 @@ ALL_PINS = [
     pin_linearity,
     pin_scale,
     pin_l2norm_flag,
+    pin_l2norm_epsilon,
     pin_grouped_heads,
     pin_packed_equals_separate,
     pin_chunked_matches_naive,

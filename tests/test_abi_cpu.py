@@ -101,6 +101,14 @@ def _decode(**kw):
     (dict(boundary_states=FAKE, boundary_interval=96), 1),   # multiples of 64 only
     (dict(boundary_states=FAKE + 8, boundary_interval=64), 1),
     (dict(boundary_interval=100), 0),                # ignored without boundary_states
+    # the gated delta product with float32 inputs runs 32-row chunks, which fit in
+    # LDS at K = 64 only
+    (dict(qkv_dtype=0, num_householder=2, head_k=128), 2),
+    (dict(qkv_dtype=0, num_householder=2, head_k=128, head_v=64), 2),
+    (dict(qkv_dtype=0, num_householder=2, head_k=64, head_v=64), 0),
+    (dict(qkv_dtype=0, num_householder=2, head_k=64, head_v=128), 0),
+    (dict(qkv_dtype=0, num_householder=1, head_k=128), 0),
+    (dict(qkv_dtype=1, num_householder=2, head_k=128), 0),
 ])
 def test_validate_prefill(lib, kw, code):
     a = _prefill(**kw)
@@ -169,6 +177,14 @@ def test_invalid_call_launches_nothing(lib):
     """An invalid call returns before any HIP call, so it works without a GPU."""
     a = _prefill(head_k=96)
     assert lib.gdr_chunk_gated_delta_rule(ctypes.byref(a), None) == 2
+    # an unsupported launch shape, also where the segment path would run (long
+    # batched rows with a workspace given): rejected before the segment set-up
+    for kw in (dict(qkv_dtype=0, num_householder=2),
+               dict(qkv_dtype=0, num_householder=2, batch=1, num_seqs=1, seqlen=65536,
+                    num_v_heads=32, num_qk_heads=16)):
+        a = _prefill(**kw)
+        a.workspace, a.workspace_bytes = FAKE, 1 << 40
+        assert lib.gdr_chunk_gated_delta_rule(ctypes.byref(a), None) == 2
     d = _decode(num_slots=0)
     assert lib.gdr_ssm_decode(ctypes.byref(d), None) == 1
 

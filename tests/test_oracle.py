@@ -35,6 +35,8 @@ MUTANTS = {
                                "if (state_indices[n] < 0) { store_state(states + p * SS, K, V, final_state + h * SS); continue; }"),
     "decode_padding_writes": ("if (slot < 0) continue; /* padding writes nothing */",
                               "if (slot < 0) { store_state(states + p * SS, K, V, cache + h * SS); continue; }"),
+    "l2norm_eps_outside_sqrt": ("1.0 / sqrt(ss + 1e-6)", "1.0 / (sqrt(ss) + 1e-6)"),
+    "l2norm_no_eps": ("1.0 / sqrt(ss + 1e-6)", "1.0 / sqrt(ss)"),
     "no_sequence_reset": ("double *S = states + p * SS;\n    double *buf",
                           "double *S = states + (p % Hv) * SS;\n    double *buf"),
 }
