@@ -26,7 +26,8 @@ import math
 
 from . import _lib
 
-__all__ = ["chunk_gated_delta_rule", "chunk_gated_delta_rule_backward", "ssm_decode",
+__all__ = ["chunk_gated_delta_rule", "chunk_gated_delta_rule_noalloc",
+           "chunk_gated_delta_rule_backward", "ssm_decode",
            "causal_conv1d", "causal_conv1d_update", "gated_rmsnorm", "library", "abi_version"]
 
 
@@ -215,6 +216,47 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     _raise(lib.gdr_chunk_gated_delta_rule(a, _stream(stream)), "gdr_chunk_gated_delta_rule")
     ret_state = final_state if (output_final_state or state_indices is not None) else None
     return out, ret_state
+
+
+def chunk_gated_delta_rule_noalloc(q, k, v, g, beta, *, out, scale=None, chunk_size=64,
+                                   initial_state=None, final_state=None,
+                                   use_qk_l2norm_in_kernel=False, cu_seqlens=None,
+                                   state_indices=None, A_log=None, dt_bias=None,
+                                   boundary_states=None, boundary_interval=None, stream=None):
+    """chunk_gated_delta_rule for callers that cannot allocate: the caller passes
+    ``out`` (and ``final_state`` when one is wanted; with ``state_indices`` the slot
+    cache is updated in place), nothing is allocated here or in the library, and
+    long batched rows take the segment path on the library's per-GPU scratch
+    (gdr_chunk_gated_delta_rule_noalloc).  Calls on one GPU share that scratch:
+    keep them on one stream.  Returns ``out``."""
+    torch = _torch()
+    lib = library()
+    _check(q, "q", ndim=4)
+    _check(k, "k", dtype=q.dtype, ndim=(4, 5))
+    _check(v, "v", dtype=q.dtype, ndim=(4, 5))
+    _check(g, "g", dtype=torch.float32, ndim=3)
+    _check(beta, "beta", dtype=torch.float32, ndim=(3, 4))
+    _check(out, "out", ndim=4)
+    _gate_params(A_log, dt_bias, v.shape[-2], torch)
+    for name, t in (("cu_seqlens", cu_seqlens), ("state_indices", state_indices)):
+        if t is not None:
+            _check(t, name, dtype=torch.int32, ndim=1)
+    if state_indices is not None and final_state is None:
+        final_state = initial_state
+    for name, st in (("initial_state", initial_state), ("final_state", final_state),
+                     ("boundary_states", boundary_states)):
+        if st is not None:
+            _check(st, name, dtype=torch.float32, ndim=4)
+    if (boundary_states is None) != (boundary_interval is None):
+        raise ValueError("boundary_states and boundary_interval go together")
+    a = prefill_args(q, k, v, g, beta, scale=scale, chunk_size=chunk_size,
+                     initial_state=initial_state, final_state=final_state,
+                     use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
+                     state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias,
+                     boundary_states=boundary_states, boundary_interval=boundary_interval)
+    _raise(lib.gdr_chunk_gated_delta_rule_noalloc(a, _stream(stream)),
+           "gdr_chunk_gated_delta_rule_noalloc")
+    return out
 
 
 def decode_args(q, k, v, g, beta, ssm_state, *, batch_indices=None, scale=None,

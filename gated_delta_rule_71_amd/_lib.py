@@ -18,7 +18,7 @@ GDR_ERR_WORKSPACE = 3
 GDR_ERR_HIP = 4
 GDR_DTYPE_F32 = 0
 GDR_DTYPE_BF16 = 1
-ABI_VERSION = 3   # GDR_ABI_VERSION the structures below are laid out for
+ABI_VERSION = 4   # GDR_ABI_VERSION the structures below are laid out for
 
 # Every symbol include/gdr.h declares.
 EXPORTS = (
@@ -28,6 +28,7 @@ EXPORTS = (
     "gdr_validate_decode",
     "gdr_prefill_workspace_bytes",
     "gdr_chunk_gated_delta_rule",
+    "gdr_chunk_gated_delta_rule_noalloc",
     "gdr_ssm_decode",
     "gdr_validate_conv_prefill",
     "gdr_validate_conv_decode",
@@ -190,6 +191,9 @@ def load(path: str = LIB_PATH):
         lib.gdr_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.gdr_chunk_gated_delta_rule.argtypes = [ctypes.POINTER(PrefillArgs), ctypes.c_void_p]
         lib.gdr_chunk_gated_delta_rule.restype = ctypes.c_int
+        lib.gdr_chunk_gated_delta_rule_noalloc.argtypes = [ctypes.POINTER(PrefillArgs),
+                                                           ctypes.c_void_p]
+        lib.gdr_chunk_gated_delta_rule_noalloc.restype = ctypes.c_int
         lib.gdr_ssm_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
         lib.gdr_ssm_decode.restype = ctypes.c_int
         for name, typ in (("conv_prefill", ConvPrefillArgs), ("conv_decode", ConvDecodeArgs),

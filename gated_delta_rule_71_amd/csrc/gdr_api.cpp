@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "gdr.h"
@@ -293,6 +295,54 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
   const int st = gdr_validate_prefill(a);
   if (st != GDR_OK) return st;
   return enqueue_prefill(a, static_cast<hipStream_t>(stream), a->workspace, a->workspace_bytes);
+}
+
+// ---- prefill without allocation -----------------------------------------------------
+
+// Scratch of gdr_chunk_gated_delta_rule_noalloc: the segment path's workspace in a
+// file-scope device array, which every GPU the library runs on holds until the
+// process ends.  The segment plan keeps segments x batch rows x value heads <= 256,
+// so its four float32 matrices per segment and head (identity and transition K x K,
+// zero-start and entering states K x V, with K, V <= 128) take at most 4 x 16 MiB;
+// the packed segment boundaries and the alignment of each part fit in the rest.
+constexpr size_t kScratchBytes = (size_t{64} << 20) + 4096;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call
+// made with that device current (each GPU holds its own copy of the array).  Host code
+// uses only this address, never the array's name.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
+}
+
+}  // namespace
+
+int gdr_chunk_gated_delta_rule_noalloc(const gdr_prefill_args *a, void *stream) {
+  const int st = gdr_validate_prefill(a);
+  if (st != GDR_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const SegPlan sp = seg_plan(a);
+  if (sp.S <= 1) return enqueue_prefill(a, s, nullptr, 0);   // no scratch needed
+  if (sp.total > kScratchBytes) return GDR_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != GDR_OK) return rc;
+  return enqueue_prefill(a, s, ws, kScratchBytes);
 }
 
 int gdr_ssm_decode(const gdr_decode_args *a, void *stream) {

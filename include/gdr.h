@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 typedef enum {
@@ -390,6 +390,30 @@ size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *args);
 /* Enqueue a prefill / a decode step on `stream` (hipStream_t). */
 int gdr_chunk_gated_delta_rule(const gdr_prefill_args *args, void *stream);
 int gdr_ssm_decode(const gdr_decode_args *args, void *stream);
+
+/*
+ * The prefill for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same call and
+ * result as gdr_chunk_gated_delta_rule given the workspace of
+ * gdr_prefill_workspace_bytes, with that workspace taken from a scratch array the
+ * library holds in device memory instead (args->workspace and workspace_bytes are
+ * ignored).  The caller still passes every input and output.
+ *  - Limit: the scratch is 64 MiB + 4 KiB per GPU, held from the library's load to
+ *    the end of the process.  Every segment plan of the library fits (its
+ *    segments x batch rows x value heads <= 256); a plan that did not would return
+ *    GDR_ERR_WORKSPACE with nothing enqueued.  Calls that need no workspace use no
+ *    scratch.
+ *  - It calls no allocator.  The first call made with a given device current looks
+ *    up that device's scratch address (a runtime query, not a stream operation);
+ *    make that first call outside graph capture.  Later calls only enqueue.
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *    contents (each call rewrites all it reads, so nothing needs clearing).  Calls
+ *    that overlap on one GPU (on different streams, or replays of graphs holding
+ *    such calls that run concurrently) race on it: order them on one stream.
+ *  - Errors as gdr_chunk_gated_delta_rule, plus GDR_ERR_HIP when the scratch
+ *    address cannot be obtained.
+ */
+int gdr_chunk_gated_delta_rule_noalloc(const gdr_prefill_args *args, void *stream);
 
 /* Host-only checks and enqueue of the causal conv and the gated RMS norm. */
 int gdr_validate_conv_prefill(const gdr_conv_prefill_args *args);

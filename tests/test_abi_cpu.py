@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdr_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.gdr_abi_version() == _lib.ABI_VERSION == 4
     for code, name in [(0, "GDR_OK"), (1, "GDR_ERR_INVALID_ARG"), (2, "GDR_ERR_UNSUPPORTED"),
                        (3, "GDR_ERR_WORKSPACE"), (4, "GDR_ERR_HIP"), (99, "GDR_ERR_UNKNOWN")]:
         assert lib.gdr_status_string(code).decode() == name
