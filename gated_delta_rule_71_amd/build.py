@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.cpp", "prefill.hip", "decode.hip", "conv_norm.hip", "backward.hip",
-           "segments.hip"]
+SOURCES = ["gdr_api.cpp", "prefill.hip", "prefill64.hip", "decode.hip", "conv_norm.hip",
+           "backward.hip", "segments.hip"]
 ARCH = "gfx950"
 
 

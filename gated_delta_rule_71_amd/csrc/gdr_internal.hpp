@@ -167,6 +167,9 @@ int prefill_state_waves(int head_v, int num_seqs, int num_v_heads);
 
 hipError_t launch_prefill(const PrefillParams &p, int qkv_f32, int head_k, int rows, int nh,
                           int state_waves, hipStream_t stream);
+// 64-row chunks of bf16 inputs (launched by launch_prefill)
+hipError_t launch_prefill64(const PrefillParams &p, int head_k, int nh, int state_waves, int grid,
+                            hipStream_t stream);
 hipError_t launch_decode(const DecodeParams &p, int qkv_f32, int dk, int dv, int nh,
                          hipStream_t stream);
 // mode 0: prefill (outputs, then conv states); mode 1: decode

@@ -49,72 +49,11 @@
 
 #include <type_traits>
 
+#include "chunk_helpers.hpp"
 #include "common.hpp"
 #include "gdr_internal.hpp"
 
 namespace gdr {
-
-// exp(x) on the hardware base-2 exponential
-__device__ __forceinline__ float fexp(float x) {
-  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
-
-// One DPP lane move of a double (both halves with the same control); lanes
-// whose source is outside the pattern, or whose row is masked off, read 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const long long b = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, ROW_MASK, 0xf, false);
-  const int hi =
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROW_MASK, 0xf, false);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-// Inclusive prefix sum over lanes 0..31 of a wave (the whole wave must be
-// active): shifts by 1, 2, 4, 8 inside each 16-lane row, then lane 15's total
-// is broadcast into the next row.
-__device__ __forceinline__ double prefix_sum32(double x) {
-  x += dpp_f64<0x111, 0xf>(x);   // row_shr:1
-  x += dpp_f64<0x112, 0xf>(x);   // row_shr:2
-  x += dpp_f64<0x114, 0xf>(x);   // row_shr:4
-  x += dpp_f64<0x118, 0xf>(x);   // row_shr:8
-  x += dpp_f64<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
-  return x;
-}
-
-__device__ __forceinline__ double readlane_f64(double x, int l) {
-  const long long b = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), l);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) |
-                              static_cast<unsigned int>(lo));
-}
-
-// four consecutive input elements (8- or 16-byte aligned) as float
-__device__ __forceinline__ void load4(const uint16_t *p, float (&x)[4]) {
-  const uint2 u = *reinterpret_cast<const uint2 *>(p);
-  x[0] = __uint_as_float(u.x << 16);
-  x[1] = __uint_as_float(u.x & 0xffff0000u);
-  x[2] = __uint_as_float(u.y << 16);
-  x[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-__device__ __forceinline__ void load4(const float *p, float (&x)[4]) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
-
-// four consecutive output elements
-__device__ __forceinline__ void store4(__bf16 *p, const float (&o)[4]) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 h;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[i]);
-  *reinterpret_cast<bf16x4 *>(p) = h;
-}
-__device__ __forceinline__ void store4(float *p, const float (&o)[4]) {
-  *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
-}
 
 // Element e of two 8-element segments (rows r and r+1 of V) as one pair, written
 // to VT[e][r..r+1]: the transpose of a 2 x 8 block, in input precision.
@@ -243,17 +182,6 @@ __device__ __forceinline__ constexpr int tile_job_count() {
   int n = 0;
   while (tile_job<Tr>(n) >= 0) ++n;
   return n;
-}
-
-// four consecutive operand elements in LDS (8 bytes for fp16, 16 for fp32)
-__device__ __forceinline__ void store4e(_Float16 *p, const float (&x)[4]) {
-  f16x4 h;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(x[i]);
-  *reinterpret_cast<f16x4 *>(p) = h;
-}
-__device__ __forceinline__ void store4e(float *p, const float (&x)[4]) {
-  *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
 // Off-diagonal tiles J0 .. J1-1: A_10 = strict_lower(diag(beta) K_1 K_0^T * Gamma) and
@@ -947,9 +875,11 @@ hipError_t launch_ns(const PrefillParams &p, int head_k, int rows, int nh, int n
 }  // namespace
 
 bool prefill_variant_exists(int qkv_f32, int head_k, int rows, int nh, int ns) {
-  // mirrors launch_ns / launch_dk / launch_rows above
+  // mirrors launch_prefill64 (64-row chunks of bf16 inputs) and launch_ns / launch_dk /
+  // launch_rows above
   if (ns != 1 && ns != 2 && ns != 4) return false;
   if (head_k != 64 && head_k != 128) return false;
+  if (rows == 64) return !qkv_f32 && (nh == 1 || nh == 2);
   const bool rows32 = !(qkv_f32 && head_k > 64);
   if (nh == 1) return rows == 16 || (rows32 && rows == 32);
   if (nh == 2) return rows32 && rows == 32;
@@ -957,8 +887,9 @@ bool prefill_variant_exists(int qkv_f32, int head_k, int rows, int nh, int ns) {
 }
 
 int prefill_chunk_rows(int chunk_size, int nh, int qkv_f32, int head_k) {
-  // fp32 operands with K = 128 only fit 16-row chunks in LDS
-  const int cap = (qkv_f32 && head_k > 64) ? 16 : 32;
+  // bf16 inputs run 64-row chunks (prefill64.hip) when the chunk size reaches them;
+  // fp32 operands fit 32-row chunks in LDS, 16-row chunks with K = 128
+  const int cap = !qkv_f32 ? 64 : head_k > 64 ? 16 : 32;
   const int rows = chunk_size * nh;
   return rows < cap ? rows : cap;
 }
@@ -980,6 +911,7 @@ hipError_t launch_prefill(const PrefillParams &p, int qkv_f32, int head_k, int r
   const int rounds = (p.num_groups + 7) / 8;
   const int grid = items_per_xcd_round * rounds;
   if (grid == 0) return hipSuccess;
+  if (rows == 64) return launch_prefill64(p, head_k, nh, state_waves, grid, stream);
   return qkv_f32 ? launch_ns<float, true>(p, head_k, rows, nh, state_waves, grid, stream)
                  : launch_ns<uint16_t, false>(p, head_k, rows, nh, state_waves, grid, stream);
 }
