@@ -134,7 +134,7 @@ struct alignas(16) Stage64 {
 };
 template <class Tr>
 struct alignas(16) Solve64 {
-  _Float16 T[Tr::CR * Tr::LDT];   // rows 16b..16b+15: T_bb in columns 0..15
+  _Float16 T[Tr::CR * Tr::LDT];   // rows 16b..16b+15: -T_bb in columns 0..15
   _Float16 A[Tr::CR * Tr::LDA];   // A_bc, b > c; diagonal and upper blocks zero
   _Float16 P[Tr::CQ * Tr::LDA];   // scale (Q K^T * Gamma), causal
 };
@@ -250,10 +250,11 @@ __device__ __forceinline__ void p64_diag(const Stage64<Tr> &s, Solve64<Tr> &v,
   steps(std::integral_constant<int, 15>(), std::integral_constant<int, 5>());
   steps(std::integral_constant<int, 10>(), std::integral_constant<int, 5>());
   steps(std::integral_constant<int, 5>(), std::integral_constant<int, 5>());
+  // stored negated: the state waves' substitution steps take -T_bb (see there)
   _Float16 *trow = v.T + (16 * bk + j) * LDT;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float x[4] = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+    const float x[4] = {-t[4 * q], -t[4 * q + 1], -t[4 * q + 2], -t[4 * q + 3]};
     store4e(trow + 4 * q, x);
   }
 }
@@ -591,25 +592,27 @@ prefill64_kernel(const PrefillParams p) {
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) hb[ct][sl] = M::from_acc(H[ct][2 * sl], H[ct][2 * sl + 1]);
-      f32x4 R[2][4];
+      // Block by block: X_b = K_b H0, then -R_b = diag(beta) (diag(exp G) X_b - V_b) (V in
+      // the accumulator layout by transposed reads of the row-major bf16 values), then
+      // the substitution step D_b = T_bb (R_b - sum_{c<b} A_bc D_c).  The solve stores
+      // -T_bb, and -R_b enters the products of A as their accumulator, so the step is
+      // two matrix-core products with no vector work between them; each block's step
+      // overlaps the next block's X.
+      const frag tf0 = M::load(v.T, LDT, l16, 0, lane);
+      const frag tf1 = M::load(v.T, LDT, 16 + l16, 0, lane);
+      const frag tf2 = M::load(v.T, LDT, 32 + l16, 0, lane);
+      const frag tf3 = M::load(v.T, LDT, 48 + l16, 0, lane);
+      const frag af1 = M::load(v.A, LDA, 16 + l16, 0, lane);
+      const frag af2 = M::load(v.A, LDA, 32 + l16, 0, lane);
+      const frag af3a = M::load(v.A, LDA, 48 + l16, 0, lane);
+      const frag af3b = M::load(v.A, LDA, 48 + l16, 32, lane);
+      f32x4 D[2][4];
+      frag d01[2];
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk) {
         frag kf[KS];
 #pragma unroll
         for (int sl = 0; sl < KS; ++sl) kf[sl] = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
-        f32x4 x0 = zero4(), x1 = zero4();
-#pragma unroll
-        for (int sl = 0; sl < KS; ++sl) {
-          x0 = M::mma(kf[sl], hb[0][sl], x0);
-          x1 = M::mma(kf[sl], hb[1][sl], x1);
-        }
-        R[0][mk] = x0;
-        R[1][mk] = x1;
-      }
-      // R = diag(beta) (V - diag(exp G) X); V in the accumulator layout by transposed
-      // reads of the row-major bf16 values
-#pragma unroll
-      for (int mk = 0; mk < 4; ++mk) {
         const int r0 = 16 * mk + 4 * g4;
         const float4 b4 = *reinterpret_cast<const float4 *>(s.B + r0);
         const float4 e4 = *reinterpret_cast<const float4 *>(s.eG + r0);
@@ -618,33 +621,29 @@ prefill64_kernel(const PrefillParams p) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const s16x4 vv = read_tr(s.V, LDV, 16 * mk, 32 * wave + 16 * ct, lane);
+          f32x4 x = zero4();
+#pragma unroll
+          for (int sl = 0; sl < KS; ++sl) x = M::mma(kf[sl], hb[ct][sl], x);
+          f32x4 rn;   // -R_b
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float vx = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(vv[i])) << 16);
-            R[ct][mk][i] = br[i] * (vx - er[i] * R[ct][mk][i]);
+            rn[i] = br[i] * (er[i] * x[i] - vx);
+          }
+          if (mk == 0) {
+            D[ct][0] = M::mma(tf0, M::from_acc(rn, zero4()), zero4());
+          } else if (mk == 1) {
+            const f32x4 z = M::mma(af1, M::from_acc(D[ct][0], zero4()), rn);
+            D[ct][1] = M::mma(tf1, M::from_acc(z, zero4()), zero4());
+            d01[ct] = M::from_acc(D[ct][0], D[ct][1]);
+          } else if (mk == 2) {
+            const f32x4 z = M::mma(af2, d01[ct], rn);
+            D[ct][2] = M::mma(tf2, M::from_acc(z, zero4()), zero4());
+          } else {
+            const f32x4 z = M::mma(af3b, M::from_acc(D[ct][2], zero4()), M::mma(af3a, d01[ct], rn));
+            D[ct][3] = M::mma(tf3, M::from_acc(z, zero4()), zero4());
           }
         }
-      }
-      // D_b = T_bb (R_b - sum_{c<b} A_bc D_c)
-      frag tf[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tf[b] = M::load(v.T, LDT, 16 * b + l16, 0, lane);
-      const frag af1 = M::load(v.A, LDA, 16 + l16, 0, lane);
-      const frag af2 = M::load(v.A, LDA, 32 + l16, 0, lane);
-      const frag af3a = M::load(v.A, LDA, 48 + l16, 0, lane);
-      const frag af3b = M::load(v.A, LDA, 48 + l16, 32, lane);
-      f32x4 D[2][4];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        D[ct][0] = M::mma(tf[0], M::from_acc(R[ct][0], zero4()), zero4());
-        const f32x4 z1 = M::mma(af1, M::from_acc(D[ct][0], zero4()), zero4());
-        D[ct][1] = M::mma(tf[1], M::from_acc(R[ct][1] - z1, zero4()), zero4());
-        const frag d01 = M::from_acc(D[ct][0], D[ct][1]);
-        const f32x4 z2 = M::mma(af2, d01, zero4());
-        f32x4 z3 = M::mma(af3a, d01, zero4());
-        D[ct][2] = M::mma(tf[2], M::from_acc(R[ct][2] - z2, zero4()), zero4());
-        z3 = M::mma(af3b, M::from_acc(D[ct][2], zero4()), z3);
-        D[ct][3] = M::mma(tf[3], M::from_acc(R[ct][3] - z3, zero4()), zero4());
       }
       // D as the operands of phase B: db = D (for O), dk = diag(exp(G_last - G)) D (for
       // the state update), both fp16
