@@ -427,15 +427,26 @@ def run_conv_norm_leg(wl2, steps, warmup):
     _, kn = time_launches(norm_launch, steps, warmup)
     norm_bytes = 3 * o.numel() * 2
     gbs = lambda byt, ms: byt / (ms * 1e-3) / 1e9
+    # reference: a plain device copy of the conv's input (the same bytes read and
+    # written once), what a stream of this size reaches on this part
+    xc = torch.empty_like(x)
+    _, kcp = time_launches(lambda: xc.copy_(x), steps, warmup)
+    copy_gbs = gbs(conv_bytes, kcp)
     return {
+        "copy_reference": {"kernel_ms": kcp, "bytes": conv_bytes, "achieved_gbs": copy_gbs,
+                           "hbm_frac": copy_gbs / HBM_PEAK_GBS,
+                           "note": "torch device copy of the conv input (read + write once)"},
         "conv_prefill": {"kernel_ms": kc, "channels": C, "tokens": T, "bytes": conv_bytes,
                          "achieved_gbs": gbs(conv_bytes, kc),
-                         "hbm_frac": gbs(conv_bytes, kc) / HBM_PEAK_GBS},
+                         "hbm_frac": gbs(conv_bytes, kc) / HBM_PEAK_GBS,
+                         "vs_copy": gbs(conv_bytes, kc) / copy_gbs,
+                         "note": "two launches: outputs, then the conv-state update"},
         "conv_decode": {"kernel_ms": kd, "requests": n, "bytes": dec_bytes,
                         "achieved_gbs": gbs(dec_bytes, kd)},
         "gated_rmsnorm": {"kernel_ms": kn, "rows": T * Hv, "group": V, "bytes": norm_bytes,
                           "achieved_gbs": gbs(norm_bytes, kn),
-                          "hbm_frac": gbs(norm_bytes, kn) / HBM_PEAK_GBS},
+                          "hbm_frac": gbs(norm_bytes, kn) / HBM_PEAK_GBS,
+                          "vs_copy": gbs(norm_bytes, kn) / copy_gbs},
     }
 
 
