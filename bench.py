@@ -152,7 +152,7 @@ def traffic_from(fetch_db, write_db):
         copy = max(v for _, n, v in rows if "copyBuffer" in n)
         scale = COPY_PROBE_BYTES / copy
         out = {}
-        for key, pat in (("prefill_varlen", "prefill_kernel"), ("decode", "decode_kernel")):
+        for key, pat in (("prefill_varlen", "prefill64_kernel"), ("decode", "decode_kernel")):
             vals = [v for _, n, v in rows if pat in n]
             out[key] = (float(np.mean(vals)) * scale, len(vals))
         return out, scale
@@ -160,7 +160,7 @@ def traffic_from(fetch_db, write_db):
     fetch, fs = per_kernel(fetch_db, "FETCH_SIZE")
     write, ws = per_kernel(write_db, "WRITE_SIZE")
     data = {}
-    for key, src in (("prefill_varlen", "prefill.hip"), ("decode", "decode.hip")):
+    for key, src in (("prefill_varlen", "prefill64.hip"), ("decode", "decode.hip")):
         data[key] = {"source_sha": kernel_source_hash(src),
                      "fetch_bytes": fetch[key][0], "write_bytes": write[key][0],
                      "bytes_per_launch": fetch[key][0] + write[key][0],
@@ -709,8 +709,8 @@ def main():
             "state": "fp32 slot cache", "parallelism": "single GPU"}
         line["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                            "traffic": stored_traffic("prefill_varlen", "prefill.hip"),
-                            "kernel": "prefill_kernel", "bytes_per_launch": p["bytes"],
+                            "traffic": stored_traffic("prefill_varlen", "prefill64.hip"),
+                            "kernel": "prefill64_kernel", "bytes_per_launch": p["bytes"],
                             "kernel_ms": p["kernel_ms"]}
         tf = p["flops"] / (p["kernel_ms"] * 1e-3) / 1e12
         line["mfma"] = {"flops_per_token": p["flops_per_token"], "achieved_tflops": tf,
