@@ -1,9 +1,10 @@
 """Benchmark of the gated delta rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--legs prefill,prefill_b4,decode,gdp,gates,boundary,conv_norm,backward]
+                    [--legs prefill,prefill_b4,decode,gdp,long_packed,gates,boundary,
+                            conv_norm,backward]
 
-Eight legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
+Nine legs, each timed over exactly K steps bracketed by torch.cuda.synchronize():
   prefill: packed varlen gated delta rule, 8 sequences of U{1..8192} tokens
            (~32.8K tokens), 16 q/k heads shared by 32 v heads, K = V = 128, bf16
            q/k/v, fp32 g/beta, fp32 slot-cache states, chunk 64.  Its tokens/s is
@@ -18,6 +19,9 @@ Eight legs, each timed over exactly K steps bracketed by torch.cuda.synchronize(
            outside the timed launch.
   gdp:     gated delta product, 2 Householder sub-steps, B=1, T=65536, H=32,
            K = V = 128, bf16, chunk 128 tokens; tokens/s.
+  long_packed: one packed request of 65 536 tokens over a slot cache (cu_seqlens,
+           H = 32, K = V = 128, bf16): the segment slots planned on the device,
+           against the single pass; tokens/s.
   gates:   the prefill and decode workloads again with g and beta given as raw
            projections and formed inside the kernels (A_log, dt_bias); kernel
            times and their ratio to the legs above.
@@ -62,7 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs",
-                    default="prefill,prefill_b4,decode,gdp,gates,boundary,conv_norm,backward")
+                    default="prefill,prefill_b4,decode,gdp,long_packed,gates,boundary,conv_norm,"
+                            "backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="value heads of the prefill workload the CPU oracle runs")
@@ -608,6 +613,17 @@ def main():
         print(f"[bench] gdp: kernel {kern:.3f} ms", file=sys.stderr, flush=True)
         del wl4
 
+    # ---- one long packed request (segments planned on the device) ----------------------
+    if "long_packed" in legs:
+        wl5 = W.long_packed()
+        wall, kern = run_prefill_leg(wl5, max(2, args.steps // 4), min(args.warmup, 2))
+        _, kern1 = run_prefill_leg(wl5, 2, 1, segments=False)
+        res["long_packed"] = dict(wall_ms=wall, kernel_ms=kern, tokens=wl5.tokens,
+                                  workload=wl5.name, single_pass_ms=kern1)
+        print(f"[bench] long_packed: kernel {kern:.3f} ms (single pass {kern1:.3f} ms)",
+              file=sys.stderr, flush=True)
+        del wl5
+
     # ---- gates formed in the kernels from raw projections (same workloads) --------------
     if "gates" in legs:
         gw2 = W.with_raw_gates(wl2, 2)
@@ -753,6 +769,14 @@ def main():
                                     "frac": tf / MFMA_PEAK_TFLOPS,
                                     "flops_per_token": gg["flops_per_token"]},
                        "hbm": {"achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS}}
+    if "long_packed" in res:
+        lp = res["long_packed"]
+        line["long_packed"] = {"workload": lp["workload"],
+                               "value": lp["tokens"] / (lp["wall_ms"] * 1e-3),
+                               "unit": "tokens/s", "kernel_ms": lp["kernel_ms"],
+                               "single_pass_ms": lp["single_pass_ms"],
+                               "note": "8 segment slots planned on the device: three "
+                                       "chunked passes and a state combine"}
     if "gates" in res:
         line["fused_gates"] = res["gates"]
     if "boundary" in res:

@@ -160,10 +160,13 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
     ``boundary_states`` float32 [E,Hv,K,V] with ``boundary_interval`` (tokens, a
     multiple of 64) receives each sequence's state after every whole multiple of
     the interval, sequences in order (E = boundary_count(lengths, interval)).
-    Long batched rows that leave compute units idle run in segments (three passes
-    of the chunked kernel and a state combine) when a workspace of
-    gdr_prefill_workspace_bytes is given; it is allocated here unless ``segments``
-    is False (then the single pass runs).
+    Long sequences (batched rows, or packed sequences without boundary states)
+    that leave compute units idle run in segments (three passes of the chunked
+    kernel and a state combine) when a workspace of gdr_prefill_workspace_bytes is
+    given.  When ``workspace`` is None that workspace is ALLOCATED here with
+    torch.empty (a device allocation per call) unless ``segments`` is False (then
+    the single pass runs); callers that cannot allocate pass their own
+    ``workspace`` or use chunk_gated_delta_rule_noalloc.
     Returns (o [B,T,Hv,V], final_state or None).
     """
     torch = _torch()
@@ -206,7 +209,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, chunk_size=64, initial_
                      use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, cu_seqlens=cu_seqlens,
                      state_indices=state_indices, out=out, A_log=A_log, dt_bias=dt_bias,
                      boundary_states=boundary_states, boundary_interval=boundary_interval)
-    # long batched rows may run in segments, with a workspace (single pass without)
+    # long sequences may run in segments, with a workspace (single pass without)
     need = int(lib.gdr_prefill_workspace_bytes(a))
     if workspace is None and need > 0 and segments:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

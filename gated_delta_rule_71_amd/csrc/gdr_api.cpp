@@ -132,19 +132,66 @@ namespace {
 
 constexpr int kComputeUnits = 256;
 
-// Segment plan for a prefill: S > 1 segments per batch row when the batch rows alone
-// leave most compute units idle (fewer workgroups than compute units even with 32
-// value columns each) and the rows are long enough for S segments of >= 2048 tokens.
+// Segment plan for a prefill: S > 1 segments per batch row (or S segment slots shared
+// by packed sequences) when the sequences alone leave most compute units idle (fewer
+// workgroups than compute units even with 32 value columns each) and are long enough
+// for segments of >= 2048 tokens.
 struct SegPlan {
   int S = 1, seg_len = 0;
-  size_t cu = 0, ident = 0, F = 0, A = 0, H_in = 0, total = 0;
+  bool packed = false;      // segments of packed sequences, planned on the device
+  size_t cu = 0, first = 0, ident = 0, F = 0, A = 0, H_in = 0, total = 0;
 };
+
+// workspace layout of a plan with `nseq` segments (and `nfirst` entries of the packed
+// plan's first-segment table)
+void seg_layout(SegPlan &sp, const gdr_prefill_args *a, size_t nseq, size_t nfirst) {
+  const size_t Hv = a->num_v_heads;
+  const size_t kk = static_cast<size_t>(a->head_k) * a->head_k;
+  const size_t kv = static_cast<size_t>(a->head_k) * a->head_v;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes);
+    return at;
+  };
+  sp.cu = take((nseq + 1) * sizeof(int32_t));
+  sp.first = nfirst ? take(nfirst * sizeof(int32_t)) : 0;
+  sp.ident = take(nseq * Hv * kk * 4);
+  sp.A = take(nseq * Hv * kk * 4);
+  sp.F = take(nseq * Hv * kv * 4);
+  sp.H_in = take(nseq * Hv * kv * 4);
+  sp.total = off;
+}
+
+// Packed sequences whose (sequence, value head) pairs leave compute units idle.  Their
+// lengths live on the device, so the plan is sized from the total: S = 256 / Hv
+// segment slots (one workgroup per slot and head at four state waves), segments of
+// seg_len >= 2048 tokens such that sum_n max(1, ceil(L_n / seg_len)) <= S.  It is taken
+// only where it pays whatever the lengths: seg_len <= T_tot / (4 N), so the longest
+// sequence (at least T_tot / N tokens) is at least four segments long and its chain
+// shortens more than the three passes cost.  Boundary states keep the single pass.
+SegPlan seg_plan_packed(const gdr_prefill_args *a) {
+  SegPlan sp;
+  if (a->boundary_states || a->num_seqs < 1) return sp;
+  const long N = a->num_seqs, Hv = a->num_v_heads, T = a->seqlen;
+  if (N * Hv * (a->head_v / 32) >= kComputeUnits) return sp;
+  const long S = kComputeUnits / Hv;
+  if (S < 5 * N) return sp;
+  long seg_len = ((T + (S - N) - 1) / (S - N) + 63) / 64 * 64;
+  if (seg_len < 2048) seg_len = 2048;
+  if (seg_len * 4 * N > T) return sp;
+  sp.S = static_cast<int>(S);
+  sp.seg_len = static_cast<int>(seg_len);
+  sp.packed = true;
+  seg_layout(sp, a, static_cast<size_t>(S), static_cast<size_t>(N) + 1);
+  return sp;
+}
 
 SegPlan seg_plan(const gdr_prefill_args *a) {
   SegPlan sp;
-  if (!a || a->cu_seqlens || a->state_indices || a->batch < 1 || a->num_v_heads < 1 ||
-      a->head_v < 32 || a->head_k < 1)
-    return sp;
+  if (!a || a->batch < 1 || a->num_v_heads < 1 || a->head_v < 32 || a->head_k < 1) return sp;
+  if (a->cu_seqlens) return seg_plan_packed(a);
+  if (a->state_indices) return sp;
   const long pairs = static_cast<long>(a->batch) * a->num_v_heads;
   if (pairs * (a->head_v / 32) >= kComputeUnits) return sp;
   int S = 1;
@@ -163,21 +210,7 @@ SegPlan seg_plan(const gdr_prefill_args *a) {
     sp.S = 1;
     return sp;
   }
-  const size_t nseq = static_cast<size_t>(a->batch) * S, Hv = a->num_v_heads;
-  const size_t kk = static_cast<size_t>(a->head_k) * a->head_k;
-  const size_t kv = static_cast<size_t>(a->head_k) * a->head_v;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off += round_up(bytes);
-    return at;
-  };
-  sp.cu = take((nseq + 1) * sizeof(int32_t));
-  sp.ident = take(nseq * Hv * kk * 4);
-  sp.A = take(nseq * Hv * kk * 4);
-  sp.F = take(nseq * Hv * kv * 4);
-  sp.H_in = take(nseq * Hv * kv * 4);
-  sp.total = off;
+  seg_layout(sp, a, static_cast<size_t>(a->batch) * S, 0);
   return sp;
 }
 
@@ -247,7 +280,13 @@ int enqueue_prefill(const gdr_prefill_args *a, hipStream_t s, void *ws_base, siz
     g.initial_state = a->initial_state;
     g.H_in = reinterpret_cast<float *>(ws + sp.H_in);
     g.final_state = a->final_state;
-    const int nseq = a->batch * sp.S;
+    if (sp.packed) {   // the caller's sequences, planned into the S slots on the device
+      g.batch = a->num_seqs;
+      g.src_cu = a->cu_seqlens;
+      g.first = reinterpret_cast<int32_t *>(ws + sp.first);
+      g.state_indices = a->state_indices;
+    }
+    const int nseq = sp.packed ? sp.S : a->batch * sp.S;
     auto run = [&](gdr::PrefillParams q, int dv) {
       q.cu_seqlens = g.cu;
       q.seqlen = a->batch * a->seqlen;
@@ -266,6 +305,7 @@ int enqueue_prefill(const gdr_prefill_args *a, hipStream_t s, void *ws_base, siz
         return GDR_ERR_UNSUPPORTED;
     if (gdr::launch_segment_setup(g, s) != hipSuccess) return GDR_ERR_HIP;
     gdr::PrefillParams pf = p;          // 1: from zero, final states F, no outputs
+    pf.state_indices = nullptr;         // the passes' states are per segment
     pf.initial_state = nullptr;
     pf.final_state = const_cast<float *>(g.F);
     pf.out = nullptr;
@@ -278,7 +318,8 @@ int enqueue_prefill(const gdr_prefill_args *a, hipStream_t s, void *ws_base, siz
     if (run(pa, a->head_k) != hipSuccess) return GDR_ERR_HIP;
     if (gdr::launch_segment_combine(g, s) != hipSuccess) return GDR_ERR_HIP;   // 3
     gdr::PrefillParams po = p;          // 4: from the entering states, outputs (and
-    po.initial_state = g.H_in;          //    boundary states)
+    po.state_indices = nullptr;         //    boundary states)
+    po.initial_state = g.H_in;
     po.final_state = nullptr;
     return run(po, a->head_v) == hipSuccess ? GDR_OK : GDR_ERR_HIP;
   }
@@ -301,10 +342,12 @@ int gdr_chunk_gated_delta_rule(const gdr_prefill_args *a, void *stream) {
 
 // Scratch of gdr_chunk_gated_delta_rule_noalloc: the segment path's workspace in a
 // file-scope device array, which every GPU the library runs on holds until the
-// process ends.  The segment plan keeps segments x batch rows x value heads <= 256,
-// so its four float32 matrices per segment and head (identity and transition K x K,
-// zero-start and entering states K x V, with K, V <= 128) take at most 4 x 16 MiB;
-// the packed segment boundaries and the alignment of each part fit in the rest.
+// process ends.  Every segment plan keeps its segment count (batch rows x segments,
+// or packed segment slots) x value heads <= 256, so its four float32 matrices per
+// segment and head (identity and transition K x K, zero-start and entering states
+// K x V, with K, V <= 128) take at most 4 x 16 MiB; the segment boundaries (<= 257
+// int32), the packed plan's first-slot table (<= 53 int32) and the 256-byte
+// alignment of each part fit in the rest.
 constexpr size_t kScratchBytes = (size_t{64} << 20) + 4096;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

@@ -136,24 +136,32 @@ struct BackwardParams {
   int nh;                        // Householder sub-steps per token (rows per token)
 };
 
-// Segments of long batched sequences (the prefill's workspace).  Segment s of batch
-// row b covers tokens [s * seg_len, min((s + 1) * seg_len, seqlen)) and is packed
-// sequence b * S + s of the internal passes.
+// Segments of long sequences (the prefill's workspace).
+//  * Batched rows (src_cu NULL): segment s of batch row b covers tokens
+//    [s * seg_len, min((s + 1) * seg_len, seqlen)) and is packed sequence b * S + s of
+//    the internal passes.
+//  * Packed sequences (src_cu = the caller's cu_seqlens): the S segment slots are
+//    planned on the device; sequence n owns slots first[n] .. first[n+1]-1, each of
+//    seg_len tokens but its last (every sequence at least one, possibly empty); the
+//    slots past the last sequence's are empty segments at the end of the tokens.
 struct SegmentParams {
-  int batch;
+  int batch;                     // batch rows, or packed sequences
   int seqlen;
-  int S;                         // segments per batch row
+  int S;                         // segments per batch row; segment slots when packed
   int seg_len;                   // tokens per segment (a multiple of 64)
   int Hv;
   int DK;
   int DV;
-  int32_t *cu;                   // [batch * S + 1]
-  float *ident;                  // [batch * S, Hv, DK, DK] identity states
-  const float *F;                // [batch * S, Hv, DK, DV] final states from zero
-  const float *A;                // [batch * S, Hv, DK, DK] transitions
-  const float *initial_state;    // [batch, Hv, DK, DV] or NULL
-  float *H_in;                   // [batch * S, Hv, DK, DV] entering states
-  float *final_state;            // [batch, Hv, DK, DV] or NULL
+  int32_t *cu;                   // [batch * S + 1] (packed: [S + 1])
+  float *ident;                  // [segments, Hv, DK, DK] identity states
+  const float *F;                // [segments, Hv, DK, DV] final states from zero
+  const float *A;                // [segments, Hv, DK, DK] transitions
+  const float *initial_state;    // [batch, Hv, DK, DV], a slot cache, or NULL
+  float *H_in;                   // [segments, Hv, DK, DV] entering states
+  float *final_state;            // [batch, Hv, DK, DV], a slot cache, or NULL
+  const int32_t *src_cu;         // packed: [batch + 1] the caller's cu_seqlens
+  int32_t *first;                // packed: [batch + 1] first segment slot of each sequence
+  const int32_t *state_indices;  // packed: slot of each sequence (NULL: dense states)
 };
 hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream);
 hipError_t launch_segment_combine(const SegmentParams &p, hipStream_t stream);

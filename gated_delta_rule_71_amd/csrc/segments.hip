@@ -22,13 +22,33 @@
 
 namespace gdr {
 
-// cu_seqlens of the packed segments, and identity states [B*S, Hv, DK, DK]
+// cu_seqlens of the segments, and identity states [segments, Hv, DK, DK].  Packed
+// sequences are planned by one thread: sequence n gets max(1, ceil(L_n / seg_len))
+// consecutive slots (the host sizes seg_len so that they never exceed S; the count is
+// still clamped so that no write leaves the slot arrays), and the remaining slots are
+// empty segments at the end of the tokens.
 __global__ void segment_setup_kernel(const SegmentParams p, long n_ident) {
   const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int nseq = p.batch * p.S;
-  if (i <= nseq) {
-    const int b = static_cast<int>(i / p.S), s = static_cast<int>(i % p.S);
-    p.cu[i] = i == nseq ? p.batch * p.seqlen : b * p.seqlen + min(s * p.seg_len, p.seqlen);
+  if (p.src_cu) {
+    if (i == 0) {
+      int s = 0;
+      for (int n = 0; n < p.batch; ++n) {
+        const int a = p.src_cu[n], e = p.src_cu[n + 1];
+        int c = e > a ? (e - a + p.seg_len - 1) / p.seg_len : 1;
+        if (c > p.S - s) c = p.S - s;
+        p.first[n] = s;
+        for (int j = 0; j < c; ++j) p.cu[s + j] = a + j * p.seg_len;
+        s += c;
+      }
+      p.first[p.batch] = s;
+      for (; s <= p.S; ++s) p.cu[s] = p.src_cu[p.batch];
+    }
+  } else {
+    const int nseq = p.batch * p.S;
+    if (i <= nseq) {
+      const int b = static_cast<int>(i / p.S), s = static_cast<int>(i % p.S);
+      p.cu[i] = i == nseq ? p.batch * p.seqlen : b * p.seqlen + min(s * p.seg_len, p.seqlen);
+    }
   }
   if (i < n_ident) {
     const int e = static_cast<int>(i % (static_cast<long>(p.DK) * p.DK));
@@ -66,6 +86,16 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
   const int h = (blockIdx.x / ntile) % p.Hv;
   const int b = blockIdx.x / ntile / p.Hv;
   const size_t sv = static_cast<size_t>(DK) * p.DV, sa = static_cast<size_t>(DK) * DK;
+  // this row's segments, and where its state comes from and goes (slot -1: read
+  // slot 0, write nothing)
+  const int s_begin = p.src_cu ? p.first[b] : b * p.S;
+  const int s_end = p.src_cu ? p.first[b + 1] : s_begin + p.S;
+  int src = b, dst = b;
+  if (p.state_indices) {
+    const int idx = p.state_indices[b];
+    src = idx < 0 ? 0 : idx;
+    dst = idx;
+  }
   // row of this lane's element v of tile t
   auto row = [&](int t, int v) { return 16 * (wave * NT + t) + 4 * g + v; };
   const size_t col = static_cast<size_t>(TC) * vt + i;
@@ -75,7 +105,7 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
 #pragma unroll
     for (int v = 0; v < 4; ++v)
       H[t][v] = p.initial_state
-                    ? p.initial_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+                    ? p.initial_state[(static_cast<size_t>(src) * p.Hv + h) * sv +
                                       static_cast<size_t>(row(t, v)) * p.DV + col]
                     : 0.0f;
   float4 ra[A4];
@@ -83,9 +113,9 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
 #pragma unroll
     for (int j = 0; j < A4; ++j) ra[j] = reinterpret_cast<const float4 *>(A)[tid + 256 * j];
   };
-  fetchA(p.A + (static_cast<size_t>(b) * p.S * p.Hv + h) * sa);
-  for (int s = 0; s < p.S; ++s) {
-    const size_t seq = static_cast<size_t>(b) * p.S + s;
+  if (s_begin < s_end) fetchA(p.A + (static_cast<size_t>(s_begin) * p.Hv + h) * sa);
+  for (int s = s_begin; s < s_end; ++s) {
+    const size_t seq = static_cast<size_t>(s);
     float *hin = p.H_in + (seq * p.Hv + h) * sv + col;
     const float *F = p.F + (seq * p.Hv + h) * sv + col;
     f32x4 acc[NT];
@@ -111,7 +141,7 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
       d[3] = ra[j].w;
     }
     __syncthreads();
-    if (s + 1 < p.S) fetchA(p.A + ((seq + 1) * p.Hv + h) * sa);
+    if (s + 1 < s_end) fetchA(p.A + ((seq + 1) * p.Hv + h) * sa);
     // acc += A_s H over k, the operands of KB k-steps read before their products
     const float *a0 = sA + (16 * wave * NT + i) * LDA + g;
     const float *b0 = sH + g * LDH + i;
@@ -133,19 +163,20 @@ __global__ void __launch_bounds__(256) segment_combine_kernel(const SegmentParam
 #pragma unroll
     for (int t = 0; t < NT; ++t) H[t] = acc[t];
   }
-  if (p.final_state) {
+  if (p.final_state && dst >= 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        p.final_state[(static_cast<size_t>(b) * p.Hv + h) * sv +
+        p.final_state[(static_cast<size_t>(dst) * p.Hv + h) * sv +
                       static_cast<size_t>(row(t, v)) * p.DV + col] = H[t][v];
   }
 }
 
 hipError_t launch_segment_setup(const SegmentParams &p, hipStream_t stream) {
-  const long n_ident = static_cast<long>(p.batch) * p.S * p.Hv * p.DK * p.DK;
-  const long n = n_ident > p.batch * p.S + 1 ? n_ident : p.batch * p.S + 1;
+  const long nseg = p.src_cu ? p.S : static_cast<long>(p.batch) * p.S;
+  const long n_ident = nseg * p.Hv * p.DK * p.DK;
+  const long n = n_ident > nseg + 1 ? n_ident : nseg + 1;
   hipLaunchKernelGGL(segment_setup_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p,
                      n_ident);
   return hipGetLastError();

@@ -257,6 +257,13 @@ def config4(decay="config", T=65536, H=32):
                          decay=decay, initial_state="random", num_householder=2)
 
 
+def long_packed(T=65536):
+    """One long request packed alone (cu_seqlens) over a 4-slot cache: T tokens,
+    16 q/k heads, 32 v heads, K = V = 128, bf16, chunk 64."""
+    return prefill_packed(f"gdn_packed_bf16_N1_T{T}_Hk16_Hv32_D128", 5, [T], 16, 32, 128, 128,
+                          BF16, 64, num_slots=4, slot_init="random")
+
+
 def config3(n=128, num_slots=256, Hk=16, Hv=32, K=128, V=128, num_padding=16, seed=3):
     """Decode: one bf16 token per request over a [256,32,128,128] fp32 slot cache.
 

@@ -376,14 +376,23 @@ int gdr_validate_decode(const gdr_decode_args *args);
 /*
  * Optional device workspace of a prefill, in bytes (a host-only function of the
  * sizes; 256-byte aligned memory owned by the caller, contents irrelevant).  It is
- * nonzero only for long batched rows (no cu_seqlens, dense states) whose
- * (sequence, value head) pairs leave compute units idle: given the workspace, such
- * a call splits every row into S segments and runs three chunked passes over them
- * (from zero, the transition from the identity with zero values, and from the true
- * entering states, combined in between), which shortens the dependent chain S
- * times.  Without it (NULL or smaller) the single pass runs; both give the same
- * result up to rounding.  Boundary states are allowed on the segment path when
- * boundary_interval divides the segment length (checked here: 0 otherwise).
+ * nonzero only for long sequences whose (sequence, value head) pairs leave compute
+ * units idle: given the workspace, such a call splits every sequence into segments
+ * and runs three chunked passes over them (from zero, the transition from the
+ * identity with zero values, and from the true entering states, combined in
+ * between), which shortens the dependent chain by the segment count.  Without it
+ * (NULL or smaller) the single pass runs; both give the same result up to rounding.
+ *  - Batched rows (no cu_seqlens, dense states): S = 2^j segments of every row,
+ *    each >= 2048 tokens.  Boundary states are allowed when boundary_interval
+ *    divides the segment length (checked here: 0 otherwise).
+ *  - Packed sequences (cu_seqlens, dense or slot states, no boundary states): the
+ *    lengths live on the device, so the plan is sized from the total token count
+ *    (seqlen): 256 / Hv segment slots, sequence n taking max(1, ceil(L_n / seg_len))
+ *    of them, planned by a device kernel.  Taken when 256 / Hv >= 5 num_seqs and the
+ *    segment length is at most seqlen / (4 num_seqs), so that it pays whatever the
+ *    lengths.  cu_seqlens must satisfy the documented layout (0 = cu[0] <= ... <=
+ *    cu[num_seqs] = seqlen); the device plan clamps its writes to the workspace
+ *    whatever the values.
  */
 size_t gdr_prefill_workspace_bytes(const gdr_prefill_args *args);
 
@@ -399,8 +408,8 @@ int gdr_ssm_decode(const gdr_decode_args *args, void *stream);
  * library holds in device memory instead (args->workspace and workspace_bytes are
  * ignored).  The caller still passes every input and output.
  *  - Limit: the scratch is 64 MiB + 4 KiB per GPU, held from the library's load to
- *    the end of the process.  Every segment plan of the library fits (its
- *    segments x batch rows x value heads <= 256); a plan that did not would return
+ *    the end of the process.  Every segment plan of the library fits (its segment
+ *    count x value heads <= 256); a plan that did not would return
  *    GDR_ERR_WORKSPACE with nothing enqueued.  Calls that need no workspace use no
  *    scratch.
  *  - It calls no allocator.  The first call made with a given device current looks

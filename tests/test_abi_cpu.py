@@ -122,8 +122,22 @@ def test_validate_prefill(lib, kw, code):
           num_householder=2), 8),
     (dict(batch=1, num_seqs=1, seqlen=8192, num_v_heads=4, num_qk_heads=4), 4),
     (dict(batch=4, num_seqs=4, seqlen=4096, num_v_heads=16, num_qk_heads=16), 1),  # full GPU
+    # packed: the lengths are on the device, so the plan takes 256 / Hv segment slots
+    # when the segment length is at most a quarter of the mean sequence length
     (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
-          cu_seqlens=FAKE), 1),                               # packed: lengths on the device
+          cu_seqlens=FAKE), 8),
+    (dict(batch=1, num_seqs=2, seqlen=65536, num_v_heads=16, num_qk_heads=16,
+          cu_seqlens=FAKE), 16),
+    (dict(batch=1, num_seqs=3, seqlen=65536, num_v_heads=4, num_qk_heads=2,
+          cu_seqlens=FAKE, state_indices=FAKE, num_slots=8), 64),
+    (dict(batch=1, num_seqs=2, seqlen=65536, num_v_heads=32, num_qk_heads=32,
+          cu_seqlens=FAKE), 1),                               # 8 slots < 5 per sequence
+    (dict(batch=1, num_seqs=1, seqlen=7000, num_v_heads=32, num_qk_heads=32,
+          cu_seqlens=FAKE), 1),                               # under 4 x 2048 tokens
+    (dict(batch=1, num_seqs=8, seqlen=36112, num_v_heads=32, num_qk_heads=16,
+          cu_seqlens=FAKE), 1),                               # full GPU already
+    (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
+          cu_seqlens=FAKE, boundary_states=FAKE, boundary_interval=64), 1),
     # boundary states stay in order when they fall on segment ends (8192 tokens)
     (dict(batch=1, num_seqs=1, seqlen=65536, num_v_heads=32, num_qk_heads=32,
           boundary_states=FAKE, boundary_interval=64), 8),
@@ -131,9 +145,10 @@ def test_validate_prefill(lib, kw, code):
           boundary_states=FAKE, boundary_interval=3072), 1),
 ])
 def test_prefill_segment_workspace(lib, kw, segments):
-    """Long batched rows that leave compute units idle may run in segments; the
+    """Long sequences that leave compute units idle may run in segments; the
     optional workspace holds, per segment and head, the identity and transition
-    (K x K) and the zero-start and entering states (K x V), all float32."""
+    (K x K) and the zero-start and entering states (K x V), all float32, plus the
+    segment boundaries (and, packed, each sequence's first segment slot)."""
     a = _prefill(**kw)
     need = lib.gdr_prefill_workspace_bytes(ctypes.byref(a))
     if segments == 1:
@@ -141,7 +156,9 @@ def test_prefill_segment_workspace(lib, kw, segments):
     else:
         nseq = a.batch * segments
         floats = nseq * a.num_v_heads * (2 * a.head_k * a.head_k + 2 * a.head_k * a.head_v)
-        assert floats * 4 <= need <= floats * 4 + 5 * 256 + 4 * (nseq + 1)
+        ints = nseq + 1 + (a.num_seqs + 1 if kw.get("cu_seqlens") else 0)
+        assert floats * 4 + 4 * ints <= need <= floats * 4 + 6 * 256 + 4 * ints
+        assert need <= (64 << 20) + 4096   # fits the allocation-free entry's scratch
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -121,3 +121,103 @@ def test_segments_with_boundary_states():
     ro, rs = _oracle(wl)
     check(res[True][0], ro, f32_inputs=False, out_bf16=True, what="segments outputs")
     check(res[True][1], rs, f32_inputs=False, out_bf16=False, what="segments final states")
+
+
+# ---- packed sequences -----------------------------------------------------------------
+
+def _packed_segments_used(wl):
+    """Whether the library plans segments for this packed call (host-only query)."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    d = {n: to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")}
+    out = torch.empty(wl.q.shape[:2] + wl.v.shape[-2:], dtype=torch.float32, device="cuda")
+    a = gdr.prefill_args(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=wl.chunk_size,
+                         out=out, cu_seqlens=to_dev(wl.cu_seqlens),
+                         state_indices=to_dev(wl.state_indices),
+                         initial_state=to_dev(wl.initial_state))
+    return int(gdr.library().gdr_prefill_workspace_bytes(a)) > 0
+
+
+def _packed_run(wl, segments, **kw):
+    """(outputs, states after the call) — states: the slot cache, or the final states."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    d = {n: to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")}
+    cache = to_dev(wl.initial_state)
+    o, fs = gdr.chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                       chunk_size=wl.chunk_size, initial_state=cache,
+                                       output_final_state=True, cu_seqlens=to_dev(wl.cu_seqlens),
+                                       state_indices=to_dev(wl.state_indices), segments=segments,
+                                       A_log=to_dev(wl.A_log), dt_bias=to_dev(wl.dt_bias), **kw)
+    torch.cuda.synchronize()
+    return to_host(o), fs.cpu().numpy()
+
+
+def _packed_check(wl, res, *, f32, l2, what):
+    from parity import oracle_prefill_batch
+    pairs = [(n, h) for n in range(wl.num_seqs) for h in range(wl.v.shape[-2])]
+    ref = oracle_prefill_batch(wl, pairs, use_qk_l2norm=l2)
+    cu = wl.cu_seqlens
+    for name, (o, st) in res.items():
+        ox, orf, sx, srf = [], [], [], []
+        for (n, h) in pairs:
+            ox.append(o[0, cu[n]:cu[n + 1], h])
+            orf.append(ref[(n, h)][0])
+            slot = n if wl.state_indices is None else int(wl.state_indices[n])
+            if slot >= 0:
+                sx.append(st[slot, h].astype(np.float64))
+                srf.append(ref[(n, h)][1])
+        e_o = check(np.concatenate(ox), np.concatenate(orf), f32_inputs=f32, out_bf16=not f32,
+                    what=f"{what} {name} outputs")
+        e_s = check(np.stack(sx), np.stack(srf), f32_inputs=f32, out_bf16=False,
+                    what=f"{what} {name} states")
+        print(f"{what} {name}: output err {e_o:.3e}, state err {e_s:.3e}", flush=True)
+
+
+def test_packed_segments_slot_cache():
+    """Packed sequences with a slot cache: a long one (10 segments of 2048 tokens, the
+    last ragged), an empty padding request (slot -1: reads slot 0, writes nothing), a
+    medium one and an empty request with a slot (written back unchanged).  Segments
+    and single pass against the oracle; slots no request writes stay byte-identical."""
+    lengths = [20000, 0, 13000, 0]
+    wl = W.prefill_packed("seg_packed", 46, lengths, 2, 4, 128, 128, W.BF16, 64, decay="slow",
+                          num_slots=8, slot_init="random")
+    idx = wl.state_indices.copy()
+    idx[1] = -1
+    from dataclasses import replace
+    wl = replace(wl, state_indices=idx)
+    assert _packed_segments_used(wl), "the shape should take the segment path"
+    res = {"segments": _packed_run(wl, True), "single pass": _packed_run(wl, False)}
+    _packed_check(wl, res, f32=False, l2=False, what="packed slots")
+    written = [int(s) for s in idx if s >= 0]
+    untouched = np.setdiff1d(np.arange(wl.initial_state.shape[0]), written)
+    for name, (_, st) in res.items():
+        assert np.array_equal(st[untouched].view(np.uint32),
+                              wl.initial_state[untouched].view(np.uint32)), name
+        # the empty request with a slot leaves its slot's state as it was
+        assert np.array_equal(st[idx[3]].view(np.uint32),
+                              wl.initial_state[idx[3]].view(np.uint32)), name
+
+
+def test_packed_segments_gdp_raw_gates_dense_states():
+    """The gated delta product (n_h = 2) on packed sequences with dense initial
+    states, gates formed from raw projections and q/k normalised in the kernel."""
+    from dataclasses import replace
+    base = W.prefill_dense("seg_packed_gdp", 47, 1, 16384, 4, 8, 128, 128, W.BF16, 32,
+                           decay="slow", num_householder=2)
+    rng = np.random.default_rng(47)
+    cu = np.array([0, 15000, 16384], dtype=np.int32)
+    h0 = (0.1 * rng.standard_normal((2, 8, 128, 128))).astype(np.float32)
+    wl = W.with_raw_gates(replace(base, cu_seqlens=cu, initial_state=h0), 47)
+    assert _packed_segments_used(wl), "the shape should take the segment path"
+    kw = {"use_qk_l2norm_in_kernel": True}
+    res = {"segments": _packed_run(wl, True, **kw), "single pass": _packed_run(wl, False, **kw)}
+    _packed_check(wl, res, f32=False, l2=True, what="packed gdp")
+
+
+def test_packed_segments_deterministic():
+    wl = W.prefill_packed("seg_packed_det", 48, [9000, 12000], 4, 4, 128, 128, W.BF16, 64,
+                          decay="config", num_slots=4, slot_init="random")
+    assert _packed_segments_used(wl)
+    a, b = _packed_run(wl, True), _packed_run(wl, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

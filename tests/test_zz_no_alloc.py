@@ -71,3 +71,30 @@ def test_noalloc_without_segments():
     assert seg_bytes == 0
     assert np.array_equal(to_host(o), to_host(o_ws))
     assert np.array_equal(fs.cpu().numpy(), s_ws.cpu().numpy())
+
+
+def test_noalloc_packed_slot_cache_two_calls():
+    """Packed sequences on a slot cache (the device-planned segment path): each call
+    equals the workspace entry point's bit for bit, the second on fewer tokens."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    for name, seed, lengths in (("noalloc_p1", 84, [15000, 9000]), ("noalloc_p2", 85, [9000])):
+        wl = W.prefill_packed(name, seed, lengths, 2, 4, 128, 128, W.BF16, 64, decay="slow",
+                              num_slots=4, slot_init="random")
+        d = [to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")]
+        cu, idx = to_dev(wl.cu_seqlens), to_dev(wl.state_indices)
+        probe = gdr.prefill_args(*d, cu_seqlens=cu, state_indices=idx,
+                                 initial_state=to_dev(wl.initial_state),
+                                 out=torch.empty(1, dtype=torch.bfloat16, device="cuda"))
+        assert int(gdr.library().gdr_prefill_workspace_bytes(probe)) > 0, name
+        c_ws = to_dev(wl.initial_state)
+        o_ws, _ = gdr.chunk_gated_delta_rule(*d, initial_state=c_ws, cu_seqlens=cu,
+                                             state_indices=idx)
+        c = to_dev(wl.initial_state)
+        o = torch.full_like(o_ws, float("nan"))
+        gdr.chunk_gated_delta_rule_noalloc(*d, out=o, initial_state=c, final_state=c,
+                                           cu_seqlens=cu, state_indices=idx)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(o), to_host(o_ws)), f"{name}: outputs differ"
+        assert torch.equal(c, c_ws), f"{name}: slot caches differ"
+        print(f"{name}: packed noalloc equals the workspace entry", flush=True)
