@@ -50,6 +50,24 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle, no stride): loads
+// and stores at offsets past the resource's byte count are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
+// four consecutive outputs at a byte offset of a buffer resource (dropped past its end)
+template <typename TOut>
+__device__ __forceinline__ void store4_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 o) {
+  if constexpr (sizeof(TOut) == 4) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o), r, off, 0, 0);
+  } else {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = __builtin_convertvector(o, bf16x4);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, h), r, off, 0, 0);
+  }
+}
+
 // two floats -> two fp16 in one word (one v_cvt_pk_f16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   const f32x2 f = {a, b};
@@ -67,6 +85,26 @@ __device__ __forceinline__ void store8_bf16_as_f16(_Float16 *dst, const uint4 &u
 __device__ __forceinline__ void store8_pk(_Float16 *dst, const float (&x)[8]) {
   *reinterpret_cast<uint4 *>(dst) =
       make_uint4(pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7]));
+}
+
+// Buffer resource over rows [r0, r0 + nrows) of a row-major 16-bit matrix with `stride`
+// elements per row: loads past those rows read as zero.
+// The arguments are uniform across the wave; the read-first-lane tells the compiler so
+// (a resource it takes for divergent would be applied lane group by lane group).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, int r0,
+                                                            int nrows, uint32_t stride) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base + static_cast<size_t>(r0) * stride);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int bytes = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(static_cast<uint32_t>(max(nrows, 0)) * stride * 2));
+  return __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo), 0, bytes, kBufferWord3);
+}
+// sixteen bytes at a byte offset of a buffer resource
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // Lane j of 16-lane group g receives M[r0 + 4g + e][c0 + j], e = 0..3, of a row-major
@@ -145,10 +183,14 @@ struct Smem64 {
   float AR[4][Tr::ARB];
 };
 
+struct Scan64 {
+  float g2, gb, eg, egl, b;
+};
+
 template <class Tr>
 struct Regs64 {
   Seg8<uint16_t> k[Tr::KPT], q[Tr::QPT], v[Tr::VPT];
-  float g, b;
+  float g, b;     // gates of the chunk the decay scan reads next
 };
 
 // ---- the solve of one chunk (producer waves, phase B) --------------------------------
@@ -192,34 +234,65 @@ __device__ __forceinline__ void p64_tile_out(const Stage64<Tr> &s, f32x4 acc, fl
   store4e(dst + 16 * c + 4 * g4, x);
 }
 
-// The four diagonal blocks A_bb and their inverses T_bb = (I + A_bb)^-1.  Row j of
-// T_bb solves the upper triangular system (I + A_bb)^T t = e_j by back substitution;
-// lane 16 b + j does it for block b, so one pass over the 64 lanes inverts all four.
+// Diagonal block b of A from the raw product K_b K_b^T (accumulator layout): fp32 in
+// AR[b].  The product is symmetric, so its accumulator tile also gives lane (l16, g4)
+// row l16, columns 4 g4 .. 4 g4 + 3: entries left of the diagonal are scaled by
+// exp2(GB_row - G2_col), the rest masked to zero before the exponential.
+struct DiagBases {
+  float base;
+  float4 gc;
+};
 template <class Tr>
-__device__ __forceinline__ void p64_diag(const Stage64<Tr> &s, Solve64<Tr> &v,
-                                         float (*AR)[Tr::ARB], int lane) {
-  using M = typename Tr::M;
-  constexpr int KS = Tr::KS, LDT = Tr::LDT, LDR = Tr::LDR;
+__device__ __forceinline__ DiagBases p64_diag_bases(const Stage64<Tr> &s, int b, int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
+  return {s.GB[16 * b + l16], *reinterpret_cast<const float4 *>(s.G2 + 16 * b + 4 * g4)};
+}
+template <class Tr>
+__device__ __forceinline__ void p64_diag_put(const DiagBases &d, f32x4 acc, int b,
+                                             float (*AR)[Tr::ARB], int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const float gcv[4] = {d.gc.x, d.gc.y, d.gc.z, d.gc.w};
+  float a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = acc[i] * __builtin_amdgcn_exp2f(4 * g4 + i < l16 ? d.base - gcv[i] : -INFINITY);
+  *reinterpret_cast<float4 *>(AR[b] + l16 * Tr::LDR + 4 * g4) = make_float4(a[0], a[1], a[2], a[3]);
+}
+template <class Tr>
+__device__ __forceinline__ void p64_diag_store(const Stage64<Tr> &s, f32x4 acc, int b,
+                                               float (*AR)[Tr::ARB], int lane) {
+  p64_diag_put<Tr>(p64_diag_bases<Tr>(s, b, lane), acc, b, AR, lane);
+}
+
+// All four diagonal blocks from the staged K (the first chunk of a sequence; later
+// chunks' blocks are formed by the producers from registers while staging).  The
+// operands are read in the staging registers' layout (lane: row l16, contraction
+// indices 32 sl + 8 g4 .. + 7), so that both ways give the same bits.
+template <class Tr>
+__device__ __forceinline__ void p64_diag_lds(const Stage64<Tr> &s, float (*AR)[Tr::ARB],
+                                             int lane) {
+  using M = typename Tr::M;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if (b == 2) __builtin_amdgcn_sched_barrier(0);   // two blocks' operands at a time
-    typename M::frag f[KS];
-    p64_block<Tr>(s.K, b, lane, f);
+    typename M::frag f[Tr::KS];
+#pragma unroll
+    for (int sl = 0; sl < Tr::KS; ++sl)
+      f[sl].v = *reinterpret_cast<const f16x8 *>(s.K + (16 * b + (lane & 15)) * Tr::LDK +
+                                                  32 * sl + 8 * (lane >> 4));
     f32x4 acc = zero4();
 #pragma unroll
-    for (int sl = 0; sl < KS; ++sl) acc = M::mma(f[sl], f[sl], acc);
-    // K_b K_b^T is symmetric: its accumulator tile also gives lane (l16, g4) row l16,
-    // columns 4 g4 .. 4 g4 + 3
-    const float base = s.GB[16 * b + l16];
-    const float4 gc = *reinterpret_cast<const float4 *>(s.G2 + 16 * b + 4 * g4);
-    const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
-    float a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = acc[i] * __builtin_amdgcn_exp2f(4 * g4 + i < l16 ? base - gcv[i] : -INFINITY);
-    *reinterpret_cast<float4 *>(AR[b] + l16 * LDR + 4 * g4) = make_float4(a[0], a[1], a[2], a[3]);
+    for (int sl = 0; sl < Tr::KS; ++sl) acc = M::mma(f[sl], f[sl], acc);
+    p64_diag_store<Tr>(s, acc, b, AR, lane);
   }
+}
+
+// The inverses T_bb = (I + A_bb)^-1 of the four diagonal blocks in AR.  Row j of T_bb
+// solves the upper triangular system (I + A_bb)^T t = e_j by back substitution; lane
+// 16 b + j does it for block b, so one pass over the 64 lanes inverts all four.
+template <class Tr>
+__device__ __forceinline__ void p64_invert(Solve64<Tr> &v, float (*AR)[Tr::ARB], int lane) {
+  constexpr int LDT = Tr::LDT, LDR = Tr::LDR;
   const int bk = lane >> 4, j = lane & 15;
   const float *Ab = AR[bk];
   float t[16];
@@ -260,6 +333,7 @@ __device__ __forceinline__ void p64_diag(const Stage64<Tr> &s, Solve64<Tr> &v,
 }
 
 // The off-diagonal blocks A_bc, b > c (no mask: every column is left of the diagonal).
+// Producer 1 forms all but A_32, which producer 0 forms beside the inversion.
 template <class Tr>
 __device__ __forceinline__ void p64_offdiag(const Stage64<Tr> &s, Solve64<Tr> &v, int lane) {
   using M = typename Tr::M;
@@ -273,7 +347,7 @@ __device__ __forceinline__ void p64_offdiag(const Stage64<Tr> &s, Solve64<Tr> &v
     const int q = 16 * b + l16;
     const float base = s.GB[q];
 #pragma unroll
-    for (int c = 0; c < b; ++c) {
+    for (int c = 0; c < (b == 3 ? 2 : b); ++c) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int sl = 0; sl < KS; ++sl) acc = M::mma(f[c][sl], f[b][sl], acc);
@@ -325,11 +399,23 @@ __device__ __forceinline__ void p64_prows(const Stage64<Tr> &s, Solve64<Tr> &v, 
   }
 }
 
+// The solve of one chunk; the diagonal blocks of A are in AR already.
 template <class Tr>
 __device__ __forceinline__ void p64_solve(const Stage64<Tr> &s, Solve64<Tr> &v,
                                           float (*AR)[Tr::ARB], int pw, float scale, int lane) {
   if (pw == 0) {
-    p64_diag<Tr>(s, v, AR, lane);
+    // A_32 beside the inversion: its operands are read first, its products issued after
+    using M = typename Tr::M;
+    typename M::frag f2[Tr::KS], f3[Tr::KS];
+    p64_block<Tr>(s.K, 2, lane, f2);
+    p64_block<Tr>(s.K, 3, lane, f3);
+    const int q = 48 + (lane & 15);
+    const float base = s.GB[q];
+    p64_invert<Tr>(v, AR, lane);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int sl = 0; sl < Tr::KS; ++sl) acc = M::mma(f2[sl], f3[sl], acc);
+    p64_tile_out<Tr, false>(s, acc, base, 0, v.A + q * Tr::LDA, 2, lane);
   } else if (pw == 1) {
     p64_offdiag<Tr>(s, v, lane);
   } else if constexpr (Tr::NQB == 4) {   // one token per row: 1 + 4 and 2 + 3 tiles
@@ -424,7 +510,7 @@ prefill64_kernel(const PrefillParams p) {
   // upper blocks of A, the P tiles above the causal boundary) must read as zero
   {
     _Float16 *z = reinterpret_cast<_Float16 *>(&sm.sv[0]);
-    constexpr int nz = static_cast<int>(sizeof(sm.sv) / sizeof(_Float16));
+    constexpr int nz = static_cast<int>(sizeof(sm.sv)) / static_cast<int>(sizeof(_Float16));
     for (int i = tid; i < nz; i += NT) z[i] = static_cast<_Float16>(0.0f);
   }
 
@@ -432,114 +518,148 @@ prefill64_kernel(const PrefillParams p) {
   const int nchunks = (row_end - row_begin + CR - 1) / CR;
 
   Regs64<Tr> rg;   // producer registers: the inputs of one chunk between fetch and staging
+  frag kh[KPT];    // producer registers: its staged K block as fp16 operand fragments
 
   // inputs of the chunk starting at row c -> producer registers (addresses clamped to
   // the sequence, also past its end; validity is applied at staging)
+  // inputs of the chunk starting at row c -> producer registers, through buffer
+  // resources that end at the sequence's last row: rows past it read as zero, which is
+  // what the chunk algebra needs of them (no clamps, no masks), and the per-lane offsets
+  // stay the same from chunk to chunk
   auto fetch = [&](Regs64<Tr> &cr, int c) __attribute__((always_inline)) {
-    const int last = row_end - 1;
-    const int tq = c / NH, tlast = t1 - 1;
+    const int nrow = min(CR, row_end - c), tq = c / NH, nq = min(CQ, t1 - tq);
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb, c, nrow, kstride);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qb, tq, nq, kstride);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
-      cr.k[j].load(kb + (static_cast<uint32_t>(min(c + r, last)) * kstride + sg * 8));
-    }
+    for (int j = 0; j < KPT; ++j)
+      cr.k[j].u = load16(rk, ((16 * pw + l16) * kstride + (4 * j + g4) * 8) * 2);
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
-      cr.q[j].load(qb + (static_cast<uint32_t>(min(tq + r, tlast)) * kstride + sg * 8));
+      cr.q[j].u = load16(rq, (r * kstride + sg * 8) * 2);
     }
     if (vrow) {   // one uniform branch around all value loads
+      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vrow, c, nrow, vstride);
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int u = stid + j * ST, r = u / VSEG, sg = u % VSEG;
-        cr.v[j].load(vrow + (static_cast<uint32_t>(min(c + r, last)) * vstride + sg * 8));
+        cr.v[j].u = load16(rv, (r * vstride + sg * 8) * 2);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < VPT; ++j) cr.v[j].zero();
     }
-    if (pw == 3) {
-      const int row = min(c + lane, last);
-      cr.g = gb[static_cast<uint32_t>(row / NH) * p.Hv];
-      cr.b = bb[static_cast<uint32_t>(row) * p.Hv];
-    }
   };
-  // producer registers (chunk starting at row c) -> staged LDS buffer.  The L2 norm and
-  // whether every row of the chunk is valid are compile-time choices, so that no
-  // branch splits the conversions and full chunks skip the row masks.
-  auto stage = [&](const Regs64<Tr> &cr, int c, Stage64<Tr> &s, auto l2c) __attribute__((always_inline)) {
+  // the gates of the chunk starting at row c (producer 0; requested a whole interval
+  // before the decay scan reads them)
+  auto fetch_gates = [&](Regs64<Tr> &cr, int c) __attribute__((always_inline)) {
+    const int row = min(c + lane, row_end - 1);
+    cr.g = gb[static_cast<uint32_t>(row / NH) * p.Hv];
+    cr.b = bb[static_cast<uint32_t>(row) * p.Hv];
+  };
+  // producer registers (a chunk; rows past the sequence hold zeros) -> staged LDS
+  // buffer.  The L2 norm is a compile-time choice, so that no branch splits the
+  // conversions.
+  auto stage = [&](const Regs64<Tr> &cr, Stage64<Tr> &s, auto l2c) __attribute__((always_inline)) {
     constexpr bool L2 = decltype(l2c)::value;
-    const int nrow = min(CR, row_end - c);          // valid rows
-    const int nq = min(CQ, t1 - c / NH);            // valid query rows
-    auto rows = [&](auto fullc) __attribute__((always_inline)) {
-      constexpr bool FULL = decltype(fullc)::value;
-      auto masked = [&](const uint4 &u, bool ok) __attribute__((always_inline)) {
-        if constexpr (FULL) return u;
-        return make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
-      };
-      // one 8-element segment of a K or Q row -> fp16 in LDS, L2-normalised over the row
-      // (the SEG lanes holding a row are consecutive)
-      auto segment = [&](const Seg8<uint16_t> &in, bool ok, _Float16 *dst) __attribute__((always_inline)) {
-        const uint4 u = masked(in.u, ok);
-        if constexpr (L2) {
-          Seg8<uint16_t> t;
-          t.u = u;
-          float x[8];
-          t.get(x);
-          float ss = 0.0f;
+    // L2 factor of a row from this lane's partial sum of squares: the lanes that hold
+    // the row's other segments are xor 16 and 32 away (K) or xor 1 .. SEG / 2 (Q)
+    auto rnorm = [&](float ss, auto krows) __attribute__((always_inline)) {
+      if constexpr (decltype(krows)::value) {
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        for (int o = SEG / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      }
+      return 1.0f / sqrtf(ss + 1e-6f);
+    };
+    {   // K: row 16 pw + l16, segments 4 j + g4 (the row's KPT segments in lanes l16,
+        // l16 + 16, l16 + 32, l16 + 48)
+      float x[KPT][8];
 #pragma unroll
-          for (int o = SEG / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-          const float rn = 1.0f / sqrtf(ss + 1e-6f);
+      for (int j = 0; j < KPT; ++j) cr.k[j].get(x[j]);
+      if constexpr (L2) {
+        float ss = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= rn;
-          store8_pk(dst, x);
-        } else {
-          store8_bf16_as_f16(dst, u);
-        }
-      };
+        for (int j = 0; j < KPT; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += x[j][e] * x[j][e];
+        const float rn = rnorm(ss, std::true_type());
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[j][e] *= rn;
+      }
+      const int r = 16 * pw + l16;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
-        segment(cr.k[j], r < nrow, s.K + r * LDK + sg * 8);
+        const uint4 w = make_uint4(pk_f16(x[j][0], x[j][1]), pk_f16(x[j][2], x[j][3]),
+                                   pk_f16(x[j][4], x[j][5]), pk_f16(x[j][6], x[j][7]));
+        *reinterpret_cast<uint4 *>(s.K + r * LDK + (4 * j + g4) * 8) = w;
+        kh[j].v = __builtin_bit_cast(f16x8, w);
       }
-#pragma unroll
-      for (int j = 0; j < QPT; ++j) {
-        const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
-        segment(cr.q[j], r < nq, s.Q + r * LDK + sg * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int u = stid + j * ST, r = u / VSEG, sg = u % VSEG;
-        *reinterpret_cast<uint4 *>(s.V + r * LDV + sg * 8) = masked(cr.v[j].u, r < nrow);
-      }
-    };
-    if (nrow == CR && nq == CQ)
-      rows(std::true_type());
-    else
-      rows(std::false_type());
-    if (pw == 3) {
-      // inclusive prefix sum of the per-row decay in fp64 (a token's g sits on its
-      // first sub-step), and the per-row factors; gates formed here from raw
-      // projections when asked
-      const bool ok = lane < nrow;
-      float gv = cr.g;
-      float bv = cr.b;
-      if (p.gate_mode) {
-        gv = gate_decay(cr.g, gate_A, gate_dt);
-        bv = gate_beta(cr.b);
-      }
-      const double gr = prefix_sum64((ok && (c + lane) % NH == 0) ? gv : 0.0);
-      bv = ok ? bv : 0.0f;
-      const double glast = readlane_f64(gr, CR - 1);
-      const float g2 = static_cast<float>(gr) * 1.4426950408889634f;
-      s.G2[lane] = g2;
-      s.GB[lane] = g2 + __builtin_amdgcn_logf(bv);   // log2(0) = -inf: beta 0 rows vanish
-      s.eG[lane] = fexp(static_cast<float>(gr));
-      s.eGl[lane] = fexp(static_cast<float>(glast - gr));
-      s.B[lane] = bv;
     }
+    // Q: segment u % SEG of row u / SEG, u = stid + j ST (a row's SEG segments in
+    // consecutive lanes)
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
+      if constexpr (L2) {
+        float x[8];
+        cr.q[j].get(x);
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        const float rn = rnorm(ss, std::false_type());
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= rn;
+        store8_pk(s.Q + r * LDK + sg * 8, x);
+      } else {
+        store8_bf16_as_f16(s.Q + r * LDK + sg * 8, cr.q[j].u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int u = stid + j * ST, r = u / VSEG, sg = u % VSEG;
+      *reinterpret_cast<uint4 *>(s.V + r * LDV + sg * 8) = cr.v[j].u;
+    }
+  };
+  // Per-row decay factors of the chunk starting at row c (producer 0, from the gates
+  // it fetched): the inclusive prefix sum of the per-row decay in fp64 (a token's g
+  // sits on its first sub-step) and the factors derived from it; gates formed here
+  // from raw projections when asked.  Evaluated one phase before the chunk's staging
+  // writes them, where producer 0 has room.
+  auto scan = [&](const Regs64<Tr> &cr, int c) __attribute__((always_inline)) {
+    const bool ok = lane < min(CR, row_end - c);
+    float gv = cr.g;
+    float bv = cr.b;
+    if (p.gate_mode) {
+      gv = gate_decay(cr.g, gate_A, gate_dt);
+      bv = gate_beta(cr.b);
+    }
+    const double gr = prefix_sum64((ok && (c + lane) % NH == 0) ? gv : 0.0);
+    bv = ok ? bv : 0.0f;
+    const double glast = readlane_f64(gr, CR - 1);
+    Scan64 sc;
+    sc.g2 = static_cast<float>(gr) * 1.4426950408889634f;
+    sc.gb = sc.g2 + __builtin_amdgcn_logf(bv);   // log2(0) = -inf: beta 0 rows vanish
+    sc.eg = fexp(static_cast<float>(gr));
+    sc.egl = fexp(static_cast<float>(glast - gr));
+    sc.b = bv;
+    return sc;
+  };
+  // the exponent bases, which the producers read (stored as soon as evaluated: the
+  // buffer's previous chunk no longer needs them), and the factors the state waves read
+  // (stored at the chunk's staging)
+  auto put_bases = [&](const Scan64 &sc, Stage64<Tr> &s) __attribute__((always_inline)) {
+    s.G2[lane] = sc.g2;
+    s.GB[lane] = sc.gb;
+  };
+  auto put_factors = [&](const Scan64 &sc, Stage64<Tr> &s) __attribute__((always_inline)) {
+    s.eG[lane] = sc.eg;
+    s.eGl[lane] = sc.egl;
+    s.B[lane] = sc.b;
   };
 
   // Each role runs its own code (its registers stay out of the other's): the prologue's
@@ -608,26 +728,35 @@ prefill64_kernel(const PrefillParams p) {
       const frag af3b = M::load(v.A, LDA, 48 + l16, 32, lane);
       f32x4 D[2][4];
       frag d01[2];
+      // the operands of block mk + 1 are read while block mk's products run
+      frag kf[2][KS];
+      s16x4 vv[2][2];
+      float4 b4[2], e4[2];
+      auto load_k = [&](int mk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) kf[mk & 1][sl] = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          vv[mk & 1][ct] = read_tr(s.V, LDV, 16 * mk, 32 * wave + 16 * ct, lane);
+        b4[mk & 1] = *reinterpret_cast<const float4 *>(s.B + 16 * mk + 4 * g4);
+        e4[mk & 1] = *reinterpret_cast<const float4 *>(s.eG + 16 * mk + 4 * g4);
+      };
+      load_k(0);
 #pragma unroll
       for (int mk = 0; mk < 4; ++mk) {
-        frag kf[KS];
-#pragma unroll
-        for (int sl = 0; sl < KS; ++sl) kf[sl] = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
-        const int r0 = 16 * mk + 4 * g4;
-        const float4 b4 = *reinterpret_cast<const float4 *>(s.B + r0);
-        const float4 e4 = *reinterpret_cast<const float4 *>(s.eG + r0);
-        const float br[4] = {b4.x, b4.y, b4.z, b4.w};
-        const float er[4] = {e4.x, e4.y, e4.z, e4.w};
+        if (mk + 1 < 4) load_k(mk + 1);
+        const float br[4] = {b4[mk & 1].x, b4[mk & 1].y, b4[mk & 1].z, b4[mk & 1].w};
+        const float er[4] = {e4[mk & 1].x, e4[mk & 1].y, e4[mk & 1].z, e4[mk & 1].w};
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const s16x4 vv = read_tr(s.V, LDV, 16 * mk, 32 * wave + 16 * ct, lane);
           f32x4 x = zero4();
 #pragma unroll
-          for (int sl = 0; sl < KS; ++sl) x = M::mma(kf[sl], hb[ct][sl], x);
+          for (int sl = 0; sl < KS; ++sl) x = M::mma(kf[mk & 1][sl], hb[ct][sl], x);
           f32x4 rn;   // -R_b
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float vx = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(vv[i])) << 16);
+            const float vx =
+                __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(vv[mk & 1][ct][i])) << 16);
             rn[i] = br[i] * (er[i] * x[i] - vx);
           }
           if (mk == 0) {
@@ -664,48 +793,57 @@ prefill64_kernel(const PrefillParams p) {
 
       // ---- phase B: O and the state update ----------------------------------------
       // O^T = scale H0^T Q^T diag(exp G) + D^T P^T (P carries the scale): a lane holds
-      // output columns 4 g4 .. 4 g4 + 3 of token l16 of each query block
+      // output columns 4 g4 .. 4 g4 + 3 of token l16 of each query block.
+      float sx[NQB];
 #pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) {
-        frag qf[KS];
+      for (int mq = 0; mq < NQB; ++mq) sx[mq] = p.scale * s.eG[NH * (16 * mq + l16) + NH - 1];
+      // this chunk's output rows through a buffer resource whose range ends at the
+      // sequence's last token (no rows at all without outputs): stores to rows past it
+      // are dropped by the range check, with no branch around them
+      const int orows = ob ? min(CQ, t1 - tq0) : 0;
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          ob ? ob + static_cast<size_t>(tq0) * vstride : nullptr, 0,
+          orows * static_cast<int>(vstride * sizeof(TOut)), kBufferWord3);
+      // operand reads are issued one block ahead of the products that use them
+      frag qf[2][KS], pf[2][2];
+      auto load_qp = [&](int mq) __attribute__((always_inline)) {
+        const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;   // key slices reaching the block
 #pragma unroll
-        for (int sl = 0; sl < KS; ++sl) qf[sl] = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
-        // key slices (32 rows) reaching this query block's last row
-        const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;
-        frag pf[2];
+        for (int sl = 0; sl < KS; ++sl) qf[mq & 1][sl] = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
 #pragma unroll
         for (int sk = 0; sk < 2; ++sk)
-          if (sk < nsk) pf[sk] = M::load(v.P, LDA, 16 * mq + l16, 32 * sk, lane);
-        const float sx = p.scale * s.eG[NH * (16 * mq + l16) + NH - 1];
-        f32x4 xo[2], yo[2];
+          if (sk < nsk) pf[mq & 1][sk] = M::load(v.P, LDA, 16 * mq + l16, 32 * sk, lane);
+      };
+      load_qp(0);
+#pragma unroll
+      for (int mq = 0; mq < NQB; ++mq) {
+        if (mq + 1 < NQB) load_qp(mq + 1);
+        const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          xo[ct] = zero4();
+          f32x4 xo = zero4();
 #pragma unroll
-          for (int sl = 0; sl < KS; ++sl) xo[ct] = M::mma(hb[ct][sl], qf[sl], xo[ct]);
-          yo[ct] = M::mma(db[ct][0], pf[0], zero4());
-          if (nsk > 1) yo[ct] = M::mma(db[ct][1], pf[1], yo[ct]);
-        }
-        const int tok = tq0 + 16 * mq + l16;
-        if (p.out && tok < t1) {
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            float o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = sx * xo[ct][i] + yo[ct][i];
-            store4(ob + (static_cast<uint32_t>(tok) * vstride + 16 * ct + 4 * g4), o);
-          }
+          for (int sl = 0; sl < KS; ++sl) xo = M::mma(hb[ct][sl], qf[mq & 1][sl], xo);
+          f32x4 yo = M::mma(db[ct][0], pf[mq & 1][0], zero4());
+          if (nsk > 1) yo = M::mma(db[ct][1], pf[mq & 1][1], yo);
+          store4_rsrc<TOut>(orsrc, ((16 * mq + l16) * vstride + 16 * ct + 4 * g4) * sizeof(TOut),
+                            sx[mq] * xo + yo);
         }
       }
       // H <- exp(G_last) H0 + K^T diag(exp(G_last - G)) D
       const float dl = s.eG[CR - 1];
+      frag kt[2][2];
+      auto load_kt = [&](int m) __attribute__((always_inline)) {
+        kt[m & 1][0] = frag_tr(s.K, LDK, 0, 16 * m, lane);
+        kt[m & 1][1] = frag_tr(s.K, LDK, 32, 16 * m, lane);
+      };
+      load_kt(0);
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
-        const frag k0 = frag_tr(s.K, LDK, 0, 16 * m, lane);
-        const frag k1 = frag_tr(s.K, LDK, 32, 16 * m, lane);
+        if (m + 1 < KM) load_kt(m + 1);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-          H[ct][m] = M::mma(k1, dk[ct][1], M::mma(k0, dk[ct][0], H[ct][m] * dl));
+          H[ct][m] = M::mma(kt[m & 1][1], dk[ct][1], M::mma(kt[m & 1][0], dk[ct][0], H[ct][m] * dl));
       }
       // a boundary state after every bnd_rows rows (boundaries fall on chunk ends)
       if (bnd_rows && ((ci + 1) * CR) % bnd_rows == 0 && (ci + 1) * CR <= row_end - row_begin) {
@@ -722,28 +860,79 @@ prefill64_kernel(const PrefillParams p) {
     // prologue: chunk 0 staged and solved, chunk 1 fetched.  Interval ci: stage chunk
     // ci+1, then fetch chunk ci+2 into the same registers (phase A); solve chunk ci+1
     // (phase B).  The loads have the rest of the interval to land before their staging.
-    auto run = [&](auto l2c) __attribute__((always_inline)) {
+    // The decay scan of a chunk runs on producer 0 in the phase B two phases before the
+    // chunk's solve, and each producer forms its diagonal block of A from its staged K
+    // registers in the phase A before the solve, so that producer 0's share of the solve
+    // is the inversion, one off-diagonal block and the scan.
+    // Producer 0 runs its own copy of the loop (P0): its gate loads are then the only
+    // loads after the chunk inputs on its path, and the waits for those inputs count
+    // them exactly instead of waiting for every load.
+    auto run = [&](auto l2c, auto p0c) __attribute__((always_inline)) {
+      constexpr bool P0 = decltype(p0c)::value;
+      Scan64 sc{};   // producer 0: the decay factors of the next chunk to stage
       if (nchunks > 0) {
         fetch(rg, row_begin);
-        stage(rg, row_begin, sm.st[0], l2c);
+        if (P0) {
+          fetch_gates(rg, row_begin);
+          sc = scan(rg, row_begin);
+          put_bases(sc, sm.st[0]);
+          put_factors(sc, sm.st[0]);
+          if (nchunks > 1) fetch_gates(rg, row_begin + CR);
+        }
+        stage(rg, sm.st[0], l2c);
         if (nchunks > 1) fetch(rg, row_begin + CR);
       }
       __syncthreads();
-      if (nchunks > 0) p64_solve<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, p.scale, lane);
+      if (nchunks > 0) {
+        if (P0) p64_diag_lds<Tr>(sm.st[0], sm.AR, lane);
+        p64_solve<Tr>(sm.st[0], sm.sv[0], sm.AR, P0 ? 0 : pw, p.scale, lane);
+      }
+      if (P0 && nchunks > 1) {
+        sc = scan(rg, row_begin + CR);
+        put_bases(sc, sm.st[1]);
+        if (nchunks > 2) fetch_gates(rg, row_begin + 2 * CR);
+      }
       __syncthreads();
       for (int ci = 0; ci < nchunks; ++ci) {
         const bool next = ci + 1 < nchunks;
-        if (next) stage(rg, row_begin + (ci + 1) * CR, sm.st[(ci + 1) & 1], l2c);
-        if (ci + 2 < nchunks) fetch(rg, row_begin + (ci + 2) * CR);
+        if (next) {
+          Stage64<Tr> &sn = sm.st[(ci + 1) & 1];
+          // this producer's diagonal block K_pw K_pw^T of chunk ci + 1 is formed after
+          // the staging; its exponent bases (stored in the previous phase B) are read
+          // first
+          const DiagBases db = p64_diag_bases<Tr>(sn, pw, lane);
+          stage(rg, sn, l2c);
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int sl = 0; sl < KS; ++sl) acc = M::mma(kh[sl], kh[sl], acc);
+          if (P0) put_factors(sc, sn);
+          if (ci + 2 < nchunks) fetch(rg, row_begin + (ci + 2) * CR);
+          p64_diag_put<Tr>(db, acc, pw, sm.AR, lane);
+        }
         __syncthreads();
-        if (next) p64_solve<Tr>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
+        if (next)
+          p64_solve<Tr>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, P0 ? 0 : pw, p.scale, lane);
+        if (P0 && ci + 2 < nchunks) {
+          sc = scan(rg, row_begin + (ci + 2) * CR);
+          put_bases(sc, sm.st[ci & 1]);   // chunk ci + 2 takes chunk ci's buffer
+          // evaluated here, not next to their stores after the barrier
+          asm volatile("" : "+v"(sc.eg), "+v"(sc.egl), "+v"(sc.b));
+          if (ci + 3 < nchunks) fetch_gates(rg, row_begin + (ci + 3) * CR);
+        }
         __syncthreads();
       }
     };
-    if (p.l2norm)
-      run(std::true_type());
-    else
-      run(std::false_type());
+    if (pw == 0) {
+      if (p.l2norm)
+        run(std::true_type(), std::true_type());
+      else
+        run(std::false_type(), std::true_type());
+    } else {
+      if (p.l2norm)
+        run(std::true_type(), std::false_type());
+      else
+        run(std::false_type(), std::false_type());
+    }
   }
 }
 
