@@ -152,20 +152,21 @@ struct P64 {
   static constexpr int SEG = DK / 8;            // 8-element segments per K / Q row
   static constexpr int KPT = CR * SEG / ST;     // K segments per staging thread
   static constexpr int QPT = CQ * SEG / ST;
-  static constexpr int VSEG = DVT / 8;
-  static constexpr int VPT = CR * VSEG / ST;
-  static_assert(KPT * ST == CR * SEG && QPT * ST == CQ * SEG && VPT * ST == CR * VSEG,
-                "staging split");
-  static_assert(QPT >= 1 && VPT >= 1 && NQB >= 1, "staging split");
+  static_assert(KPT * ST == CR * SEG && QPT * ST == CQ * SEG, "staging split");
+  static_assert(QPT >= 1 && NQB >= 1, "staging split");
 };
 
 template <class Tr>
 struct alignas(16) Stage64 {
   _Float16 K[Tr::CR * Tr::LDK];
   _Float16 Q[Tr::CQ * Tr::LDK];
-  uint16_t V[Tr::CR * Tr::LDV];   // raw bf16
   float G2[Tr::CR];               // G_r log2(e): exponent base of the solve's columns
   float GB[Tr::CR];               // G_r log2(e) + log2(beta_r): base of A's rows
+};
+// the per-row factors the state waves read (a chunk's are written two phases before its
+// interval, and read through all of it: three buffers)
+template <class Tr>
+struct alignas(16) Fac64 {
   float eG[Tr::CR];               // exp(G_r)
   float eGl[Tr::CR];              // exp(G_last - G_r)
   float B[Tr::CR];                // beta
@@ -180,8 +181,13 @@ template <class Tr>
 struct Smem64 {
   Stage64<Tr> st[2];
   Solve64<Tr> sv[2];
+  Fac64<Tr> fac[3];
   float AR[4][Tr::ARB];
+  uint16_t V[Tr::CR * Tr::LDV];   // the chunk's values (raw bf16), 32 columns per state wave
 };
+
+// the producer wave that loads the gates and runs the per-chunk decay scan
+constexpr int kScanProducer = 1;
 
 struct Scan64 {
   float g2, gb, eg, egl, b;
@@ -189,7 +195,7 @@ struct Scan64 {
 
 template <class Tr>
 struct Regs64 {
-  Seg8<uint16_t> k[Tr::KPT], q[Tr::QPT], v[Tr::VPT];
+  Seg8<uint16_t> k[Tr::KPT], q[Tr::QPT];
   float g, b;     // gates of the chunk the decay scan reads next
 };
 
@@ -440,7 +446,6 @@ prefill64_kernel(const PrefillParams p) {
   constexpr int CR = Tr::CR, CQ = Tr::CQ, NQB = Tr::NQB, DVT = Tr::DVT, SEG = Tr::SEG;
   constexpr int LDK = Tr::LDK, LDV = Tr::LDV, LDA = Tr::LDA, LDT = Tr::LDT, NT = Tr::NT;
   constexpr int ST = Tr::ST, KS = Tr::KS, KM = Tr::KM, KPT = Tr::KPT, QPT = Tr::QPT;
-  constexpr int VPT = Tr::VPT, VSEG = Tr::VSEG;
 
   __shared__ Smem64<Tr> sm;
 
@@ -538,17 +543,6 @@ prefill64_kernel(const PrefillParams p) {
       const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
       cr.q[j].u = load16(rq, (r * kstride + sg * 8) * 2);
     }
-    if (vrow) {   // one uniform branch around all value loads
-      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vrow, c, nrow, vstride);
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int u = stid + j * ST, r = u / VSEG, sg = u % VSEG;
-        cr.v[j].u = load16(rv, (r * vstride + sg * 8) * 2);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) cr.v[j].zero();
-    }
   };
   // the gates of the chunk starting at row c (producer 0; requested a whole interval
   // before the decay scan reads them)
@@ -619,11 +613,6 @@ prefill64_kernel(const PrefillParams p) {
         store8_bf16_as_f16(s.Q + r * LDK + sg * 8, cr.q[j].u);
       }
     }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int u = stid + j * ST, r = u / VSEG, sg = u % VSEG;
-      *reinterpret_cast<uint4 *>(s.V + r * LDV + sg * 8) = cr.v[j].u;
-    }
   };
   // Per-row decay factors of the chunk starting at row c (producer 0, from the gates
   // it fetched): the inclusive prefix sum of the per-row decay in fp64 (a token's g
@@ -649,17 +638,17 @@ prefill64_kernel(const PrefillParams p) {
     sc.b = bv;
     return sc;
   };
-  // the exponent bases, which the producers read (stored as soon as evaluated: the
-  // buffer's previous chunk no longer needs them), and the factors the state waves read
-  // (stored at the chunk's staging)
+  // the exponent bases, which the producers read (into the chunk's stage buffer, whose
+  // previous chunk no longer needs them), and the factors the state waves read (into
+  // the chunk's factor buffer); both stored as soon as evaluated
   auto put_bases = [&](const Scan64 &sc, Stage64<Tr> &s) __attribute__((always_inline)) {
     s.G2[lane] = sc.g2;
     s.GB[lane] = sc.gb;
   };
-  auto put_factors = [&](const Scan64 &sc, Stage64<Tr> &s) __attribute__((always_inline)) {
-    s.eG[lane] = sc.eg;
-    s.eGl[lane] = sc.egl;
-    s.B[lane] = sc.b;
+  auto put_factors = [&](const Scan64 &sc, Fac64<Tr> &f) __attribute__((always_inline)) {
+    f.eG[lane] = sc.eg;
+    f.eGl[lane] = sc.egl;
+    f.B[lane] = sc.b;
   };
 
   // Each role runs its own code (its registers stay out of the other's): the prologue's
@@ -696,6 +685,32 @@ prefill64_kernel(const PrefillParams p) {
           }
     };
 
+    // The chunk's values: each state wave brings in its own 32 columns (rows
+    // 16 j + lane / 4, columns 8 (lane % 4) .. + 7 of its tile) through a resource that
+    // ends at the sequence's last row (rows past it read as zero; no values: all zero).
+    // They are only ever read by the wave that wrote them, so one LDS buffer serves:
+    // a chunk's values are written in the phase B before its interval, after the wave's
+    // reads of the previous chunk's, from registers loaded an interval earlier.
+    // (Branch-free: without values, and past the sequence's end, the resource holds no
+    // rows and the loads return zeros.)
+    uint4 vr[4];
+    auto load_v = [&](int c) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rv =
+          rows_rsrc(vrow ? vrow + 32 * wave : kb, c, vrow ? min(CR, row_end - c) : 0, vstride);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vr[j] = load16(rv, ((16 * j + (lane >> 2)) * vstride + 8 * (lane & 3)) * 2);
+    };
+    auto put_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4 *>(sm.V + (16 * j + (lane >> 2)) * LDV + 32 * wave +
+                                   8 * (lane & 3)) = vr[j];
+    };
+    load_v(row_begin);
+    put_v();
+    load_v(row_begin + CR);
+
     // the initial state has landed before the pipeline starts
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // prologue: producers stage chunk 0
@@ -704,6 +719,7 @@ prefill64_kernel(const PrefillParams p) {
       const int c0 = row_begin + ci * CR;
       const Stage64<Tr> &s = sm.st[ci & 1];
       const Solve64<Tr> &v = sm.sv[ci & 1];
+      const Fac64<Tr> &f = sm.fac[ci % 3];
       const int tq0 = c0 / NH;
 
       // ---- phase A: X = K H0, R, D ----------------------------------------------
@@ -737,9 +753,9 @@ prefill64_kernel(const PrefillParams p) {
         for (int sl = 0; sl < KS; ++sl) kf[mk & 1][sl] = M::load(s.K, LDK, 16 * mk + l16, 32 * sl, lane);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-          vv[mk & 1][ct] = read_tr(s.V, LDV, 16 * mk, 32 * wave + 16 * ct, lane);
-        b4[mk & 1] = *reinterpret_cast<const float4 *>(s.B + 16 * mk + 4 * g4);
-        e4[mk & 1] = *reinterpret_cast<const float4 *>(s.eG + 16 * mk + 4 * g4);
+          vv[mk & 1][ct] = read_tr(sm.V, LDV, 16 * mk, 32 * wave + 16 * ct, lane);
+        b4[mk & 1] = *reinterpret_cast<const float4 *>(f.B + 16 * mk + 4 * g4);
+        e4[mk & 1] = *reinterpret_cast<const float4 *>(f.eG + 16 * mk + 4 * g4);
       };
       load_k(0);
 #pragma unroll
@@ -779,8 +795,8 @@ prefill64_kernel(const PrefillParams p) {
       frag db[2][2], dk[2][2];
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
-        const float4 l0 = *reinterpret_cast<const float4 *>(s.eGl + 32 * sk + 4 * g4);
-        const float4 l1 = *reinterpret_cast<const float4 *>(s.eGl + 32 * sk + 16 + 4 * g4);
+        const float4 l0 = *reinterpret_cast<const float4 *>(f.eGl + 32 * sk + 4 * g4);
+        const float4 l1 = *reinterpret_cast<const float4 *>(f.eGl + 32 * sk + 16 + 4 * g4);
         const f32x4 e0 = {l0.x, l0.y, l0.z, l0.w};
         const f32x4 e1 = {l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
@@ -792,11 +808,15 @@ prefill64_kernel(const PrefillParams p) {
       __syncthreads();
 
       // ---- phase B: O and the state update ----------------------------------------
+      // (first, the next chunk's values replace this chunk's, which this wave has read,
+      // and the one after is requested)
+      put_v();
+      load_v(c0 + 2 * CR);
       // O^T = scale H0^T Q^T diag(exp G) + D^T P^T (P carries the scale): a lane holds
       // output columns 4 g4 .. 4 g4 + 3 of token l16 of each query block.
       float sx[NQB];
 #pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) sx[mq] = p.scale * s.eG[NH * (16 * mq + l16) + NH - 1];
+      for (int mq = 0; mq < NQB; ++mq) sx[mq] = p.scale * f.eG[NH * (16 * mq + l16) + NH - 1];
       // this chunk's output rows through a buffer resource whose range ends at the
       // sequence's last token (no rows at all without outputs): stores to rows past it
       // are dropped by the range check, with no branch around them
@@ -831,7 +851,7 @@ prefill64_kernel(const PrefillParams p) {
         }
       }
       // H <- exp(G_last) H0 + K^T diag(exp(G_last - G)) D
-      const float dl = s.eG[CR - 1];
+      const float dl = f.eG[CR - 1];
       frag kt[2][2];
       auto load_kt = [&](int m) __attribute__((always_inline)) {
         kt[m & 1][0] = frag_tr(s.K, LDK, 0, 16 * m, lane);
@@ -864,19 +884,19 @@ prefill64_kernel(const PrefillParams p) {
     // chunk's solve, and each producer forms its diagonal block of A from its staged K
     // registers in the phase A before the solve, so that producer 0's share of the solve
     // is the inversion, one off-diagonal block and the scan.
-    // Producer 0 runs its own copy of the loop (P0): its gate loads are then the only
-    // loads after the chunk inputs on its path, and the waits for those inputs count
-    // them exactly instead of waiting for every load.
-    auto run = [&](auto l2c, auto p0c) __attribute__((always_inline)) {
-      constexpr bool P0 = decltype(p0c)::value;
-      Scan64 sc{};   // producer 0: the decay factors of the next chunk to stage
+    // The producer that runs the decay scan (SCAN) has its own copy of the loop: its
+    // gate loads are then the only loads after the chunk inputs on its path, and the
+    // waits for those inputs count them exactly instead of waiting for every load.
+    auto run = [&](auto l2c, auto scanc) __attribute__((always_inline)) {
+      constexpr bool SCAN = decltype(scanc)::value;
+      Scan64 sc{};   // the scan producer: the decay factors of one chunk
       if (nchunks > 0) {
         fetch(rg, row_begin);
-        if (P0) {
+        if (SCAN) {
           fetch_gates(rg, row_begin);
           sc = scan(rg, row_begin);
           put_bases(sc, sm.st[0]);
-          put_factors(sc, sm.st[0]);
+          put_factors(sc, sm.fac[0]);
           if (nchunks > 1) fetch_gates(rg, row_begin + CR);
         }
         stage(rg, sm.st[0], l2c);
@@ -884,12 +904,13 @@ prefill64_kernel(const PrefillParams p) {
       }
       __syncthreads();
       if (nchunks > 0) {
-        if (P0) p64_diag_lds<Tr>(sm.st[0], sm.AR, lane);
-        p64_solve<Tr>(sm.st[0], sm.sv[0], sm.AR, P0 ? 0 : pw, p.scale, lane);
+        if (pw == 0) p64_diag_lds<Tr>(sm.st[0], sm.AR, lane);
+        p64_solve<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, p.scale, lane);
       }
-      if (P0 && nchunks > 1) {
+      if (SCAN && nchunks > 1) {
         sc = scan(rg, row_begin + CR);
         put_bases(sc, sm.st[1]);
+        put_factors(sc, sm.fac[1]);
         if (nchunks > 2) fetch_gates(rg, row_begin + 2 * CR);
       }
       __syncthreads();
@@ -905,24 +926,22 @@ prefill64_kernel(const PrefillParams p) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int sl = 0; sl < KS; ++sl) acc = M::mma(kh[sl], kh[sl], acc);
-          if (P0) put_factors(sc, sn);
           if (ci + 2 < nchunks) fetch(rg, row_begin + (ci + 2) * CR);
           p64_diag_put<Tr>(db, acc, pw, sm.AR, lane);
         }
         __syncthreads();
         if (next)
-          p64_solve<Tr>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, P0 ? 0 : pw, p.scale, lane);
-        if (P0 && ci + 2 < nchunks) {
+          p64_solve<Tr>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
+        if (SCAN && ci + 2 < nchunks) {
           sc = scan(rg, row_begin + (ci + 2) * CR);
           put_bases(sc, sm.st[ci & 1]);   // chunk ci + 2 takes chunk ci's buffer
-          // evaluated here, not next to their stores after the barrier
-          asm volatile("" : "+v"(sc.eg), "+v"(sc.egl), "+v"(sc.b));
+          put_factors(sc, sm.fac[(ci + 2) % 3]);
           if (ci + 3 < nchunks) fetch_gates(rg, row_begin + (ci + 3) * CR);
         }
         __syncthreads();
       }
     };
-    if (pw == 0) {
+    if (pw == kScanProducer) {
       if (p.l2norm)
         run(std::true_type(), std::true_type());
       else
