@@ -187,7 +187,7 @@ struct Smem64 {
 };
 
 // the producer wave that loads the gates and runs the per-chunk decay scan
-constexpr int kScanProducer = 1;
+constexpr int kScanProducer = 0;
 
 struct Scan64 {
   float g2, gb, eg, egl, b;

@@ -221,3 +221,56 @@ def test_packed_segments_deterministic():
     assert _packed_segments_used(wl)
     a, b = _packed_run(wl, True), _packed_run(wl, True)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("entry", ["workspace", "noalloc"])
+def test_packed_segments_graph_replay(entry):
+    """The packed segment path (device plan, three passes, combine) captured in a HIP
+    graph replays to the eager result every time, the slot cache carried from call
+    to call; with a caller workspace, and on the allocation-free entry's scratch."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    wl = W.prefill_packed("seg_graph", 49, [12000, 5000], 2, 4, 128, 128, W.BF16, 64,
+                          decay="slow", num_slots=4, slot_init="random")
+    assert _packed_segments_used(wl)
+    dev = [to_dev(getattr(wl, n)) for n in ("q", "k", "v", "g", "beta")]
+    cu, idx = to_dev(wl.cu_seqlens), to_dev(wl.state_indices)
+    cache0 = to_dev(wl.initial_state)
+    out = torch.empty(wl.q.shape[:2] + wl.v.shape[-2:], dtype=torch.bfloat16, device="cuda")
+    probe = gdr.prefill_args(*dev, cu_seqlens=cu, state_indices=idx, initial_state=cache0,
+                             out=out)
+    ws = torch.empty(int(gdr.library().gdr_prefill_workspace_bytes(probe)), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(cache):
+        if entry == "workspace":
+            gdr.chunk_gated_delta_rule(*dev, initial_state=cache, cu_seqlens=cu,
+                                       state_indices=idx, out=out, workspace=ws)
+        else:
+            gdr.chunk_gated_delta_rule_noalloc(*dev, out=out, initial_state=cache,
+                                               final_state=cache, cu_seqlens=cu,
+                                               state_indices=idx)
+
+    eager_c = cache0.clone()
+    eager = []
+    for _ in range(3):
+        call(eager_c)
+        eager.append((out.clone(), eager_c.clone()))
+    torch.cuda.synchronize()
+    graph_c = cache0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(graph_c.clone())
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(graph_c)
+    torch.cuda.synchronize()
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[step][0]), f"replay {step}: outputs differ"
+        assert torch.equal(graph_c, eager[step][1]), f"replay {step}: slot cache differs"
+        _ = torch.ones(1, device="cuda").sum().item()
+    print(f"packed segments in a graph ({entry}): 3 replays bitwise", flush=True)
