@@ -33,12 +33,20 @@
 // sequence) and four producer waves.  Each chunk interval has two phases separated
 // by workgroup barriers:
 //   phase A: state waves  X = K H0, R and D of chunk i;
-//            producers    fetch chunk i+2 into registers, stage chunk i+1 into LDS;
-//   phase B: state waves  O and the state update of chunk i;
-//            producers    solve chunk i+1: diagonal blocks and their inverses
-//                         (wave 0), off-diagonal blocks of A (wave 1), the causal
-//                         tiles of P = scale (Q K^T * Gamma) (waves 2 and 3).
-// Staged chunks and solved operands are double-buffered in LDS.
+//            producers    stage chunk i+1 (K in the layout of an operand of the
+//                         producer's own 16-row block, whose diagonal block of A each
+//                         producer then forms from registers), fetch chunk i+2;
+//   phase B: state waves  O and the state update of chunk i; the next chunk's
+//                         values into the wave's own LDS columns;
+//            producers    solve chunk i+1: the inverses of the diagonal blocks, A_32
+//                         and the decay scan of chunk i+2 (wave 0), the other
+//                         off-diagonal blocks of A (wave 1), the causal tiles of
+//                         P = scale (Q K^T * Gamma) (waves 2 and 3).
+// Staged chunks and solved operands are double-buffered in LDS, the per-row decay
+// factors triple-buffered (written two phases before their interval), the values
+// single-buffered (each state wave reads only the columns it wrote).  Inputs and
+// outputs go through range-checked buffer resources that end at the sequence's last
+// row: rows past it read as zero and are never written, with no clamps or branches.
 
 #include "chunk_helpers.hpp"
 #include "common.hpp"
