@@ -184,6 +184,34 @@ __device__ __forceinline__ void mmf3(f32x4 (&acc1)[TPW], f32x4 (&acc2)[TPW], f32
   });
 }
 
+// fp16 matrix-core products of the form acc_j[t] += X_j Y^T over k in [0, K), both
+// row-major fp16 in LDS with k contiguous (leading dimensions ldx, ldy halves, rows
+// 16-byte aligned): tile t of wave tile w covers rows r0 .. r0 + 15 of X_j and rows
+// c0 + 16 t .. + 15 of Y.  v_mfma_f32_16x16x32_f16: lane l supplies row l % 16 of X_j
+// and of Y with contraction indices 8 (l / 16) .. + 7, one 16-byte read each, and its
+// accumulator layout is that of the fp32 products above.
+template <int NA, int N, int TPW>
+__device__ __forceinline__ void mmh_xyt(f32x4 *const (&acc)[NA], const WTile<N, TPW> &w,
+                                        const _Float16 *const (&X)[NA], int ldx,
+                                        const _Float16 *Y, int ldy, int K, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f16x8 a[NA], b[TPW];
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      a[j] = *reinterpret_cast<const f16x8 *>(X[j] + (w.r0 + i) * ldx + k0 + 8 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      b[t] = *reinterpret_cast<const f16x8 *>(Y + (w.c0 + 16 * t + i) * ldy + k0 + 8 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int j = 0; j < NA; ++j)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b[t], acc[j][t], 0, 0, 0);
+  }
+}
+
 template <int TPW>
 __device__ __forceinline__ void zero(f32x4 (&acc)[TPW]) {
 #pragma unroll
@@ -294,6 +322,24 @@ struct RowsRegs {
       }
     }
   }
+  // the same rows as fp16 (one 16-byte store per segment)
+  __device__ __forceinline__ void store_h(_Float16 *dst, int ld, int rows, int tid, int ts = 0,
+                                          int nh = 1) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      const int r = u / SEGS, sg = u % SEGS;
+      if (UNITS % BT == 0 || u < UNITS) {
+        const bool ok = r < rows && (nh == 1 || (ts + r) % nh == nh - 1);
+        float x[8];
+        buf[j].get(x);
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(ok ? x[e] : 0.0f);
+        *reinterpret_cast<f16x8 *>(dst + r * ld + 8 * sg) = h;
+      }
+    }
+  }
 };
 
 template <typename TIn, int D, int NC>
@@ -331,6 +377,51 @@ struct MatRegs {
         d[3] = buf[j].w;
       }
     }
+  }
+  // the same matrix as fp16 (one 8-byte store per four values)
+  __device__ __forceinline__ void store_h(_Float16 *dst, int ld, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      if (UNITS % BT == 0 || u < UNITS) {
+        f16x4 h = {static_cast<_Float16>(buf[j].x), static_cast<_Float16>(buf[j].y),
+                   static_cast<_Float16>(buf[j].z), static_cast<_Float16>(buf[j].w)};
+        *reinterpret_cast<f16x4 *>(dst + (u / Q4) * ld + 4 * (u % Q4)) = h;
+      }
+    }
+  }
+  // as an fp16 pair hi + lo (lo = the rounding error of hi, in fp16): two products
+  // with the pair carry ~22 bits of the fp32 value instead of 11
+  __device__ __forceinline__ void store_hl(_Float16 *hi, _Float16 *lo, int ld, int tid) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = tid + j * BT;
+      if (UNITS % BT == 0 || u < UNITS) {
+        const float x[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
+        f16x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = static_cast<_Float16>(x[e]);
+          b[e] = static_cast<_Float16>(x[e] - static_cast<float>(a[e]));
+        }
+        const int off = (u / Q4) * ld + 4 * (u % Q4);
+        *reinterpret_cast<f16x4 *>(hi + off) = a;
+        *reinterpret_cast<f16x4 *>(lo + off) = b;
+      }
+    }
+  }
+  // sum over this thread's values of the elementwise product with another matrix held
+  // the same way
+  __device__ __forceinline__ float dot(const MatRegs &o) const {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      s = fmaf(buf[j].x, o.buf[j].x, s);
+      s = fmaf(buf[j].y, o.buf[j].y, s);
+      s = fmaf(buf[j].z, o.buf[j].z, s);
+      s = fmaf(buf[j].w, o.buf[j].w, s);
+    }
+    return s;
   }
 };
 
@@ -708,10 +799,15 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   constexpr int HALVES = NW / (BC / 16);            // waves sharing one tile row of 64 x D
   static_assert(BT == 8 * BC, "row sums and dots: eight threads per row");
   // phase 1 and phases 2-3 share one LDS arena
-  constexpr int P1 = 4 * BC * LDV + 2 * D * LDV;
+  // bf16 inputs run phase 1's products on the fp16 matrix cores (float32 inputs keep
+  // the fp32 ones, whose 1e-5 bound fp16 operands would not meet)
+  constexpr bool H16 = sizeof(TIn) == 2;
+  constexpr int LDH = 40;   // fp16 slice rows: 16-byte reads on 16 rows, conflict-free
+  constexpr int P1 = H16 ? (5 * BC * LDH + 4 * D * LDH) / 2 + 2 * BC * LDV
+                         : 4 * BC * LDV + 2 * D * LDV;
   constexpr int P23 = 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
   constexpr int ARENA = P1 > P23 ? P1 : P23;
-  __shared__ float arena[ARENA];
+  __shared__ __align__(16) float arena[ARENA];
   __shared__ RowFactors rf;
   __shared__ float srow[3][BC];         // row sums of E + F, column sums of E + F, row sums of dA * Araw
   __shared__ float sdot[3][HALVES][BC]; // q.U1, k.Ua, k.Ub per row, one partial per wave of a tile row
@@ -751,6 +847,91 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   constexpr bool kPreKQ = sizeof(TQK) == 2 || D <= 64;
   RowsRegs<TQK, D, D> fk, fq;
   float ar[TPC][4], pv[TPC][4];
+  if constexpr (H16) {
+    // bf16 inputs: the slices as fp16 for the matrix cores (k contiguous in every
+    // operand), dR and V also as fp32 for the row dots, <dH_n, H0> from the fp32
+    // registers before they are refilled
+    _Float16 *hD = reinterpret_cast<_Float16 *>(arena), *hR = hD + BC * LDH, *hO = hR + BC * LDH;
+    _Float16 *hDl = hO + BC * LDH, *hRl = hDl + BC * LDH;   // low parts of D and dR
+    _Float16 *hH = hRl + BC * LDH, *hG = hH + D * LDH;
+    _Float16 *hHl = hG + D * LDH, *hGl = hHl + D * LDH;     // low parts of the states
+    float *sRb = reinterpret_cast<float *>(hGl + D * LDH), *svb = sRb + BC * LDV;
+    MatRegs<BC, 32> fD, fR;
+    RowsRegs<TIn, D, 32> fO, fV;
+    MatRegs<D, 32> fH, fG;
+    auto fetch = [&](int vb) {
+      fD.fetch(dm + vb, D, tid);
+      fR.fetch(drm + vb, D, tid);
+      fO.fetch(static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, tid, p.nh);
+      fV.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
+      fH.fetch(h0 ? h0 + vb : nullptr, D, tid);
+      fG.fetch(dhn + vb, D, tid);
+    };
+    fetch(0);
+    for (int vb = 0; vb < D; vb += 32) {
+      __syncthreads();
+      fD.store_hl(hD, hDl, LDH, tid);
+      fR.store_hl(hR, hRl, LDH, tid);
+      fR.store(sRb, LDV, tid);
+      fO.store_h(hO, LDH, rows, tid, ts, p.nh);
+      fV.store(svb, LDV, rows, tid);
+      fH.store_hl(hH, hHl, LDH, tid);
+      fG.store_hl(hG, hGl, LDH, tid);
+      hh += fH.dot(fG);
+      if (vb + 32 < D) {
+        fetch(vb + 32);
+      } else {
+        if constexpr (kPreKQ) {
+          fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+          fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+        }
+        const float *araw = p.araw + cc * BC * BC;
+        const float *pm = p.pmat + cc * BC * BC;
+#pragma unroll
+        for (int t = 0; t < TPC; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = wc.row(v, lane), q = wc.col(t, lane);
+            ar[t][v] = araw[r * BC + q];
+            pv[t][v] = pm[r * BC + q];
+          }
+      }
+      __syncthreads();
+      // x y with x = xh + xl, y = yh + yl (dO is exact in fp16): xh yh + xh yl + xl yh
+      {
+        f32x4 *const acc[2] = {dA, dP};
+        const _Float16 *const X[2] = {hR, hO};
+        mmh_xyt<2>(acc, wc, X, LDH, hD, LDH, 32, lane);
+        mmh_xyt<2>(acc, wc, X, LDH, hDl, LDH, 32, lane);
+        f32x4 *const acc1[1] = {dA};
+        const _Float16 *const X1[1] = {hRl};
+        mmh_xyt<1>(acc1, wc, X1, LDH, hD, LDH, 32, lane);
+      }
+      {
+        f32x4 *const acc[2] = {U1, Ua};
+        const _Float16 *const X[2] = {hO, hR};
+        mmh_xyt<2>(acc, wd, X, LDH, hH, LDH, 32, lane);
+        mmh_xyt<2>(acc, wd, X, LDH, hHl, LDH, 32, lane);
+        f32x4 *const acc1[1] = {Ua};
+        const _Float16 *const X1[1] = {hRl};
+        mmh_xyt<1>(acc1, wd, X1, LDH, hH, LDH, 32, lane);
+      }
+      {
+        f32x4 *const acc[1] = {Ub};
+        const _Float16 *const X[1] = {hD};
+        mmh_xyt<1>(acc, wd, X, LDH, hG, LDH, 32, lane);
+        mmh_xyt<1>(acc, wd, X, LDH, hGl, LDH, 32, lane);
+        const _Float16 *const X1[1] = {hDl};
+        mmh_xyt<1>(acc, wd, X1, LDH, hG, LDH, 32, lane);
+      }
+      {
+        // dR . v of row tid / 8, this thread's 4 columns of the slice
+        const int r = tid >> 3, q0 = 4 * (tid & 7);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv = fmaf(sRb[r * LDV + q0 + e], svb[r * LDV + q0 + e], rv);
+      }
+    }
+  } else
   {
     float *sDb = arena, *sRb = sDb + BC * LDV, *sOb = sRb + BC * LDV, *svb = sOb + BC * LDV;
     float *sHb = svb + BC * LDV, *sGb = sHb + D * LDV;
