@@ -37,6 +37,7 @@
 // operands in LDS; the cumulative decay is summed in fp64 so that differences of
 // large sums stay exact.
 
+#include "chunk_helpers.hpp"
 #include "common.hpp"
 #include "gdr_internal.hpp"
 
@@ -805,7 +806,13 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   constexpr int LDH = 40;   // fp16 slice rows: 16-byte reads on 16 rows, conflict-free
   constexpr int P1 = H16 ? (5 * BC * LDH + 4 * D * LDH) / 2 + 2 * BC * LDV
                          : 4 * BC * LDV + 2 * D * LDV;
-  constexpr int P23 = 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
+  // phase 3 on the fp16 matrix cores too when q and k are bf16 (exact in fp16): dAs and
+  // dPs as fp16 hi/lo pairs
+  constexpr bool H16Q = H16 && sizeof(TQK) == 2;
+  constexpr int LDS64 = BC + 8;   // fp16 64 x 64 rows: conflict-free 8-byte and transposed reads
+  constexpr int LDKH = D + 8;     // fp16 K, Q rows
+  constexpr int P23 = H16Q ? (4 * BC * LDS64 + 2 * BC * LDKH) / 2 + 2 * BC * LDC
+                           : 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
   constexpr int ARENA = P1 > P23 ? P1 : P23;
   __shared__ __align__(16) float arena[ARENA];
   __shared__ RowFactors rf;
@@ -998,6 +1005,20 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 
   float *sdAs = arena, *sdPs = sdAs + BC * LDG, *sM1 = sdPs + BC * LDG, *sM2 = sM1 + BC * LDC;
   float *sK = sM2 + BC * LDC, *sQ = sK + BC * LDD;
+  // the fp16 layout of the same arena
+  _Float16 *hA = reinterpret_cast<_Float16 *>(arena), *hAl = hA + BC * LDS64;
+  _Float16 *hP = hAl + BC * LDS64, *hPl = hP + BC * LDS64;
+  _Float16 *hK = hPl + BC * LDS64, *hQ = hK + BC * LDKH;
+  if constexpr (H16Q) {
+    sM1 = reinterpret_cast<float *>(hQ + BC * LDKH);
+    sM2 = sM1 + BC * LDC;
+  }
+  // x -> fp16 hi, lo with hi + lo carrying ~22 bits of x
+  auto put_hl = [](_Float16 *hi, _Float16 *lo, int i, float x) {
+    const _Float16 a = static_cast<_Float16>(x);
+    hi[i] = a;
+    lo[i] = static_cast<_Float16>(x - static_cast<float>(a));
+  };
 #pragma unroll
   for (int t = 0; t < TPC; ++t)
 #pragma unroll
@@ -1006,12 +1027,20 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
       const float a = q < r ? -dA[t][v] : 0.0f;
       const float pp = q <= r ? dP[t][v] : 0.0f;
-      sdAs[r * LDG + q] = a * rf.beta[r] * gam;
-      sdPs[r * LDG + q] = p.scale * pp * gam;
+      if constexpr (H16Q) {
+        put_hl(hA, hAl, r * LDS64 + q, a * rf.beta[r] * gam);
+        put_hl(hP, hPl, r * LDS64 + q, p.scale * pp * gam);
+      } else {
+        sdAs[r * LDG + q] = a * rf.beta[r] * gam;
+        sdPs[r * LDG + q] = p.scale * pp * gam;
+      }
       sM1[r * LDC + q] = a * rf.beta[r] * ar[t][v] + pp * pv[t][v];
       sM2[r * LDC + q] = a * ar[t][v];
     }
-  if constexpr (kPreKQ) {
+  if constexpr (H16Q) {
+    fk.store_h(hK, LDKH, rows, tid);
+    fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
+  } else if constexpr (kPreKQ) {
     fk.store(sK, LDD, rows, tid);
     fq.store(sQ, LDD, rows, tid, ts, p.nh);
   } else {
@@ -1061,9 +1090,17 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
 #pragma unroll
     for (int t = 0; t < TPD; ++t) {
       const int col = wd.col(t, lane);
-      s1 = fmaf(sQ[r * LDD + col], U1[t][v], s1);
-      s2 = fmaf(sK[r * LDD + col], Ua[t][v], s2);
-      s3 = fmaf(sK[r * LDD + col], Ub[t][v], s3);
+      float qv, kv;
+      if constexpr (H16Q) {
+        qv = static_cast<float>(hQ[r * LDKH + col]);
+        kv = static_cast<float>(hK[r * LDKH + col]);
+      } else {
+        qv = sQ[r * LDD + col];
+        kv = sK[r * LDD + col];
+      }
+      s1 = fmaf(qv, U1[t][v], s1);
+      s2 = fmaf(kv, Ua[t][v], s2);
+      s3 = fmaf(kv, Ub[t][v], s3);
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) {
@@ -1084,8 +1121,35 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   f32x4 dq[TPD], dk[TPD];
   zero(dq);
   zero(dk);
-  mmf3(dq, dk, dk, wd, sdPs, LDG, 1, sdAs, LDG, 1, sdAs, 1, LDG, sK, LDD, 1, BC, lane);
-  mmf(dk, wd, sdPs, 1, LDG, sQ, LDD, 1, BC, lane);
+  if constexpr (H16Q) {
+    // A fragments of dPs, dAs (this wave's rows) and of dAs^T, dPs^T (transposed reads),
+    // B fragments of K, Q (transposed reads), 32 chunk rows per step
+    using M = Mma<false>;
+    const int i = lane & 15;
+#pragma unroll
+    for (int k0 = 0; k0 < BC; k0 += 32) {
+      const M::frag aP = M::load(hP, LDS64, wd.r0 + i, k0, lane);
+      const M::frag aPl = M::load(hPl, LDS64, wd.r0 + i, k0, lane);
+      const M::frag aA = M::load(hA, LDS64, wd.r0 + i, k0, lane);
+      const M::frag aAl = M::load(hAl, LDS64, wd.r0 + i, k0, lane);
+      const M::frag tA = frag_tr(hA, LDS64, k0, wd.r0, lane);
+      const M::frag tAl = frag_tr(hAl, LDS64, k0, wd.r0, lane);
+      const M::frag tP = frag_tr(hP, LDS64, k0, wd.r0, lane);
+      const M::frag tPl = frag_tr(hPl, LDS64, k0, wd.r0, lane);
+#pragma unroll
+      for (int t = 0; t < TPD; ++t) {
+        const M::frag bK = frag_tr(hK, LDKH, k0, wd.c0 + 16 * t, lane);
+        const M::frag bQ = frag_tr(hQ, LDKH, k0, wd.c0 + 16 * t, lane);
+        dq[t] = M::mma(aPl, bK, M::mma(aP, bK, dq[t]));
+        dk[t] = M::mma(aAl, bK, M::mma(aA, bK, dk[t]));
+        dk[t] = M::mma(tAl, bK, M::mma(tA, bK, dk[t]));
+        dk[t] = M::mma(tPl, bQ, M::mma(tP, bQ, dk[t]));
+      }
+    }
+  } else {
+    mmf3(dq, dk, dk, wd, sdPs, LDG, 1, sdAs, LDG, 1, sdAs, 1, LDG, sK, LDD, 1, BC, lane);
+    mmf(dk, wd, sdPs, 1, LDG, sQ, LDD, 1, BC, lane);
+  }
   {
     float *dst;
     size_t rs;

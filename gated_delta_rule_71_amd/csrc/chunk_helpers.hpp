@@ -1,5 +1,6 @@
-// Device helpers shared by the chunked prefill kernels (gfx950): the hardware
-// exponential, fp64 lane scans over DPP, and 4-element loads and stores.
+// Device helpers shared by the chunked prefill and backward kernels (gfx950): the
+// hardware exponential, fp64 lane scans over DPP, 4-element loads and stores, and
+// the LDS transpose read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,6 +9,31 @@
 #include "common.hpp"
 
 namespace gdr {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Lane j of 16-lane group g receives M[r0 + 4g + e][c0 + j], e = 0..3, of a row-major
+// 16-bit matrix M in LDS (leading dimension ld elements): the gfx950 LDS transpose
+// load, each lane s of the group naming the 8 bytes at row r0 + 4g + s/4, column
+// c0 + 4 (s % 4).
+template <typename T>
+__device__ __forceinline__ s16x4 read_tr(const T *base, int ld, int r0, int c0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const T *p = base + (r0 + 4 * g + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+}
+
+// B fragment of a row-major fp16 matrix M (rows = contraction index k0 .. k0+31,
+// columns n0 .. n0+15), equivalently the A fragment of M^T: two transposed reads.
+__device__ __forceinline__ Mma<false>::frag frag_tr(const _Float16 *base, int ld, int k0, int n0,
+                                                   int lane) {
+  const s16x4 lo = read_tr(base, ld, k0, n0, lane);
+  const s16x4 hi = read_tr(base, ld, k0 + 16, n0, lane);
+  Mma<false>::frag f;
+  f.v = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
 
 // exp(x) on the hardware base-2 exponential
 __device__ __forceinline__ float fexp(float x) {

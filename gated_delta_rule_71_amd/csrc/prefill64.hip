@@ -54,7 +54,6 @@
 
 namespace gdr {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -113,27 +112,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// Lane j of 16-lane group g receives M[r0 + 4g + e][c0 + j], e = 0..3, of a row-major
-// 16-bit matrix M in LDS (leading dimension ld elements).
-template <typename T>
-__device__ __forceinline__ s16x4 read_tr(const T *base, int ld, int r0, int c0, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const T *p = base + (r0 + 4 * g + (s >> 2)) * ld + c0 + 4 * (s & 3);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p));
-}
-
-// B fragment of a row-major fp16 matrix M (rows = contraction index k0 .. k0+31,
-// columns n0 .. n0+15), equivalently the A fragment of M^T: two transposed reads.
-__device__ __forceinline__ Mma<false>::frag frag_tr(const _Float16 *base, int ld, int k0, int n0,
-                                                   int lane) {
-  const s16x4 lo = read_tr(base, ld, k0, n0, lane);
-  const s16x4 hi = read_tr(base, ld, k0 + 16, n0, lane);
-  Mma<false>::frag f;
-  f.v = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  return f;
 }
 
 template <int DK_, int NH_, int NS_>
