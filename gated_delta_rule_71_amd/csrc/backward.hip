@@ -629,8 +629,209 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
 // dH <- e^{G_n} dH + Q^T diag(scale e^G) dO - K^T diag(beta e^G) dR.
 // (CW = 32, or 16 when 32-column workgroups would leave compute units idle: the
 // chain per workgroup stays the same, its products halve)
+// The sweep of bf16 inputs (q, k, dO exact in fp16) on the fp16 matrix cores: the
+// same steps as the fp32 sweep below, with every operand that is not an fp16 input (P,
+// T, dD, dH, the scaled dO and dR) held as an fp16 pair hi + lo (~22 bits) and each
+// product with such an operand taken as hi and lo terms (both pairs: hi hi + hi lo +
+// lo hi).  Operands are read k-contiguous (8-byte reads in the contraction order of
+// the fp16 tile helpers) or by LDS transpose reads.
+template <typename TIn, typename TQK, int D, int CW>
+__device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
+  using M = Mma<false>;
+  using frag = M::frag;
+  constexpr int LDKH = D + 8;      // K, Q rows (fp16)
+  constexpr int LDS64 = BC + 8;    // P, T rows
+  constexpr int LDO = CW + 16;     // 64 x CW operands: transposed reads conflict-free
+  constexpr int LDHT = D + 8;      // dH^T rows (CW x D)
+  constexpr int TPH = (D / 16) * (CW / 16) / NW;
+  constexpr int NACT = (BC / 16) * (CW / 16) < NW ? (BC / 16) * (CW / 16) : NW;
+  constexpr int TPS = (BC / 16) * (CW / 16) / NACT;
+  static_assert(TPH >= 1 && TPS >= 1, "column tile");
+  const bool sact = (threadIdx.x >> 6) < NACT;
+  __shared__ __align__(16) _Float16 hK[BC * LDKH];
+  __shared__ __align__(16) _Float16 hQ[BC * LDKH];
+  __shared__ __align__(16) _Float16 hPh[BC * LDS64], hPl[BC * LDS64];
+  __shared__ __align__(16) _Float16 hTh[BC * LDS64], hTl[BC * LDS64];
+  __shared__ __align__(16) _Float16 hO[BC * LDO];                   // dO
+  __shared__ __align__(16) _Float16 hDh[BC * LDO], hDl[BC * LDO];   // dD
+  __shared__ __align__(16) _Float16 hSh[BC * LDO], hSl[BC * LDO];   // diag(scale e^G) dO
+  __shared__ __align__(16) _Float16 hRh[BC * LDO], hRl[BC * LDO];   // -diag(beta e^G) dR
+  __shared__ __align__(16) _Float16 hHh[CW * LDHT], hHl[CW * LDHT]; // dH^T
+  __shared__ RowFactors rf;
+  auto put_hl = [](_Float16 *hi, _Float16 *lo, int i, float x) {
+    const _Float16 a = static_cast<_Float16>(x);
+    hi[i] = a;
+    lo[i] = static_cast<_Float16>(x - static_cast<float>(a));
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
+  constexpr int NVT = D / CW;
+  const int item = xcd_work_item(blockIdx.x, NVT, p.num_seqs * p.Hv);
+  if (item < 0) return;
+  const int vt = item % NVT;
+  const int h = (item / NVT) % p.Hv;
+  const int n = item / NVT / p.Hv;
+  const int col0 = CW * vt;
+  const int hk = h / (p.Hv / p.Hk);
+  int t0, t1;
+  seq_span(p, n, t0, t1);
+  const int nch = (t1 - t0 + BC - 1) / BC;
+  const size_t ss = static_cast<size_t>(D) * D;
+
+  const WTile<CW, TPH> wh(wave);
+  const WTile<CW, TPS> ws(wave);
+  f32x4 dh[TPH];
+  zero(dh);
+  if (p.d_final_state) {
+    const float *s = p.d_final_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
+#pragma unroll
+    for (int t = 0; t < TPH; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dh[t][v] = s[wh.row(v, lane) * D + col0 + wh.col(t, lane)];
+  }
+  const TIn *dO = static_cast<const TIn *>(p.d_out);
+  RowsRegs<TQK, D, D> fk, fq;
+  RowsRegs<TIn, D, CW> fo;
+  MatRegs<BC, BC> fp, ft;
+  RowInputs fr;
+  auto fetch = [&](int jc) {
+    const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
+    const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
+    fr.fetch(p, h, ts, rows, tid);
+    fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+    fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+    fo.fetch(dO, p.Hv, h, ts, rows, col0, tid, p.nh);
+    fp.fetch(p.pmat + cc * BC * BC, BC, tid);
+    ft.fetch(p.tmat + cc * BC * BC, BC, tid);
+  };
+  if (nch > 0) fetch(nch - 1);
+  for (int jc = nch - 1; jc >= 0; --jc) {
+    const int c = p.cb[n] + jc;
+    const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
+    const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+    float *dhn = p.dhn + cc * ss;
+#pragma unroll
+    for (int t = 0; t < TPH; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = wh.row(v, lane), q = wh.col(t, lane);
+        dhn[r * D + col0 + q] = dh[t][v];
+        put_hl(hHh, hHl, q * LDHT + r, dh[t][v]);
+      }
+    fk.store_h(hK, LDKH, rows, tid);
+    fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
+    fo.store_h(hO, LDO, rows, tid, ts, p.nh);
+    fp.store_hl(hPh, hPl, LDS64, tid);
+    ft.store_hl(hTh, hTl, LDS64, tid);
+    row_factors(rf, fr, tid);
+    if (jc > 0) fetch(jc - 1);
+    __syncthreads();
+
+    // dD = P^T dO + diag(e^{G_n - G}) (K dH)
+    if (sact) {
+      f32x4 a1[TPS], a2[TPS];
+      zero(a1);
+      zero(a2);
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 32) {
+        const frag ph = frag_tr(hPh, LDS64, k0, ws.r0, lane);
+        const frag pl = frag_tr(hPl, LDS64, k0, ws.r0, lane);
+#pragma unroll
+        for (int t = 0; t < TPS; ++t) {
+          const frag ob = frag_tr(hO, LDO, k0, ws.c0 + 16 * t, lane);
+          a1[t] = M::mma(pl, ob, M::mma(ph, ob, a1[t]));
+        }
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        const frag ka = M::load(hK, LDKH, ws.r0 + l16, k0, lane);
+#pragma unroll
+        for (int t = 0; t < TPS; ++t) {
+          const frag bh = M::load(hHh, LDHT, ws.c0 + 16 * t + l16, k0, lane);
+          const frag bl = M::load(hHl, LDHT, ws.c0 + 16 * t + l16, k0, lane);
+          a2[t] = M::mma(ka, bl, M::mma(ka, bh, a2[t]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TPS; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = ws.row(v, lane);
+          put_hl(hDh, hDl, r * LDO + ws.col(t, lane), a1[t][v] + rf.eGl[r] * a2[t][v]);
+        }
+    }
+    __syncthreads();
+    // dR = T^T dD; dR stored, dV = diag(beta) dR, -diag(beta e^G) dR and
+    // diag(scale e^G) dO for the dH products
+    if (sact) {
+      f32x4 dr[TPS];
+      zero(dr);
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 32) {
+        const frag th = frag_tr(hTh, LDS64, k0, ws.r0, lane);
+        const frag tl = frag_tr(hTl, LDS64, k0, ws.r0, lane);
+#pragma unroll
+        for (int t = 0; t < TPS; ++t) {
+          const frag dhi = frag_tr(hDh, LDO, k0, ws.c0 + 16 * t, lane);
+          const frag dlo = frag_tr(hDl, LDO, k0, ws.c0 + 16 * t, lane);
+          dr[t] = M::mma(tl, dhi, M::mma(th, dlo, M::mma(th, dhi, dr[t])));
+        }
+      }
+      float *drm = p.drmat + cc * BC * D;
+#pragma unroll
+      for (int t = 0; t < TPS; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = ws.row(v, lane), q = ws.col(t, lane);
+          drm[r * D + col0 + q] = dr[t][v];
+          if (r < rows)
+            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
+                rf.beta[r] * dr[t][v];
+          put_hl(hRh, hRl, r * LDO + q, -rf.beta[r] * rf.eG[r] * dr[t][v]);
+        }
+    }
+    for (int idx = tid; idx < BC * CW; idx += BT) {
+      const int r = idx / CW, q = idx % CW;
+      put_hl(hSh, hSl, r * LDO + q, static_cast<float>(hO[r * LDO + q]) * (p.scale * rf.eG[r]));
+    }
+    __syncthreads();
+    // dH <- e^{G_n} dH + Q^T (diag(scale e^G) dO) + K^T (-diag(beta e^G) dR)
+    {
+      const float en = rf.eG[BC - 1];
+#pragma unroll
+      for (int t = 0; t < TPH; ++t) dh[t] *= en;
+#pragma unroll
+      for (int k0 = 0; k0 < BC; k0 += 32) {
+        const frag qa = frag_tr(hQ, LDKH, k0, wh.r0, lane);
+        const frag ka = frag_tr(hK, LDKH, k0, wh.r0, lane);
+#pragma unroll
+        for (int t = 0; t < TPH; ++t) {
+          const int cn = wh.c0 + 16 * t;
+          const frag sh = frag_tr(hSh, LDO, k0, cn, lane);
+          const frag sl = frag_tr(hSl, LDO, k0, cn, lane);
+          const frag rh = frag_tr(hRh, LDO, k0, cn, lane);
+          const frag rl = frag_tr(hRl, LDO, k0, cn, lane);
+          dh[t] = M::mma(qa, sl, M::mma(qa, sh, dh[t]));
+          dh[t] = M::mma(ka, rl, M::mma(ka, rh, dh[t]));
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (p.d_initial_state) {
+    float *s = p.d_initial_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
+#pragma unroll
+    for (int t = 0; t < TPH; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[wh.row(v, lane) * D + col0 + wh.col(t, lane)] = dh[t][v];
+  }
+}
+
 template <typename TIn, typename TQK, int D, int CW>
 __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
+  if constexpr (sizeof(TIn) == 2 && sizeof(TQK) == 2) {
+    bwd_sweep_h16<TIn, TQK, D, CW>(p);
+  } else {
   constexpr int LDK = ld_any_read(D);    // K: by rows (K dH) and by columns (K^T)
   constexpr int LDQ = ld_col_read(D);    // Q: by columns
   constexpr int LDP = ld_col_read(BC);   // P, T: by columns
@@ -777,6 +978,7 @@ __global__ void __launch_bounds__(BT) bwd_sweep_kernel(const BackwardParams p) {
     for (int t = 0; t < TPH; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) s[wh.row(v, lane) * D + col0 + wh.col(t, lane)] = dh[t][v];
+  }
   }
 }
 
