@@ -465,8 +465,205 @@ __global__ void bwd_table_kernel(const BackwardParams p) {
 
 // Per (chunk, value head): Araw = strict_lower((K K^T) * Gamma), P, T = (I + A)^-1
 // with A = diag(beta) Araw, and D = T R, R = diag(beta) (V - diag(e^G) K H0).
+// The local pass of bf16 inputs (q, k, v exact in fp16) on the fp16 matrix cores: K K^T
+// and Q K^T exactly, X = K H0 with H0 as an fp16 hi/lo pair (~22 bits), D = T R with
+// T and R as pairs (hi hi + hi lo + lo hi).  The inverse T = (I + A)^-1 stays on the
+// fp32 path (substitution and 16 x 16 block steps).
+template <typename TIn, typename TQK, int D>
+__device__ __forceinline__ void bwd_local_h16(const BackwardParams &p) {
+  using M = Mma<false>;
+  using frag = M::frag;
+  constexpr int LDA = ld_row_read(BC);   // A: by rows
+  constexpr int LDT = ld_row_read(BC);   // T: by rows (by columns only in the block steps)
+  constexpr int LDKH = D + 8;            // K, Q, V / R rows (fp16)
+  constexpr int LDS64 = BC + 8;          // T rows (fp16)
+  constexpr int TPC = (BC / 16) * (BC / 16) / NW;
+  constexpr int TPD = (BC / 16) * (D / 16) / NW;
+  __shared__ __align__(16) _Float16 hK[BC * LDKH];
+  __shared__ __align__(16) _Float16 hQ[BC * LDKH];     // later V
+  __shared__ __align__(16) _Float16 hRh[BC * LDKH], hRl[BC * LDKH];
+  __shared__ __align__(16) _Float16 hHh[32 * LDKH], hHl[32 * LDKH];   // 32 rows of H0
+  __shared__ __align__(16) _Float16 hTh[BC * LDS64], hTl[BC * LDS64];
+  __shared__ float sA[BC * LDA];
+  __shared__ float sT[BC * LDT];
+  __shared__ float sM[(BC / 16) * 16 * 17];   // the block steps' 16 x 16 blocks
+  __shared__ RowFactors rf;
+  auto put_hl = [](_Float16 *hi, _Float16 *lo, int i, float x) {
+    const _Float16 a = static_cast<_Float16>(x);
+    hi[i] = a;
+    lo[i] = static_cast<_Float16>(x - static_cast<float>(a));
+  };
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= p.cb[p.num_seqs]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
+  const int n = chunk_seq(p.cb, p.num_seqs, c);
+  const int j = c - p.cb[n];
+  int t0, t1;
+  seq_span(p, n, t0, t1);
+  const int ts = t0 + BC * j, rows = min(BC, t1 - ts);
+  const int hk = h / (p.Hv / p.Hk);
+
+  RowsRegs<TQK, D, D> fk, fq;
+  RowInputs fr;
+  fr.fetch(p, h, ts, rows, tid);
+  fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+  fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
+  const float *h0 = entry_state(p, n, j, h, D);
+  MatRegs<32, D> fh[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) fh[b].fetch(h0 ? h0 + static_cast<size_t>(32 * b) * D : nullptr, D, tid);
+  RowsRegs<TIn, D, D> fv;
+  fv.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
+  fk.store_h(hK, LDKH, rows, tid);
+  fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
+  row_factors(rf, fr, tid);
+  __syncthreads();
+
+  const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+  {
+    // K K^T and Q K^T: operands exact in fp16, one product per 32-deep slice
+    const WTile<BC, TPC> w(wave);
+    f32x4 kk[TPC], qk[TPC];
+    zero(kk);
+    zero(qk);
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      const frag ka = M::load(hK, LDKH, w.r0 + l16, k0, lane);
+      const frag qa = M::load(hQ, LDKH, w.r0 + l16, k0, lane);
+#pragma unroll
+      for (int t = 0; t < TPC; ++t) {
+        const frag kb = M::load(hK, LDKH, w.c0 + 16 * t + l16, k0, lane);
+        kk[t] = M::mma(ka, kb, kk[t]);
+        qk[t] = M::mma(qa, kb, qk[t]);
+      }
+    }
+    float *araw = p.araw + cc * BC * BC;
+    float *pm = p.pmat + cc * BC * BC;
+#pragma unroll
+    for (int t = 0; t < TPC; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = w.row(v, lane), q = w.col(t, lane);
+        // mask before the exponential
+        const float gam = q <= r ? expf(static_cast<float>(rf.G[r] - rf.G[q])) : 0.0f;
+        const float a = q < r ? kk[t][v] * gam : 0.0f;
+        araw[r * BC + q] = a;
+        pm[r * BC + q] = q <= r ? p.scale * qk[t][v] * gam : 0.0f;
+        sA[r * LDA + q] = rf.beta[r] * a;
+      }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1 by 16 x 16 blocks, as in the fp32 local pass
+  {
+    for (int idx = tid; idx < BC * BC; idx += BT) sT[(idx / BC) * LDT + idx % BC] = 0.0f;
+    __syncthreads();
+    if (wave < BC / 16 && lane < 16) {
+      const int b = 16 * wave, jc = lane;
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = r == jc ? 1.0f : 0.0f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) x = fmaf(-sA[(b + r) * LDA + b + i], t[i], x);
+        t[r] = x;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(b + r) * LDT + b + jc] = t[r];
+    }
+    __syncthreads();
+    constexpr int LDM = 17;
+    const WTile<16, 1> w0(0);
+    for (int i = 1; i < BC / 16; ++i) {
+      if (wave < i) {
+        const int jb = wave;
+        f32x4 m[1];
+        zero(m);
+        for (int k = jb; k < i; ++k)
+          mmf(m, w0, sA + (16 * i) * LDA + 16 * k, LDA, 1, sT + (16 * k) * LDT + 16 * jb, LDT, 1,
+              16, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sM[jb * 16 * LDM + w0.row(v, lane) * LDM + w0.col(0, lane)] = m[0][v];
+      }
+      __syncthreads();
+      if (wave < i) {
+        const int jb = wave;
+        f32x4 m[1];
+        zero(m);
+        mmf(m, w0, sT + (16 * i) * LDT + 16 * i, LDT, 1, sM + jb * 16 * LDM, LDM, 1, 16, lane);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sT[(16 * i + w0.row(v, lane)) * LDT + 16 * jb + w0.col(0, lane)] = -m[0][v];
+      }
+      __syncthreads();
+    }
+    float *tm = p.tmat + cc * BC * BC;
+    for (int idx = tid; idx < BC * BC; idx += BT) {
+      const float x = sT[(idx / BC) * LDT + idx % BC];
+      tm[idx] = x;
+      put_hl(hTh, hTl, (idx / BC) * LDS64 + idx % BC, x);
+    }
+  }
+
+  // X = K H0, H0 streamed 32 rows at a time as an fp16 pair
+  const WTile<D, TPD> wd(wave);
+  f32x4 x[TPD];
+  zero(x);
+  if (h0) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      __syncthreads();
+      fh[b].store_hl(hHh, hHl, LDKH, tid);
+      __syncthreads();
+      const frag ka = M::load(hK, LDKH, wd.r0 + l16, 32 * b, lane);
+#pragma unroll
+      for (int t = 0; t < TPD; ++t) {
+        const frag bh = frag_tr(hHh, LDKH, 0, wd.c0 + 16 * t, lane);
+        const frag bl = frag_tr(hHl, LDKH, 0, wd.c0 + 16 * t, lane);
+        x[t] = M::mma(ka, bl, M::mma(ka, bh, x[t]));
+      }
+    }
+  }
+  // R = diag(beta) (V - diag(e^G) X) as an fp16 pair (V is staged in Q's place first)
+  __syncthreads();
+  fv.store_h(hQ, LDKH, rows, tid);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TPD; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = wd.row(v, lane), col = wd.col(t, lane);
+      const float y = static_cast<float>(hQ[r * LDKH + col]);
+      put_hl(hRh, hRl, r * LDKH + col, rf.beta[r] * (y - rf.eG[r] * x[t][v]));
+    }
+  __syncthreads();
+  // D = T R
+  f32x4 d[TPD];
+  zero(d);
+#pragma unroll
+  for (int k0 = 0; k0 < BC; k0 += 32) {
+    const frag th = M::load(hTh, LDS64, wd.r0 + l16, k0, lane);
+    const frag tl = M::load(hTl, LDS64, wd.r0 + l16, k0, lane);
+#pragma unroll
+    for (int t = 0; t < TPD; ++t) {
+      const frag rh = frag_tr(hRh, LDKH, k0, wd.c0 + 16 * t, lane);
+      const frag rl = frag_tr(hRl, LDKH, k0, wd.c0 + 16 * t, lane);
+      d[t] = M::mma(tl, rh, M::mma(th, rl, M::mma(th, rh, d[t])));
+    }
+  }
+  float *dm = p.dmat + cc * BC * D;
+#pragma unroll
+  for (int t = 0; t < TPD; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dm[wd.row(v, lane) * D + wd.col(t, lane)] = d[t][v];
+}
+
 template <typename TIn, typename TQK, int D>
 __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
+  if constexpr (sizeof(TIn) == 2 && sizeof(TQK) == 2) {
+    bwd_local_h16<TIn, TQK, D>(p);
+  } else {
   constexpr int LDK = ld_row_read(D);    // K: by rows
   constexpr int LDQ = ld_any_read(D);    // Q by rows, R by columns
   constexpr int LDA = ld_row_read(BC);   // A: by rows
@@ -621,6 +818,7 @@ __global__ void __launch_bounds__(BT) bwd_local_kernel(const BackwardParams p) {
   for (int t = 0; t < TPD; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) dm[wd.row(v, lane) * D + wd.col(t, lane)] = d[t][v];
+  }
 }
 
 // Per (sequence, value head, CW value columns), last chunk to first, carrying
