@@ -424,7 +424,7 @@ namespace {
 
 // Workspace carve-up of the backward (byte offsets from the base, each aligned).
 struct BwdLayout {
-  size_t tab, states, o, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, qn, kn, gg, gb, fwd, total;
+  size_t tab, states, dhn, araw, pmat, tmat, dmat, drmat, dqh, dkh, qn, kn, gg, gb, fwd, total;
   size_t fwd_bytes;   // workspace of the forward recompute (long rows in segments)
   int max_chunks;
 };
@@ -469,7 +469,6 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   const size_t chunks = (rows + 63 * N) / 64;
   const size_t entries = rows / 64;
   L.max_chunks = static_cast<int>(chunks);
-  const size_t elem = a->qkv_dtype == GDR_DTYPE_F32 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -478,7 +477,6 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   };
   L.tab = take(2 * (N + 1) * sizeof(int32_t));
   L.states = take(entries * Hv * D * D * 4);
-  L.o = take(tokens * Hv * D * elem);
   L.dhn = take(chunks * Hv * D * D * 4);
   L.araw = take(chunks * Hv * 64 * 64 * 4);
   L.pmat = take(chunks * Hv * 64 * 64 * 4);
@@ -626,7 +624,8 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
   if (gdr::launch_backward_prologue(p, f32, a->head_k, s) != hipSuccess) return GDR_ERR_HIP;
   if (tokens > 0) {
     // forward recompute: the state after every 64 rows of each sequence (long
-    // batched rows run in segments with their workspace)
+    // batched rows run in segments with their workspace); its outputs are not needed,
+    // so the kernels write none (the checks see a stand-in for them)
     gdr_prefill_args f = bwd_forward_args(a);
     f.q = a->q;
     f.k = a->k;
@@ -634,11 +633,12 @@ int gdr_chunk_gated_delta_rule_backward(const gdr_backward_args *a, void *stream
     f.g = a->g;
     f.beta = a->beta;
     f.initial_state = a->initial_state;
-    f.out = ws + L.o;
+    f.out = const_cast<void *>(a->d_out);   // a stand-in for the checks only
     f.boundary_states = p.states;
-    f.workspace = L.fwd_bytes ? ws + L.fwd : nullptr;
-    f.workspace_bytes = L.fwd_bytes;
-    const int fs = gdr_chunk_gated_delta_rule(&f, stream);
+    const int fv = gdr_validate_prefill(&f);
+    if (fv != GDR_OK) return fv;
+    f.out = nullptr;
+    const int fs = enqueue_prefill(&f, s, L.fwd_bytes ? ws + L.fwd : nullptr, L.fwd_bytes);
     if (fs != GDR_OK) return fs;
   }
   if (gdr::launch_backward(p, f32, a->head_k, L.max_chunks, tokens, s) != hipSuccess)

@@ -231,11 +231,12 @@ def test_backward_workspace_size(lib):
     # 2 sequences of 100 tokens (cu_seqlens may be anything on the device, so the
     # host sizes for the most chunks any split of 200 tokens into 2 sequences has:
     # (200 + 63 * 2) // 64 = 5), 200 // 64 = 3 boundary states, Hv = 4, D = 128
+    # (the forward recompute writes no outputs, so none are kept)
     chunks, entries, Hv, D = 5, 3, 4, 128
     floats = entries * Hv * D * D + chunks * Hv * (D * D + 3 * 64 * 64 + 2 * 64 * D) \
         + 2 * 200 * Hv * D
-    assert need >= floats * 4 + 200 * Hv * D * 2
-    assert need < floats * 4 + 200 * Hv * D * 2 + 16 * 256
+    assert need >= floats * 4
+    assert need < floats * 4 + 16 * 256
     assert lib.gdr_validate_backward(ctypes.byref(a)) == _lib.GDR_OK
     same_heads = _backward(num_qk_heads=4)
     assert lib.gdr_backward_workspace_bytes(ctypes.byref(same_heads)) < need
