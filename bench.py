@@ -33,8 +33,10 @@ Nine legs, each timed over exactly K steps bracketed by torch.cuda.synchronize()
   backward: the chunked backward (gradients of q, k, v, g, beta and the initial
            state) at B=4, T=4096, H=16, D=128, bf16 inputs, and of the gated delta
            product (n_h = 2) at B=1, T=16384, H=32; one call = the forward
-           recompute plus the backward kernels; tokens/s and the fraction of the
-           fp32 matrix-core peak its dense contractions reach.
+           recompute plus the backward kernels; tokens/s, the fraction of the
+           bf16 matrix-core peak its dense contractions reach (their products of
+           bf16 inputs run on the fp16 matrix cores) and the HBM rate of its
+           algorithmic bytes.
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -57,7 +59,6 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s (H=32,K=V=128) + decode state GB/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2516.6   # dense fp16/bf16
-FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix cores
 
 
 def parse():
@@ -497,14 +498,26 @@ def run_backward_leg(steps, warmup, *, name="bwd_bf16_B4_T4096_H16_D128", B=4, T
     tokens = B * T
     F = backward_flops_per_token(Hv, D, n_h=n_h)
     tf = F * tokens / (kern * 1e-3) / 1e12
+    # algorithmic bytes: bf16 q, k, v, dO and fp32 g, beta read once, fp32 gradients
+    # written once, the initial state and dH_T read and dH0 written once
+    rows = tokens * n_h
+    alg = (2 * (tokens * Hk * D + rows * Hk * D + rows * Hv * D + tokens * Hv * D)
+           + 4 * (tokens * Hv + rows * Hv)
+           + 4 * (tokens * Hk * D + rows * Hk * D + rows * Hv * D + tokens * Hv + rows * Hv)
+           + 4 * 3 * B * Hv * D * D)
+    gbs = alg / (kern * 1e-3) / 1e9
     return {"workload": bw.fwd.name, "tokens": tokens, "call_ms": kern, "wall_ms": wall,
             "value": tokens / (kern * 1e-3), "unit": "tokens/s",
             "workspace_bytes": ws.numel(),
             "flops_per_token": F, "achieved_tflops": tf,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / FP32_MFMA_PEAK_TFLOPS,
-                         "note": "backward contractions on the fp32 matrix cores; the call "
-                                 "time includes the forward recompute"}}
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
+                         "note": "products of bf16 inputs on the fp16 matrix cores, other "
+                                 "operands as fp16 hi/lo pairs (the extra instructions not "
+                                 "counted); the call time includes the forward recompute"},
+            "hbm": {"algorithmic_bytes": alg, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                    "note": "the per-chunk states and matrices of the workspace come on top "
+                            "of these bytes"}}
 
 
 def profile_run():

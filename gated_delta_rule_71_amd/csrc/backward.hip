@@ -465,34 +465,25 @@ __global__ void bwd_table_kernel(const BackwardParams p) {
 
 // Per (chunk, value head): Araw = strict_lower((K K^T) * Gamma), P, T = (I + A)^-1
 // with A = diag(beta) Araw, and D = T R, R = diag(beta) (V - diag(e^G) K H0).
-// The local pass of bf16 inputs (q, k, v exact in fp16) on the fp16 matrix cores: K K^T
-// and Q K^T exactly, X = K H0 with H0 as an fp16 hi/lo pair (~22 bits), D = T R with
-// T and R as pairs (hi hi + hi lo + lo hi).  The inverse T = (I + A)^-1 stays on the
-// fp32 path (substitution and 16 x 16 block steps).
+// The local pass of bf16 inputs (q, k exact in fp16): K K^T and Q K^T exactly on the
+// fp16 matrix cores, and the inverse T = (I + A)^-1 on the fp32 path (substitution and
+// 16 x 16 block steps).  It writes Araw, P and T only (see the gradient kernel for D).
 template <typename TIn, typename TQK, int D>
 __device__ __forceinline__ void bwd_local_h16(const BackwardParams &p) {
   using M = Mma<false>;
   using frag = M::frag;
   constexpr int LDA = ld_row_read(BC);   // A: by rows
   constexpr int LDT = ld_row_read(BC);   // T: by rows (by columns only in the block steps)
-  constexpr int LDKH = D + 8;            // K, Q, V / R rows (fp16)
-  constexpr int LDS64 = BC + 8;          // T rows (fp16)
+  constexpr int LDKH = D + 8;            // K, Q rows (fp16)
   constexpr int TPC = (BC / 16) * (BC / 16) / NW;
-  constexpr int TPD = (BC / 16) * (D / 16) / NW;
+  // no D = T R here: the gradient kernel forms it slice by slice from H0, which it
+  // reads anyway, so this pass reads no state and its LDS fits two workgroups per CU
   __shared__ __align__(16) _Float16 hK[BC * LDKH];
-  __shared__ __align__(16) _Float16 hQ[BC * LDKH];     // later V
-  __shared__ __align__(16) _Float16 hRh[BC * LDKH], hRl[BC * LDKH];
-  __shared__ __align__(16) _Float16 hHh[32 * LDKH], hHl[32 * LDKH];   // 32 rows of H0
-  __shared__ __align__(16) _Float16 hTh[BC * LDS64], hTl[BC * LDS64];
+  __shared__ __align__(16) _Float16 hQ[BC * LDKH];
   __shared__ float sA[BC * LDA];
   __shared__ float sT[BC * LDT];
   __shared__ float sM[(BC / 16) * 16 * 17];   // the block steps' 16 x 16 blocks
   __shared__ RowFactors rf;
-  auto put_hl = [](_Float16 *hi, _Float16 *lo, int i, float x) {
-    const _Float16 a = static_cast<_Float16>(x);
-    hi[i] = a;
-    lo[i] = static_cast<_Float16>(x - static_cast<float>(a));
-  };
 
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= p.cb[p.num_seqs]) return;
@@ -509,12 +500,6 @@ __device__ __forceinline__ void bwd_local_h16(const BackwardParams &p) {
   fr.fetch(p, h, ts, rows, tid);
   fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
   fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
-  const float *h0 = entry_state(p, n, j, h, D);
-  MatRegs<32, D> fh[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) fh[b].fetch(h0 ? h0 + static_cast<size_t>(32 * b) * D : nullptr, D, tid);
-  RowsRegs<TIn, D, D> fv;
-  fv.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, 0, tid);
   fk.store_h(hK, LDKH, rows, tid);
   fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
   row_factors(rf, fr, tid);
@@ -599,64 +584,8 @@ __device__ __forceinline__ void bwd_local_h16(const BackwardParams &p) {
       __syncthreads();
     }
     float *tm = p.tmat + cc * BC * BC;
-    for (int idx = tid; idx < BC * BC; idx += BT) {
-      const float x = sT[(idx / BC) * LDT + idx % BC];
-      tm[idx] = x;
-      put_hl(hTh, hTl, (idx / BC) * LDS64 + idx % BC, x);
-    }
+    for (int idx = tid; idx < BC * BC; idx += BT) tm[idx] = sT[(idx / BC) * LDT + idx % BC];
   }
-
-  // X = K H0, H0 streamed 32 rows at a time as an fp16 pair
-  const WTile<D, TPD> wd(wave);
-  f32x4 x[TPD];
-  zero(x);
-  if (h0) {
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-      __syncthreads();
-      fh[b].store_hl(hHh, hHl, LDKH, tid);
-      __syncthreads();
-      const frag ka = M::load(hK, LDKH, wd.r0 + l16, 32 * b, lane);
-#pragma unroll
-      for (int t = 0; t < TPD; ++t) {
-        const frag bh = frag_tr(hHh, LDKH, 0, wd.c0 + 16 * t, lane);
-        const frag bl = frag_tr(hHl, LDKH, 0, wd.c0 + 16 * t, lane);
-        x[t] = M::mma(ka, bl, M::mma(ka, bh, x[t]));
-      }
-    }
-  }
-  // R = diag(beta) (V - diag(e^G) X) as an fp16 pair (V is staged in Q's place first)
-  __syncthreads();
-  fv.store_h(hQ, LDKH, rows, tid);
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < TPD; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = wd.row(v, lane), col = wd.col(t, lane);
-      const float y = static_cast<float>(hQ[r * LDKH + col]);
-      put_hl(hRh, hRl, r * LDKH + col, rf.beta[r] * (y - rf.eG[r] * x[t][v]));
-    }
-  __syncthreads();
-  // D = T R
-  f32x4 d[TPD];
-  zero(d);
-#pragma unroll
-  for (int k0 = 0; k0 < BC; k0 += 32) {
-    const frag th = M::load(hTh, LDS64, wd.r0 + l16, k0, lane);
-    const frag tl = M::load(hTl, LDS64, wd.r0 + l16, k0, lane);
-#pragma unroll
-    for (int t = 0; t < TPD; ++t) {
-      const frag rh = frag_tr(hRh, LDKH, k0, wd.c0 + 16 * t, lane);
-      const frag rl = frag_tr(hRl, LDKH, k0, wd.c0 + 16 * t, lane);
-      d[t] = M::mma(tl, rh, M::mma(th, rl, M::mma(th, rh, d[t])));
-    }
-  }
-  float *dm = p.dmat + cc * BC * D;
-#pragma unroll
-  for (int t = 0; t < TPD; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) dm[wd.row(v, lane) * D + wd.col(t, lane)] = d[t][v];
 }
 
 template <typename TIn, typename TQK, int D>
@@ -1204,17 +1133,21 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   // the fp32 ones, whose 1e-5 bound fp16 operands would not meet)
   constexpr bool H16 = sizeof(TIn) == 2;
   constexpr int LDH = 40;   // fp16 slice rows: 16-byte reads on 16 rows, conflict-free
-  constexpr int P1 = H16 ? (5 * BC * LDH + 4 * D * LDH) / 2 + 2 * BC * LDV
-                         : 4 * BC * LDV + 2 * D * LDV;
   // phase 3 on the fp16 matrix cores too when q and k are bf16 (exact in fp16): dAs and
-  // dPs as fp16 hi/lo pairs
+  // dPs as fp16 hi/lo pairs.  Then the local pass keeps no D either: phase 1 forms each
+  // slice of D = T R from K, H0, V and T (K and T staged once, in LDS of their own
+  // for K, which phase 3 reads too)
   constexpr bool H16Q = H16 && sizeof(TQK) == 2;
   constexpr int LDS64 = BC + 8;   // fp16 64 x 64 rows: conflict-free 8-byte and transposed reads
   constexpr int LDKH = D + 8;     // fp16 K, Q rows
-  constexpr int P23 = H16Q ? (4 * BC * LDS64 + 2 * BC * LDKH) / 2 + 2 * BC * LDC
+  constexpr int P1 = H16 ? (5 * BC * LDH + 4 * D * LDH) / 2 + 2 * BC * LDV +
+                               (H16Q ? (2 * BC * LDH + 2 * BC * LDS64) / 2 : 0)
+                         : 4 * BC * LDV + 2 * D * LDV;
+  constexpr int P23 = H16Q ? (4 * BC * LDS64 + BC * LDKH) / 2 + 2 * BC * LDC
                            : 2 * BC * LDG + 2 * BC * LDC + 2 * BC * LDD;
   constexpr int ARENA = P1 > P23 ? P1 : P23;
   __shared__ __align__(16) float arena[ARENA];
+  __shared__ __align__(16) _Float16 hK1[H16Q ? BC * LDKH : 8];   // K (fp16) for phases 1 and 3
   __shared__ RowFactors rf;
   __shared__ float srow[3][BC];         // row sums of E + F, column sums of E + F, row sums of dA * Araw
   __shared__ float sdot[3][HALVES][BC]; // q.U1, k.Ua, k.Ub per row, one partial per wave of a tile row
@@ -1263,21 +1196,31 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
     _Float16 *hH = hRl + BC * LDH, *hG = hH + D * LDH;
     _Float16 *hHl = hG + D * LDH, *hGl = hHl + D * LDH;     // low parts of the states
     float *sRb = reinterpret_cast<float *>(hGl + D * LDH), *svb = sRb + BC * LDV;
+    // H16Q: R = diag(beta) (V - diag(e^G) K H0) of the slice and T, as fp16 pairs
+    _Float16 *hY = reinterpret_cast<_Float16 *>(svb + BC * LDV), *hYl = hY + BC * LDH;
+    _Float16 *hTh = hYl + BC * LDH, *hTl = hTh + BC * LDS64;
     MatRegs<BC, 32> fD, fR;
     RowsRegs<TIn, D, 32> fO, fV;
     MatRegs<D, 32> fH, fG;
     auto fetch = [&](int vb) {
-      fD.fetch(dm + vb, D, tid);
+      if constexpr (!H16Q) fD.fetch(dm + vb, D, tid);
       fR.fetch(drm + vb, D, tid);
       fO.fetch(static_cast<const TIn *>(p.d_out), p.Hv, h, ts, rows, vb, tid, p.nh);
       fV.fetch(static_cast<const TIn *>(p.v), p.Hv, h, ts, rows, vb, tid);
       fH.fetch(h0 ? h0 + vb : nullptr, D, tid);
       fG.fetch(dhn + vb, D, tid);
     };
+    if constexpr (H16Q) {
+      fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+      MatRegs<BC, BC> ft;
+      ft.fetch(p.tmat + cc * BC * BC, BC, tid);
+      fk.store_h(hK1, LDKH, rows, tid);
+      ft.store_hl(hTh, hTl, LDS64, tid);
+    }
     fetch(0);
     for (int vb = 0; vb < D; vb += 32) {
       __syncthreads();
-      fD.store_hl(hD, hDl, LDH, tid);
+      if constexpr (!H16Q) fD.store_hl(hD, hDl, LDH, tid);
       fR.store_hl(hR, hRl, LDH, tid);
       fR.store(sRb, LDV, tid);
       fO.store_h(hO, LDH, rows, tid, ts, p.nh);
@@ -1289,7 +1232,7 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
         fetch(vb + 32);
       } else {
         if constexpr (kPreKQ) {
-          fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
+          if constexpr (!H16Q) fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
           fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
         }
         const float *araw = p.araw + cc * BC * BC;
@@ -1304,6 +1247,47 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
           }
       }
       __syncthreads();
+      if constexpr (H16Q) {
+        // this slice of D = T R, R = diag(beta) (V - diag(e^G) K H0): one 16 x 16 tile of
+        // the 64 x 32 slice per wave; K exact, H0, R and T as pairs
+        using M = Mma<false>;
+        const WTile<32, 1> wx(wave);
+        const int l16 = lane & 15;
+        f32x4 x = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          const M::frag ka = M::load(hK1, LDKH, wx.r0 + l16, k0, lane);
+          const M::frag bh = frag_tr(hH, LDH, k0, wx.c0, lane);
+          const M::frag bl = frag_tr(hHl, LDH, k0, wx.c0, lane);
+          x = M::mma(ka, bl, M::mma(ka, bh, x));
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = wx.row(v, lane), q = wx.col(0, lane);
+          const float y = rf.beta[r] * (svb[r * LDV + q] - rf.eG[r] * x[v]);
+          const _Float16 a = static_cast<_Float16>(y);
+          hY[r * LDH + q] = a;
+          hYl[r * LDH + q] = static_cast<_Float16>(y - static_cast<float>(a));
+        }
+        __syncthreads();
+        f32x4 d = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32) {
+          const M::frag th = M::load(hTh, LDS64, wx.r0 + l16, k0, lane);
+          const M::frag tl = M::load(hTl, LDS64, wx.r0 + l16, k0, lane);
+          const M::frag rh = frag_tr(hY, LDH, k0, wx.c0, lane);
+          const M::frag rl = frag_tr(hYl, LDH, k0, wx.c0, lane);
+          d = M::mma(tl, rh, M::mma(th, rl, M::mma(th, rh, d)));
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = wx.row(v, lane), q = wx.col(0, lane);
+          const _Float16 a = static_cast<_Float16>(d[v]);
+          hD[r * LDH + q] = a;
+          hDl[r * LDH + q] = static_cast<_Float16>(d[v] - static_cast<float>(a));
+        }
+        __syncthreads();
+      }
       // x y with x = xh + xl, y = yh + yl (dO is exact in fp16): xh yh + xh yl + xl yh
       {
         f32x4 *const acc[2] = {dA, dP};
@@ -1408,7 +1392,8 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
   // the fp16 layout of the same arena
   _Float16 *hA = reinterpret_cast<_Float16 *>(arena), *hAl = hA + BC * LDS64;
   _Float16 *hP = hAl + BC * LDS64, *hPl = hP + BC * LDS64;
-  _Float16 *hK = hPl + BC * LDS64, *hQ = hK + BC * LDKH;
+  _Float16 *hQ = hPl + BC * LDS64;
+  const _Float16 *hK = hK1;   // staged before phase 1
   if constexpr (H16Q) {
     sM1 = reinterpret_cast<float *>(hQ + BC * LDKH);
     sM2 = sM1 + BC * LDC;
@@ -1438,7 +1423,6 @@ __global__ void __launch_bounds__(BT) bwd_grads_kernel(const BackwardParams p) {
       sM2[r * LDC + q] = a * ar[t][v];
     }
   if constexpr (H16Q) {
-    fk.store_h(hK, LDKH, rows, tid);
     fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
   } else if constexpr (kPreKQ) {
     fk.store(sK, LDD, rows, tid);

@@ -481,7 +481,9 @@ BwdLayout bwd_layout(const gdr_backward_args *a) {
   L.araw = take(chunks * Hv * 64 * 64 * 4);
   L.pmat = take(chunks * Hv * 64 * 64 * 4);
   L.tmat = take(chunks * Hv * 64 * 64 * 4);
-  L.dmat = take(chunks * Hv * 64 * D * 4);
+  // bf16 q, k (no in-kernel norm): the gradient kernel forms D itself
+  const bool d_kept = a->qkv_dtype == GDR_DTYPE_F32 || a->use_qk_l2norm;
+  L.dmat = take(d_kept ? chunks * Hv * 64 * D * 4 : 0);
   L.drmat = take(chunks * Hv * 64 * D * 4);
   const bool grouped = a->num_v_heads != a->num_qk_heads;
   L.dqh = take(grouped ? tokens * Hv * D * 4 : 0);

@@ -320,9 +320,10 @@ typedef struct {
  * Workspace: gdr_backward_workspace_bytes(args) bytes of device memory, 256-byte
  *   aligned, owned by the caller; its contents on entry do not matter.  It holds
  *   per 64-token chunk and value head the entering state, the gradient of the
- *   leaving state and five 64 x 64 or 64 x D float32 matrices (about
- *   2 D^2 + 3 * 64^2 + 2 * 64 D floats, 200 KiB at D = 128), plus float32 copies
- *   of the normalised q, k (use_qk_l2norm) and of the formed gates (gate_mode 1).
+ *   leaving state and four 64 x 64 or 64 x D float32 matrices (about
+ *   2 D^2 + 3 * 64^2 + 64 D floats, 176 KiB at D = 128; one more 64 x D matrix
+ *   with F32 inputs or use_qk_l2norm), plus float32 copies of the normalised q, k
+ *   (use_qk_l2norm) and of the formed gates (gate_mode 1).
  * Supported: head_k == head_v = D in {64, 128}; q/k/v/d_out F32 or BF16;
  *   n_h in {1, 2} (n_h = 2 with F32 inputs only at D = 64, as in the prefill).
  * The outputs must not alias the inputs or the workspace.

@@ -232,14 +232,19 @@ def test_backward_workspace_size(lib):
     # host sizes for the most chunks any split of 200 tokens into 2 sequences has:
     # (200 + 63 * 2) // 64 = 5), 200 // 64 = 3 boundary states, Hv = 4, D = 128
     # (the forward recompute writes no outputs, so none are kept)
+    # bf16 q, k: the gradient kernel forms D = T R itself, so one 64 x D matrix (dR) per
+    # chunk and head; f32 inputs keep D as well
     chunks, entries, Hv, D = 5, 3, 4, 128
-    floats = entries * Hv * D * D + chunks * Hv * (D * D + 3 * 64 * 64 + 2 * 64 * D) \
+    floats = entries * Hv * D * D + chunks * Hv * (D * D + 3 * 64 * 64 + 64 * D) \
         + 2 * 200 * Hv * D
     assert need >= floats * 4
     assert need < floats * 4 + 16 * 256
     assert lib.gdr_validate_backward(ctypes.byref(a)) == _lib.GDR_OK
     same_heads = _backward(num_qk_heads=4)
     assert lib.gdr_backward_workspace_bytes(ctypes.byref(same_heads)) < need
+    f32 = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(qkv_dtype=0)))
+    assert f32 >= (floats + chunks * Hv * 64 * D) * 4
+    assert f32 < (floats + chunks * Hv * 64 * D) * 4 + 16 * 256
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -296,8 +301,9 @@ def test_backward_workspace_counts_rows(lib):
     one = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward()))
     two = lib.gdr_backward_workspace_bytes(ctypes.byref(_backward(num_householder=2)))
     # 200 tokens, 2 sequences, Hv = 4, D = 128; n_h = 2 doubles the rows: 8 instead
-    # of 5 chunks of 64 rows (per chunk and head D^2 + 3 * 64^2 + 2 * 64 D floats),
-    # 6 instead of 3 boundary states, and the per-row dk of the grouped heads
-    per_chunk = 4 * (128 * 128 + 3 * 64 * 64 + 2 * 64 * 128) * 4
+    # of 5 chunks of 64 rows (per chunk and head D^2 + 3 * 64^2 + 64 D floats with
+    # bf16 inputs), 6 instead of 3 boundary states, and the per-row dk of the grouped
+    # heads
+    per_chunk = 4 * (128 * 128 + 3 * 64 * 64 + 64 * 128) * 4
     extra = 3 * per_chunk + 3 * 4 * 128 * 128 * 4 + 200 * 4 * 128 * 4
     assert abs(two - one - extra) <= 8 * 256
