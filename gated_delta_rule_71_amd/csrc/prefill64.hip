@@ -517,18 +517,26 @@ prefill64_kernel(const PrefillParams p) {
   // resources that end at the sequence's last row: rows past it read as zero, which is
   // what the chunk algebra needs of them (no clamps, no masks), and the per-lane offsets
   // stay the same from chunk to chunk
+  auto k_rsrc = [&](int c) __attribute__((always_inline)) {
+    return rows_rsrc(kb, c, min(CR, row_end - c), kstride);
+  };
+  auto q_rsrc = [&](int c) __attribute__((always_inline)) {
+    const int tq = c / NH;
+    return rows_rsrc(qb, tq, min(CQ, t1 - tq), kstride);
+  };
+  auto k_off = [&](int j) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(((16 * pw + l16) * kstride + (4 * j + g4) * 8) * 2);
+  };
+  auto q_off = [&](int j) __attribute__((always_inline)) {
+    const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
+    return static_cast<uint32_t>((r * kstride + sg * 8) * 2);
+  };
   auto fetch = [&](Regs64<Tr> &cr, int c) __attribute__((always_inline)) {
-    const int nrow = min(CR, row_end - c), tq = c / NH, nq = min(CQ, t1 - tq);
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb, c, nrow, kstride);
-    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qb, tq, nq, kstride);
+    const __amdgpu_buffer_rsrc_t rk = k_rsrc(c), rq = q_rsrc(c);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      cr.k[j].u = load16(rk, ((16 * pw + l16) * kstride + (4 * j + g4) * 8) * 2);
+    for (int j = 0; j < KPT; ++j) cr.k[j].u = load16(rk, k_off(j));
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
-      cr.q[j].u = load16(rq, (r * kstride + sg * 8) * 2);
-    }
+    for (int j = 0; j < QPT; ++j) cr.q[j].u = load16(rq, q_off(j));
   };
   // the gates of the chunk starting at row c (producer 0; requested a whole interval
   // before the decay scan reads them)
@@ -539,9 +547,13 @@ prefill64_kernel(const PrefillParams p) {
   };
   // producer registers (a chunk; rows past the sequence hold zeros) -> staged LDS
   // buffer.  The L2 norm is a compile-time choice, so that no branch splits the
-  // conversions.
-  auto stage = [&](const Regs64<Tr> &cr, Stage64<Tr> &s, auto l2c) __attribute__((always_inline)) {
+  // conversions.  Each register is refilled with chunk cn's inputs as soon as it has
+  // been consumed, so that those loads have almost a whole interval to land (they
+  // take longer than what is left of it after the staging; a chunk past the sequence's
+  // end reads zeros).
+  auto stage = [&](Regs64<Tr> &cr, Stage64<Tr> &s, auto l2c, int cn) __attribute__((always_inline)) {
     constexpr bool L2 = decltype(l2c)::value;
+    const __amdgpu_buffer_rsrc_t rk = k_rsrc(cn), rq = q_rsrc(cn);
     // L2 factor of a row from this lane's partial sum of squares: the lanes that hold
     // the row's other segments are xor 16 and 32 away (K) or xor 1 .. SEG / 2 (Q)
     auto rnorm = [&](float ss, auto krows) __attribute__((always_inline)) {
@@ -578,6 +590,7 @@ prefill64_kernel(const PrefillParams p) {
                                    pk_f16(x[j][4], x[j][5]), pk_f16(x[j][6], x[j][7]));
         *reinterpret_cast<uint4 *>(s.K + r * LDK + (4 * j + g4) * 8) = w;
         kh[j].v = __builtin_bit_cast(f16x8, w);
+        cr.k[j].u = load16(rk, k_off(j));
       }
     }
     // Q: segment u % SEG of row u / SEG, u = stid + j ST (a row's SEG segments in
@@ -598,6 +611,7 @@ prefill64_kernel(const PrefillParams p) {
       } else {
         store8_bf16_as_f16(s.Q + r * LDK + sg * 8, cr.q[j].u);
       }
+      cr.q[j].u = load16(rq, q_off(j));
     }
   };
   // Per-row decay factors of the chunk starting at row c (producer 0, from the gates
@@ -864,8 +878,8 @@ prefill64_kernel(const PrefillParams p) {
   } else {
     // ---- producers ---------------------------------------------------------------
     // prologue: chunk 0 staged and solved, chunk 1 fetched.  Interval ci: stage chunk
-    // ci+1, then fetch chunk ci+2 into the same registers (phase A); solve chunk ci+1
-    // (phase B).  The loads have the rest of the interval to land before their staging.
+    // ci+1, each register refilled with chunk ci+2's inputs as soon as it is staged
+    // (phase A); solve chunk ci+1 (phase B).  The loads have almost an interval to land.
     // The decay scan of a chunk runs on producer 0 in the phase B two phases before the
     // chunk's solve, and each producer forms its diagonal block of A from its staged K
     // registers in the phase A before the solve, so that producer 0's share of the solve
@@ -885,8 +899,7 @@ prefill64_kernel(const PrefillParams p) {
           put_factors(sc, sm.fac[0]);
           if (nchunks > 1) fetch_gates(rg, row_begin + CR);
         }
-        stage(rg, sm.st[0], l2c);
-        if (nchunks > 1) fetch(rg, row_begin + CR);
+        stage(rg, sm.st[0], l2c, row_begin + CR);
       }
       __syncthreads();
       if (nchunks > 0) {
@@ -908,11 +921,10 @@ prefill64_kernel(const PrefillParams p) {
           // the staging; its exponent bases (stored in the previous phase B) are read
           // first
           const DiagBases db = p64_diag_bases<Tr>(sn, pw, lane);
-          stage(rg, sn, l2c);
+          stage(rg, sn, l2c, row_begin + (ci + 2) * CR);
           f32x4 acc = zero4();
 #pragma unroll
           for (int sl = 0; sl < KS; ++sl) acc = M::mma(kh[sl], kh[sl], acc);
-          if (ci + 2 < nchunks) fetch(rg, row_begin + (ci + 2) * CR);
           p64_diag_put<Tr>(db, acc, pw, sm.AR, lane);
         }
         __syncthreads();
