@@ -173,6 +173,40 @@ def test_backward_l2norm_and_raw_gates(dtype):
     compare(x, r, dtype == W.F32, f"l2norm + raw gates {dtype}", names=names)
 
 
+def test_backward_l2norm_raw_gates_T4096_sampled():
+    """The module's defaults (in-kernel q/k L2 norm, gates from raw projections) at a
+    training length, bf16, B = 1, T = 4096, H = 2: the sweep's dH recursion runs 64
+    chunks, where fp16 copies of the normalised q, k would carry their rounding from
+    chunk to chunk (the sweep reads float32 copies).  q/k heads are not shared, so head 1
+    is checked on its own against the oracle."""
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    from oracle.backward import prefill_backward
+    bw = W.backward_workload("bwd_l2_long", 23, Hk=2, Hv=2, D=128, dtype=W.BF16, B=1, T=4096,
+                             decay="config")
+    f = bw.fwd
+    q, k, alpha, b, A_log, dt_bias = _raw_inputs(bw, 23)
+    out = gdr.chunk_gated_delta_rule_backward(
+        to_dev(q), to_dev(k), to_dev(f.v), to_dev(alpha), to_dev(b), to_dev(bw.do),
+        dht=to_dev(bw.dht), initial_state=to_dev(f.initial_state), use_qk_l2norm_in_kernel=True,
+        A_log=to_dev(A_log), dt_bias=to_dev(dt_bias))
+    torch.cuda.synchronize()
+    names = NAMES
+    x = {n: t.cpu().numpy().astype(np.float64) for n, t in zip(names, out)}
+    h = 1
+    sl = (slice(None), slice(None), slice(h, h + 1))
+    r = prefill_backward(W.as_f64(q[sl], W.BF16), W.as_f64(k[sl], W.BF16),
+                         W.as_f64(f.v[sl], W.BF16), alpha[sl].astype(np.float64),
+                         b[sl].astype(np.float64), W.as_f64(bw.do[sl], W.BF16),
+                         bw.dht[:, h:h + 1].astype(np.float64),
+                         initial_state=f.initial_state[:, h:h + 1].astype(np.float64),
+                         use_qk_l2norm=True, A_log=A_log[h:h + 1].astype(np.float64),
+                         dt_bias=dt_bias[h:h + 1].astype(np.float64))
+    xs = {n: x[n][sl] for n in ("dq", "dk", "dv", "dg", "dbeta")}
+    xs["dh0"] = x["dh0"][:, h:h + 1]
+    compare(xs, r, False, "l2norm + raw gates bf16 T=4096", names=names)
+
+
 def test_backward_l2norm_only_fp32():
     import torch
     import gated_delta_rule_71_amd as gdr
