@@ -36,7 +36,8 @@ Nine legs, each timed over exactly K steps bracketed by torch.cuda.synchronize()
            recompute plus the backward kernels; tokens/s, the fraction of the
            bf16 matrix-core peak its dense contractions reach (their products of
            bf16 inputs run on the fp16 matrix cores) and the HBM rate of its
-           algorithmic bytes.
+           algorithmic bytes; the roofline object is the one of the two whose
+           algorithmic time at peak is longer (HBM at these shapes).
 Per-launch kernel durations come from HIP events on the launch stream.  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
@@ -506,18 +507,23 @@ def run_backward_leg(steps, warmup, *, name="bwd_bf16_B4_T4096_H16_D128", B=4, T
            + 4 * (tokens * Hk * D + rows * Hk * D + rows * Hv * D + tokens * Hv + rows * Hv)
            + 4 * 3 * B * Hv * D * D)
     gbs = alg / (kern * 1e-3) / 1e9
+    mfma = {"achieved": tf, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_PEAK_TFLOPS,
+            "note": "products of bf16 inputs on the fp16 matrix cores, other operands as "
+                    "fp16 hi/lo pairs (the extra instructions not counted)"}
+    hbm = {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+           "algorithmic_bytes": alg,
+           "note": "the per-chunk states and matrices of the workspace come on top of these "
+                   "bytes"}
+    # the roofline's bound: the larger of the two algorithmic times at peak
+    hbm_bound = alg / (HBM_PEAK_GBS * 1e9) >= F * tokens / (MFMA_PEAK_TFLOPS * 1e12)
+    roof = dict(hbm if hbm_bound else mfma, bound="hbm" if hbm_bound else "mfma")
+    roof["note"] += "; the call time includes the forward recompute"
     return {"workload": bw.fwd.name, "tokens": tokens, "call_ms": kern, "wall_ms": wall,
             "value": tokens / (kern * 1e-3), "unit": "tokens/s",
             "workspace_bytes": ws.numel(),
             "flops_per_token": F, "achieved_tflops": tf,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
-                         "note": "products of bf16 inputs on the fp16 matrix cores, other "
-                                 "operands as fp16 hi/lo pairs (the extra instructions not "
-                                 "counted); the call time includes the forward recompute"},
-            "hbm": {"algorithmic_bytes": alg, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
-                    "note": "the per-chunk states and matrices of the workspace come on top "
-                            "of these bytes"}}
+            "roofline": roof, "mfma": mfma, "hbm": hbm}
 
 
 def profile_run():
