@@ -110,7 +110,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base
 }
 // sixteen bytes at a byte offset of a buffer resource
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
@@ -172,8 +171,10 @@ struct Smem64 {
   uint16_t V[Tr::CR * Tr::LDV];   // the chunk's values (raw bf16), 32 columns per state wave
 };
 
-// the producer wave that loads the gates and runs the per-chunk decay scan
-constexpr int kScanProducer = 0;
+// the producer wave that loads the gates and runs the per-chunk decay scan (with outputs;
+// without them, producer 3, which then has no tiles of P to form)
+template <bool OUT>
+constexpr int scan_producer() { return OUT ? 0 : 3; }
 
 struct Scan64 {
   float g2, gb, eg, egl, b;
@@ -391,10 +392,35 @@ __device__ __forceinline__ void p64_prows(const Stage64<Tr> &s, Solve64<Tr> &v, 
   }
 }
 
-// The solve of one chunk; the diagonal blocks of A are in AR already.
+// A_32 on its own (the pass that writes no outputs)
 template <class Tr>
+__device__ __forceinline__ void p64_a32(const Stage64<Tr> &s, Solve64<Tr> &v, int lane) {
+  using M = typename Tr::M;
+  typename M::frag f2[Tr::KS], f3[Tr::KS];
+  p64_block<Tr>(s.K, 2, lane, f2);
+  p64_block<Tr>(s.K, 3, lane, f3);
+  const int q = 48 + (lane & 15);
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int sl = 0; sl < Tr::KS; ++sl) acc = M::mma(f2[sl], f3[sl], acc);
+  p64_tile_out<Tr, false>(s, acc, s.GB[q], 0, v.A + q * Tr::LDA, 2, lane);
+}
+
+// The solve of one chunk; the diagonal blocks of A are in AR already.  Without
+// outputs there is no P to form, and the producers share the rest: the inversions (0),
+// five off-diagonal blocks (1), A_32 (2); producer 3 runs the decay scan.
+template <class Tr, bool OUT>
 __device__ __forceinline__ void p64_solve(const Stage64<Tr> &s, Solve64<Tr> &v,
                                           float (*AR)[Tr::ARB], int pw, float scale, int lane) {
+  if constexpr (!OUT) {
+    if (pw == 0)
+      p64_invert<Tr>(v, AR, lane);
+    else if (pw == 1)
+      p64_offdiag<Tr>(s, v, lane);
+    else if (pw == 2)
+      p64_a32<Tr>(s, v, lane);
+    return;
+  }
   if (pw == 0) {
     // A_32 beside the inversion: its operands are read first, its products issued after
     using M = typename Tr::M;
@@ -423,7 +449,11 @@ __device__ __forceinline__ void p64_solve(const Stage64<Tr> &s, Solve64<Tr> &v,
   }
 }
 
-template <typename TOut, int DK, int NH, int NS>
+// OUT = false: the call writes no outputs (out == NULL: the passes of a long sequence in
+// segments that only carry states, the backward's forward recompute).  Then neither Q
+// nor P is needed: Q is neither fetched nor staged, P not formed, and the state waves
+// skip the output products.
+template <typename TOut, int DK, int NH, int NS, bool OUT>
 __global__ void __launch_bounds__(64 * (NS + 4))
 prefill64_kernel(const PrefillParams p) {
   using Tr = P64<DK, NH, NS>;
@@ -535,8 +565,10 @@ prefill64_kernel(const PrefillParams p) {
     const __amdgpu_buffer_rsrc_t rk = k_rsrc(c), rq = q_rsrc(c);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) cr.k[j].u = load16(rk, k_off(j));
+    if constexpr (OUT) {
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) cr.q[j].u = load16(rq, q_off(j));
+      for (int j = 0; j < QPT; ++j) cr.q[j].u = load16(rq, q_off(j));
+    }
   };
   // the gates of the chunk starting at row c (producer 0; requested a whole interval
   // before the decay scan reads them)
@@ -594,9 +626,9 @@ prefill64_kernel(const PrefillParams p) {
       }
     }
     // Q: segment u % SEG of row u / SEG, u = stid + j ST (a row's SEG segments in
-    // consecutive lanes)
+    // consecutive lanes); only with outputs
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
+    for (int j = 0; j < (OUT ? QPT : 0); ++j) {
       const int u = stid + j * ST, r = u / SEG, sg = u % SEG;
       if constexpr (L2) {
         float x[8];
@@ -792,7 +824,7 @@ prefill64_kernel(const PrefillParams p) {
       }
       // D as the operands of phase B: db = D (for O), dk = diag(exp(G_last - G)) D (for
       // the state update), both fp16
-      frag db[2][2], dk[2][2];
+      frag db[2][2], dk[2][2];   // db unused without outputs
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
         const float4 l0 = *reinterpret_cast<const float4 *>(f.eGl + 32 * sk + 4 * g4);
@@ -801,7 +833,7 @@ prefill64_kernel(const PrefillParams p) {
         const f32x4 e1 = {l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          db[ct][sk] = M::from_acc(D[ct][2 * sk], D[ct][2 * sk + 1]);
+          if constexpr (OUT) db[ct][sk] = M::from_acc(D[ct][2 * sk], D[ct][2 * sk + 1]);
           dk[ct][sk] = M::from_acc(D[ct][2 * sk] * e0, D[ct][2 * sk + 1] * e1);
         }
       }
@@ -812,42 +844,44 @@ prefill64_kernel(const PrefillParams p) {
       // and the one after is requested)
       put_v();
       load_v(c0 + 2 * CR);
-      // O^T = scale H0^T Q^T diag(exp G) + D^T P^T (P carries the scale): a lane holds
-      // output columns 4 g4 .. 4 g4 + 3 of token l16 of each query block.
-      float sx[NQB];
-#pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) sx[mq] = p.scale * f.eG[NH * (16 * mq + l16) + NH - 1];
-      // this chunk's output rows through a buffer resource whose range ends at the
-      // sequence's last token (no rows at all without outputs): stores to rows past it
-      // are dropped by the range check, with no branch around them
-      const int orows = ob ? min(CQ, t1 - tq0) : 0;
-      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-          ob ? ob + static_cast<size_t>(tq0) * vstride : nullptr, 0,
-          orows * static_cast<int>(vstride * sizeof(TOut)), kBufferWord3);
-      // operand reads are issued one block ahead of the products that use them
-      frag qf[2][KS], pf[2][2];
-      auto load_qp = [&](int mq) __attribute__((always_inline)) {
-        const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;   // key slices reaching the block
-#pragma unroll
-        for (int sl = 0; sl < KS; ++sl) qf[mq & 1][sl] = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-          if (sk < nsk) pf[mq & 1][sk] = M::load(v.P, LDA, 16 * mq + l16, 32 * sk, lane);
-      };
-      load_qp(0);
-#pragma unroll
-      for (int mq = 0; mq < NQB; ++mq) {
-        if (mq + 1 < NQB) load_qp(mq + 1);
-        const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          f32x4 xo = zero4();
-#pragma unroll
-          for (int sl = 0; sl < KS; ++sl) xo = M::mma(hb[ct][sl], qf[mq & 1][sl], xo);
-          f32x4 yo = M::mma(db[ct][0], pf[mq & 1][0], zero4());
-          if (nsk > 1) yo = M::mma(db[ct][1], pf[mq & 1][1], yo);
-          store4_rsrc<TOut>(orsrc, ((16 * mq + l16) * vstride + 16 * ct + 4 * g4) * sizeof(TOut),
-                            sx[mq] * xo + yo);
+      if constexpr (OUT) {
+        // O^T = scale H0^T Q^T diag(exp G) + D^T P^T (P carries the scale): a lane holds
+        // output columns 4 g4 .. 4 g4 + 3 of token l16 of each query block.
+        float sx[NQB];
+  #pragma unroll
+        for (int mq = 0; mq < NQB; ++mq) sx[mq] = p.scale * f.eG[NH * (16 * mq + l16) + NH - 1];
+        // this chunk's output rows through a buffer resource whose range ends at the
+        // sequence's last token (no rows at all without outputs): stores to rows past it
+        // are dropped by the range check, with no branch around them
+        const int orows = ob ? min(CQ, t1 - tq0) : 0;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            ob ? ob + static_cast<size_t>(tq0) * vstride : nullptr, 0,
+            orows * static_cast<int>(vstride * sizeof(TOut)), kBufferWord3);
+        // operand reads are issued one block ahead of the products that use them
+        frag qf[2][KS], pf[2][2];
+        auto load_qp = [&](int mq) __attribute__((always_inline)) {
+          const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;   // key slices reaching the block
+  #pragma unroll
+          for (int sl = 0; sl < KS; ++sl) qf[mq & 1][sl] = M::load(s.Q, LDK, 16 * mq + l16, 32 * sl, lane);
+  #pragma unroll
+          for (int sk = 0; sk < 2; ++sk)
+            if (sk < nsk) pf[mq & 1][sk] = M::load(v.P, LDA, 16 * mq + l16, 32 * sk, lane);
+        };
+        load_qp(0);
+  #pragma unroll
+        for (int mq = 0; mq < NQB; ++mq) {
+          if (mq + 1 < NQB) load_qp(mq + 1);
+          const int nsk = (NH * (16 * mq + 16) - 1) / 32 + 1;
+  #pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            f32x4 xo = zero4();
+  #pragma unroll
+            for (int sl = 0; sl < KS; ++sl) xo = M::mma(hb[ct][sl], qf[mq & 1][sl], xo);
+            f32x4 yo = M::mma(db[ct][0], pf[mq & 1][0], zero4());
+            if (nsk > 1) yo = M::mma(db[ct][1], pf[mq & 1][1], yo);
+            store4_rsrc<TOut>(orsrc, ((16 * mq + l16) * vstride + 16 * ct + 4 * g4) * sizeof(TOut),
+                              sx[mq] * xo + yo);
+          }
         }
       }
       // H <- exp(G_last) H0 + K^T diag(exp(G_last - G)) D
@@ -880,10 +914,11 @@ prefill64_kernel(const PrefillParams p) {
     // prologue: chunk 0 staged and solved, chunk 1 fetched.  Interval ci: stage chunk
     // ci+1, each register refilled with chunk ci+2's inputs as soon as it is staged
     // (phase A); solve chunk ci+1 (phase B).  The loads have almost an interval to land.
-    // The decay scan of a chunk runs on producer 0 in the phase B two phases before the
-    // chunk's solve, and each producer forms its diagonal block of A from its staged K
-    // registers in the phase A before the solve, so that producer 0's share of the solve
-    // is the inversion, one off-diagonal block and the scan.
+    // The decay scan of a chunk runs in the phase B two phases before the chunk's solve
+    // (on producer 0 with outputs, on producer 3 without), and each producer forms its
+    // diagonal block of A from its staged K registers in the phase A before the solve, so
+    // that producer 0's share of the solve is the inversion, one off-diagonal block and
+    // the scan.  Without outputs no Q is loaded or staged and no P is formed.
     // The producer that runs the decay scan (SCAN) has its own copy of the loop: its
     // gate loads are then the only loads after the chunk inputs on its path, and the
     // waits for those inputs count them exactly instead of waiting for every load.
@@ -904,7 +939,7 @@ prefill64_kernel(const PrefillParams p) {
       __syncthreads();
       if (nchunks > 0) {
         if (pw == 0) p64_diag_lds<Tr>(sm.st[0], sm.AR, lane);
-        p64_solve<Tr>(sm.st[0], sm.sv[0], sm.AR, pw, p.scale, lane);
+        p64_solve<Tr, OUT>(sm.st[0], sm.sv[0], sm.AR, pw, p.scale, lane);
       }
       if (SCAN && nchunks > 1) {
         sc = scan(rg, row_begin + CR);
@@ -929,7 +964,7 @@ prefill64_kernel(const PrefillParams p) {
         }
         __syncthreads();
         if (next)
-          p64_solve<Tr>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
+          p64_solve<Tr, OUT>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
         if (SCAN && ci + 2 < nchunks) {
           sc = scan(rg, row_begin + (ci + 2) * CR);
           put_bases(sc, sm.st[ci & 1]);   // chunk ci + 2 takes chunk ci's buffer
@@ -939,7 +974,7 @@ prefill64_kernel(const PrefillParams p) {
         __syncthreads();
       }
     };
-    if (pw == kScanProducer) {
+    if (pw == scan_producer<OUT>()) {
       if (p.l2norm)
         run(std::true_type(), std::true_type());
       else
@@ -960,11 +995,14 @@ namespace {
 template <int DK, int NH, int NS>
 hipError_t launch64_one(const PrefillParams &p, int grid, hipStream_t stream) {
   constexpr int threads = 64 * P64<DK, NH, NS>::NW;
-  if (p.out_bf16)
-    hipLaunchKernelGGL((prefill64_kernel<__bf16, DK, NH, NS>), dim3(grid), dim3(threads), 0,
+  if (!p.out)
+    hipLaunchKernelGGL((prefill64_kernel<__bf16, DK, NH, NS, false>), dim3(grid), dim3(threads),
+                       0, stream, p);
+  else if (p.out_bf16)
+    hipLaunchKernelGGL((prefill64_kernel<__bf16, DK, NH, NS, true>), dim3(grid), dim3(threads), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((prefill64_kernel<float, DK, NH, NS>), dim3(grid), dim3(threads), 0,
+    hipLaunchKernelGGL((prefill64_kernel<float, DK, NH, NS, true>), dim3(grid), dim3(threads), 0,
                        stream, p);
   return hipGetLastError();
 }
