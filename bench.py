@@ -38,7 +38,8 @@ Nine legs, each timed over exactly K steps bracketed by torch.cuda.synchronize()
            bf16 inputs run on the fp16 matrix cores) and the HBM rate of its
            algorithmic bytes; the roofline object is the one of the two whose
            algorithmic time at peak is longer (HBM at these shapes).
-Per-launch kernel durations come from HIP events on the launch stream.  The
+Kernel durations come from HIP events on the launch stream: one pair around the K
+back-to-back launches (a pair around each launch where a cache flush precedes it).  The
 roofline object is for the headline prefill kernel: algorithmic HBM bytes per
 launch (inputs read once, outputs and states written once) over the mean launch
 time, against 8 TB/s.  The CPU baseline is the fp64 oracle on a bounded sample
@@ -266,17 +267,19 @@ def time_launches(launch, steps, warmup, before=None):
     stream = torch.cuda.current_stream()
     wall = 0.0
     if before is None:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        # one event pair around the K back-to-back launches: an event between launches
+        # would add its own marker packet (and cache release) to every launch's time
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            starts[i].record(stream)
+        start.record(stream)
+        for _ in range(steps):
             launch()
-            ends[i].record(stream)
+        end.record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
-        evs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        evs = [start.elapsed_time(end) / steps]
     else:
         # per-launch preparation (cache flush) stays outside the timed launches
         for i in range(steps):
