@@ -266,15 +266,12 @@ struct RowInputs {
     }
   }
 };
+// the row factors of one chunk, on all 64 lanes of wave 0: the fp64 prefix sum of g
+// runs on DPP lane moves (the prefill's scan)
 __device__ __forceinline__ void row_factors(RowFactors &rf, const RowInputs &ri, int tid) {
   if (tid < BC) {
-    double x = static_cast<double>(ri.g);
-#pragma unroll
-    for (int o = 1; o < BC; o <<= 1) {
-      const double y = __shfl_up(x, o, 64);
-      if (tid >= o) x += y;
-    }
-    const double last = __shfl(x, BC - 1, 64);
+    const double x = prefix_sum64(static_cast<double>(ri.g));
+    const double last = readlane_f64(x, BC - 1);
     rf.G[tid] = x;
     rf.beta[tid] = ri.beta;
     rf.eG[tid] = expf(static_cast<float>(x));
@@ -775,7 +772,9 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
   constexpr int TPS = (BC / 16) * (CW / 16) / NACT;
   static_assert(TPH >= 1 && TPS >= 1, "column tile");
   const bool sact = (threadIdx.x >> 6) < NACT;
-  __shared__ __align__(16) _Float16 hK[BC * LDKH];
+  // K and the row factors are double-buffered: the last products of a step read them
+  // while the next chunk is staged
+  __shared__ __align__(16) _Float16 hK[2][BC * LDKH];
   __shared__ __align__(16) _Float16 hQ[BC * LDKH];
   __shared__ __align__(16) _Float16 hPh[BC * LDS64], hPl[BC * LDS64];
   __shared__ __align__(16) _Float16 hTh[BC * LDS64], hTl[BC * LDS64];
@@ -784,7 +783,7 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
   __shared__ __align__(16) _Float16 hSh[BC * LDO], hSl[BC * LDO];   // diag(scale e^G) dO
   __shared__ __align__(16) _Float16 hRh[BC * LDO], hRl[BC * LDO];   // -diag(beta e^G) dR
   __shared__ __align__(16) _Float16 hHh[CW * LDHT], hHl[CW * LDHT]; // dH^T
-  __shared__ RowFactors rf;
+  __shared__ RowFactors rfs[2];
   auto put_hl = [](_Float16 *hi, _Float16 *lo, int i, float x) {
     const _Float16 a = static_cast<_Float16>(x);
     hi[i] = a;
@@ -803,6 +802,8 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
   int t0, t1;
   seq_span(p, n, t0, t1);
   const int nch = (t1 - t0 + BC - 1) / BC;
+  // read once: a reload inside the loop would wait for every load and store in flight
+  const int cb0 = p.cb[n];
   const size_t ss = static_cast<size_t>(D) * D;
 
   const WTile<CW, TPH> wh(wave);
@@ -823,7 +824,7 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
   RowInputs fr;
   auto fetch = [&](int jc) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
-    const size_t cc = static_cast<size_t>(p.cb[n] + jc) * p.Hv + h;
+    const size_t cc = static_cast<size_t>(cb0 + jc) * p.Hv + h;
     fr.fetch(p, h, ts, rows, tid);
     fk.fetch(static_cast<const TQK *>(p.k), p.Hk, hk, ts, rows, 0, tid);
     fq.fetch(static_cast<const TQK *>(p.q), p.Hk, hk, ts, rows, 0, tid, p.nh);
@@ -831,12 +832,20 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
     fp.fetch(p.pmat + cc * BC * BC, BC, tid);
     ft.fetch(p.tmat + cc * BC * BC, BC, tid);
   };
-  if (nch > 0) fetch(nch - 1);
-  for (int jc = nch - 1; jc >= 0; --jc) {
-    const int c = p.cb[n] + jc;
+  // chunk jc from the registers into LDS (K into buffer jc & 1)
+  auto stage = [&](int jc) __attribute__((always_inline)) {
     const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
-    const size_t cc = static_cast<size_t>(c) * p.Hv + h;
-    float *dhn = p.dhn + cc * ss;
+    fk.store_h(hK[jc & 1], LDKH, rows, tid);
+    fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
+    fo.store_h(hO, LDO, rows, tid, ts, p.nh);
+    fp.store_hl(hPh, hPl, LDS64, tid);
+    ft.store_hl(hTh, hTl, LDS64, tid);
+    row_factors(rfs[jc & 1], fr, tid);
+  };
+  // dH leaving chunk jc (this wave's tiles): stored as dH_n, and as the fp16 pair of
+  // the dD products
+  auto put_dh = [&](int jc) __attribute__((always_inline)) {
+    float *dhn = p.dhn + (static_cast<size_t>(cb0 + jc) * p.Hv + h) * ss;
 #pragma unroll
     for (int t = 0; t < TPH; ++t)
 #pragma unroll
@@ -845,105 +854,127 @@ __device__ __forceinline__ void bwd_sweep_h16(const BackwardParams &p) {
         dhn[r * D + col0 + q] = dh[t][v];
         put_hl(hHh, hHl, q * LDHT + r, dh[t][v]);
       }
-    fk.store_h(hK, LDKH, rows, tid);
-    fq.store_h(hQ, LDKH, rows, tid, ts, p.nh);
-    fo.store_h(hO, LDO, rows, tid, ts, p.nh);
-    fp.store_hl(hPh, hPl, LDS64, tid);
-    ft.store_hl(hTh, hTl, LDS64, tid);
-    row_factors(rf, fr, tid);
-    if (jc > 0) fetch(jc - 1);
-    __syncthreads();
+  };
+  if (nch > 0) {
+    put_dh(nch - 1);
+    fetch(nch - 1);
+    stage(nch - 1);
+    if (nch > 1) fetch(nch - 2);
+    // Three barriers per chunk: (1) dH and the chunk staged, (2) dD and
+    // S = diag(scale e^G) dO, (3) dR and the Q^T S part of the update; then the K^T part,
+    // after which this wave puts the next chunk's dH (its operand was last read before
+    // barrier 2), stages the next chunk (every buffer written was last read before
+    // barrier 3, K into the other buffer) and requests the one after.
+    for (int jc = nch - 1; jc >= 0; --jc) {
+      const int c = cb0 + jc;
+      const int ts = t0 + BC * jc, rows = min(BC, t1 - ts);
+      const size_t cc = static_cast<size_t>(c) * p.Hv + h;
+      const _Float16 *hKc = hK[jc & 1];
+      const RowFactors &rf = rfs[jc & 1];
+      __syncthreads();
 
-    // dD = P^T dO + diag(e^{G_n - G}) (K dH)
-    if (sact) {
-      f32x4 a1[TPS], a2[TPS];
-      zero(a1);
-      zero(a2);
+      // dD = P^T dO + diag(e^{G_n - G}) (K dH)
+      if (sact) {
+        f32x4 a1[TPS], a2[TPS];
+        zero(a1);
+        zero(a2);
 #pragma unroll
-      for (int k0 = 0; k0 < BC; k0 += 32) {
-        const frag ph = frag_tr(hPh, LDS64, k0, ws.r0, lane);
-        const frag pl = frag_tr(hPl, LDS64, k0, ws.r0, lane);
+        for (int k0 = 0; k0 < BC; k0 += 32) {
+          const frag ph = frag_tr(hPh, LDS64, k0, ws.r0, lane);
+          const frag pl = frag_tr(hPl, LDS64, k0, ws.r0, lane);
 #pragma unroll
-        for (int t = 0; t < TPS; ++t) {
-          const frag ob = frag_tr(hO, LDO, k0, ws.c0 + 16 * t, lane);
-          a1[t] = M::mma(pl, ob, M::mma(ph, ob, a1[t]));
+          for (int t = 0; t < TPS; ++t) {
+            const frag ob = frag_tr(hO, LDO, k0, ws.c0 + 16 * t, lane);
+            a1[t] = M::mma(pl, ob, M::mma(ph, ob, a1[t]));
+          }
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          const frag ka = M::load(hKc, LDKH, ws.r0 + l16, k0, lane);
+#pragma unroll
+          for (int t = 0; t < TPS; ++t) {
+            const frag bh = M::load(hHh, LDHT, ws.c0 + 16 * t + l16, k0, lane);
+            const frag bl = M::load(hHl, LDHT, ws.c0 + 16 * t + l16, k0, lane);
+            a2[t] = M::mma(ka, bl, M::mma(ka, bh, a2[t]));
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TPS; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = ws.row(v, lane);
+            put_hl(hDh, hDl, r * LDO + ws.col(t, lane), a1[t][v] + rf.eGl[r] * a2[t][v]);
+          }
+      }
+      for (int idx = tid; idx < BC * CW; idx += BT) {
+        const int r = idx / CW, q = idx % CW;
+        put_hl(hSh, hSl, r * LDO + q, static_cast<float>(hO[r * LDO + q]) * (p.scale * rf.eG[r]));
+      }
+      __syncthreads();
+      // dR = T^T dD; dR stored, dV = diag(beta) dR and -diag(beta e^G) dR for the update
+      if (sact) {
+        f32x4 dr[TPS];
+        zero(dr);
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32) {
+          const frag th = frag_tr(hTh, LDS64, k0, ws.r0, lane);
+          const frag tl = frag_tr(hTl, LDS64, k0, ws.r0, lane);
+#pragma unroll
+          for (int t = 0; t < TPS; ++t) {
+            const frag dhi = frag_tr(hDh, LDO, k0, ws.c0 + 16 * t, lane);
+            const frag dlo = frag_tr(hDl, LDO, k0, ws.c0 + 16 * t, lane);
+            dr[t] = M::mma(tl, dhi, M::mma(th, dlo, M::mma(th, dhi, dr[t])));
+          }
+        }
+        float *drm = p.drmat + cc * BC * D;
+#pragma unroll
+        for (int t = 0; t < TPS; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = ws.row(v, lane), q = ws.col(t, lane);
+            drm[r * D + col0 + q] = dr[t][v];
+            if (r < rows)
+              p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
+                  rf.beta[r] * dr[t][v];
+            put_hl(hRh, hRl, r * LDO + q, -rf.beta[r] * rf.eG[r] * dr[t][v]);
+          }
+      }
+      // dH <- e^{G_n} dH + Q^T (diag(scale e^G) dO) ...
+      {
+        const float en = rf.eG[BC - 1];
+#pragma unroll
+        for (int t = 0; t < TPH; ++t) dh[t] *= en;
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32) {
+          const frag qa = frag_tr(hQ, LDKH, k0, wh.r0, lane);
+#pragma unroll
+          for (int t = 0; t < TPH; ++t) {
+            const int cn = wh.c0 + 16 * t;
+            const frag sh = frag_tr(hSh, LDO, k0, cn, lane);
+            const frag sl = frag_tr(hSl, LDO, k0, cn, lane);
+            dh[t] = M::mma(qa, sl, M::mma(qa, sh, dh[t]));
+          }
         }
       }
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) {
-        const frag ka = M::load(hK, LDKH, ws.r0 + l16, k0, lane);
-#pragma unroll
-        for (int t = 0; t < TPS; ++t) {
-          const frag bh = M::load(hHh, LDHT, ws.c0 + 16 * t + l16, k0, lane);
-          const frag bl = M::load(hHl, LDHT, ws.c0 + 16 * t + l16, k0, lane);
-          a2[t] = M::mma(ka, bl, M::mma(ka, bh, a2[t]));
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < TPS; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = ws.row(v, lane);
-          put_hl(hDh, hDl, r * LDO + ws.col(t, lane), a1[t][v] + rf.eGl[r] * a2[t][v]);
-        }
-    }
-    __syncthreads();
-    // dR = T^T dD; dR stored, dV = diag(beta) dR, -diag(beta e^G) dR and
-    // diag(scale e^G) dO for the dH products
-    if (sact) {
-      f32x4 dr[TPS];
-      zero(dr);
+      __syncthreads();
+      // ... + K^T (-diag(beta e^G) dR)
 #pragma unroll
       for (int k0 = 0; k0 < BC; k0 += 32) {
-        const frag th = frag_tr(hTh, LDS64, k0, ws.r0, lane);
-        const frag tl = frag_tr(hTl, LDS64, k0, ws.r0, lane);
-#pragma unroll
-        for (int t = 0; t < TPS; ++t) {
-          const frag dhi = frag_tr(hDh, LDO, k0, ws.c0 + 16 * t, lane);
-          const frag dlo = frag_tr(hDl, LDO, k0, ws.c0 + 16 * t, lane);
-          dr[t] = M::mma(tl, dhi, M::mma(th, dlo, M::mma(th, dhi, dr[t])));
-        }
-      }
-      float *drm = p.drmat + cc * BC * D;
-#pragma unroll
-      for (int t = 0; t < TPS; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = ws.row(v, lane), q = ws.col(t, lane);
-          drm[r * D + col0 + q] = dr[t][v];
-          if (r < rows)
-            p.dv[(static_cast<size_t>(ts + r) * p.Hv + h) * D + col0 + q] =
-                rf.beta[r] * dr[t][v];
-          put_hl(hRh, hRl, r * LDO + q, -rf.beta[r] * rf.eG[r] * dr[t][v]);
-        }
-    }
-    for (int idx = tid; idx < BC * CW; idx += BT) {
-      const int r = idx / CW, q = idx % CW;
-      put_hl(hSh, hSl, r * LDO + q, static_cast<float>(hO[r * LDO + q]) * (p.scale * rf.eG[r]));
-    }
-    __syncthreads();
-    // dH <- e^{G_n} dH + Q^T (diag(scale e^G) dO) + K^T (-diag(beta e^G) dR)
-    {
-      const float en = rf.eG[BC - 1];
-#pragma unroll
-      for (int t = 0; t < TPH; ++t) dh[t] *= en;
-#pragma unroll
-      for (int k0 = 0; k0 < BC; k0 += 32) {
-        const frag qa = frag_tr(hQ, LDKH, k0, wh.r0, lane);
-        const frag ka = frag_tr(hK, LDKH, k0, wh.r0, lane);
+        const frag ka = frag_tr(hKc, LDKH, k0, wh.r0, lane);
 #pragma unroll
         for (int t = 0; t < TPH; ++t) {
           const int cn = wh.c0 + 16 * t;
-          const frag sh = frag_tr(hSh, LDO, k0, cn, lane);
-          const frag sl = frag_tr(hSl, LDO, k0, cn, lane);
           const frag rh = frag_tr(hRh, LDO, k0, cn, lane);
           const frag rl = frag_tr(hRl, LDO, k0, cn, lane);
-          dh[t] = M::mma(qa, sl, M::mma(qa, sh, dh[t]));
           dh[t] = M::mma(ka, rl, M::mma(ka, rh, dh[t]));
         }
       }
+      if (jc > 0) {
+        put_dh(jc - 1);
+        stage(jc - 1);
+        if (jc > 1) fetch(jc - 2);
+      }
     }
-    __syncthreads();
   }
   if (p.d_initial_state) {
     float *s = p.d_initial_state + (static_cast<size_t>(n) * p.Hv + h) * ss;
