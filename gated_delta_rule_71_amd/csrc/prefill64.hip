@@ -108,6 +108,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base
   return __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo), 0, bytes, kBufferWord3);
 }
+// Gates from raw projections (g = -A softplus(alpha + dt_bias), beta = sigmoid(b)) on
+// the hardware exp2, log2 and reciprocal, each within about 1 ulp: this kernel's
+// inputs are bf16, whose rounding is far coarser.  softplus(x) = max(x, 0) +
+// log1p(e^-|x|), with log1p(y) = ln(u) y / (u - 1) for u = 1 + y (u - 1 is exact;
+// y itself when u rounds to 1), so that exp never overflows and small y keep their
+// relative accuracy.
+__device__ __forceinline__ float softplus_hw(float x) {
+  const float y = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+  const float u = 1.0f + y;
+  const float l = u == 1.0f ? y
+                            : __builtin_amdgcn_logf(u) * 0.6931471805599453f * y *
+                                  __builtin_amdgcn_rcpf(u - 1.0f);
+  return fmaxf(x, 0.0f) + l;
+}
+__device__ __forceinline__ float sigmoid_hw(float b) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-b * 1.4426950408889634f));
+}
+
 // sixteen bytes at a byte offset of a buffer resource
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -656,8 +674,8 @@ prefill64_kernel(const PrefillParams p) {
     float gv = cr.g;
     float bv = cr.b;
     if (p.gate_mode) {
-      gv = gate_decay(cr.g, gate_A, gate_dt);
-      bv = gate_beta(cr.b);
+      gv = -gate_A * softplus_hw(cr.g + gate_dt);
+      bv = sigmoid_hw(cr.b);
     }
     const double gr = prefix_sum64((ok && (c + lane) % NH == 0) ? gv : 0.0);
     bv = ok ? bv : 0.0f;
