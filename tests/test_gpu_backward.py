@@ -101,6 +101,18 @@ def test_backward_empty_sequences_pass_dht():
     compare(x, r, True, "empty sequences")
 
 
+def test_backward_bf16_empty_and_ragged_sequences():
+    # the fp16 sweep with empty sequences (dH_T handed to dH0 with no chunk step) beside
+    # ragged ones, D = 128, grouped heads
+    bw = W.backward_workload("bwd_bf16_empty", 16, Hk=2, Hv=4, D=128, dtype=W.BF16,
+                             lengths=[0, 70, 0, 1, 64, 130], decay="config")
+    x = gpu_backward(bw)
+    r = oracle_backward(bw)
+    for i in (0, 2):
+        assert np.array_equal(x["dh0"][i], bw.dht[i].astype(np.float64))
+    compare(x, r, False, "bf16 empty and ragged")
+
+
 def test_backward_deterministic():
     bw = W.backward_workload("bwd_det", 16, Hk=2, Hv=4, D=128, dtype=W.BF16,
                              lengths=[300, 77], decay="config")
