@@ -95,12 +95,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 1 << 30     # the calibration copy reads and writes 1 GiB each
 
 
-def kernel_source_hash(name):
-    """sha256 of a kernel source file: ties stored counter data to the code measured."""
+def kernel_source_hash(name, text=None):
+    """sha256 of a kernel source file's code (comments and whitespace removed): ties
+    stored counter data to the code measured, not to its commentary."""
     import hashlib
-    path = os.path.join(ROOT, "gated_delta_rule_71_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    if text is None:
+        path = os.path.join(ROOT, "gated_delta_rule_71_amd", "csrc", name)
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+    code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = re.sub(r"\s+", "", code)
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def stored_traffic(kernel, source):

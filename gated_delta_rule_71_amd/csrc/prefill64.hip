@@ -937,9 +937,10 @@ prefill64_kernel(const PrefillParams p) {
     // diagonal block of A from its staged K registers in the phase A before the solve, so
     // that producer 0's share of the solve is the inversion, one off-diagonal block and
     // the scan.  Without outputs no Q is loaded or staged and no P is formed.
-    // The producer that runs the decay scan (SCAN) has its own copy of the loop: its
-    // gate loads are then the only loads after the chunk inputs on its path, and the
-    // waits for those inputs count them exactly instead of waiting for every load.
+    // The producer that runs the decay scan (SCAN) has its own copy of the loop, so the
+    // gate loads and the scan are compiled only there.  (The compiler's wait counts
+    // in that copy leave out the two gate loads issued at the end of phase B: the
+    // staging's last register slot also waits for the first of them.)
     auto run = [&](auto l2c, auto scanc) __attribute__((always_inline)) {
       constexpr bool SCAN = decltype(scanc)::value;
       Scan64 sc{};   // the scan producer: the decay factors of one chunk
