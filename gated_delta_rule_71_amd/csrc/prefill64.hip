@@ -938,9 +938,7 @@ prefill64_kernel(const PrefillParams p) {
     // that producer 0's share of the solve is the inversion, one off-diagonal block and
     // the scan.  Without outputs no Q is loaded or staged and no P is formed.
     // The producer that runs the decay scan (SCAN) has its own copy of the loop, so the
-    // gate loads and the scan are compiled only there.  (The compiler's wait counts
-    // in that copy leave out the two gate loads issued at the end of phase B: the
-    // staging's last register slot also waits for the first of them.)
+    // gate loads and the scan are compiled only there.
     auto run = [&](auto l2c, auto scanc) __attribute__((always_inline)) {
       constexpr bool SCAN = decltype(scanc)::value;
       Scan64 sc{};   // the scan producer: the decay factors of one chunk
@@ -969,6 +967,16 @@ prefill64_kernel(const PrefillParams p) {
       __syncthreads();
       for (int ci = 0; ci < nchunks; ++ci) {
         const bool next = ci + 1 < nchunks;
+        // the scan producer requests the gates of chunk ci + 3 first (rows clamped to
+        // the sequence), into registers of their own that take the place of the current
+        // ones after this interval's scan: issued before the staging and unconditionally,
+        // they are counted in the staging's waits, which then no longer wait for them
+        float gnext = 0.0f, bnext = 0.0f;
+        if constexpr (SCAN) {
+          const int row = min(row_begin + (ci + 3) * CR + lane, row_end - 1);
+          gnext = gb[static_cast<uint32_t>(row / NH) * p.Hv];
+          bnext = bb[static_cast<uint32_t>(row) * p.Hv];
+        }
         if (next) {
           Stage64<Tr> &sn = sm.st[(ci + 1) & 1];
           // this producer's diagonal block K_pw K_pw^T of chunk ci + 1 is formed after
@@ -984,11 +992,14 @@ prefill64_kernel(const PrefillParams p) {
         __syncthreads();
         if (next)
           p64_solve<Tr, OUT>(sm.st[(ci + 1) & 1], sm.sv[(ci + 1) & 1], sm.AR, pw, p.scale, lane);
-        if (SCAN && ci + 2 < nchunks) {
-          sc = scan(rg, row_begin + (ci + 2) * CR);
-          put_bases(sc, sm.st[ci & 1]);   // chunk ci + 2 takes chunk ci's buffer
-          put_factors(sc, sm.fac[(ci + 2) % 3]);
-          if (ci + 3 < nchunks) fetch_gates(rg, row_begin + (ci + 3) * CR);
+        if constexpr (SCAN) {
+          if (ci + 2 < nchunks) {
+            sc = scan(rg, row_begin + (ci + 2) * CR);
+            put_bases(sc, sm.st[ci & 1]);   // chunk ci + 2 takes chunk ci's buffer
+            put_factors(sc, sm.fac[(ci + 2) % 3]);
+          }
+          rg.g = gnext;
+          rg.b = bnext;
         }
         __syncthreads();
       }
