@@ -1667,28 +1667,47 @@ __global__ void bwd_group_sum_kernel(const BackwardParams p, long total_q, long 
 
 // ---- in-kernel L2 norm and gates from raw projections ------------------------------
 
-// one wave per (token, q/k head) row of D: x / sqrt(sum x^2 + 1e-6) into fp32 copies
+// The rows of D elements of the L2 norm kernels: eight consecutive elements per lane
+// (one 16-byte load of bf16), D / 8 lanes per row, 64 / (D / 8) rows per wave; a row's
+// sums are reduced over its lane group.  Rows past the end load zeros and store nothing,
+// so that every lane takes part in the shuffles.
+template <int D>
+struct L2Rows {
+  static constexpr int LPR = D / 8, RPW = 64 / LPR, RPB = 4 * RPW;   // 256 threads
+  static __device__ __forceinline__ float sum(float x) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+  }
+};
+
+// (token, q/k head) rows of D: x / sqrt(sum x^2 + 1e-6) into fp32 copies
 template <typename TIn, int D>
-__global__ void bwd_l2norm_kernel(const BackwardParams p, float *qn, float *kn, long rows_q,
-                                  long rows) {
-  const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
+__global__ void __launch_bounds__(256) bwd_l2norm_kernel(const BackwardParams p, float *qn,
+                                                         float *kn, long rows_q, long rows) {
+  using R = L2Rows<D>;
   const int lane = threadIdx.x & 63;
-  constexpr int E = D / 64;
-  for (int w = row < rows_q ? 0 : 1; w < 2; ++w) {
-    const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
-    float *dst = (w ? kn : qn) + row * D;
-    float x[E], ss = 0.0f;
+  const long row = (static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * R::RPW +
+                   lane / R::LPR;
+  const int c0 = 8 * (lane % R::LPR);
+  for (int w = 0; w < 2; ++w) {   // q rows exist below rows_q, k rows below rows
+    const bool has = row < (w ? rows : rows_q);
+    Seg8<TIn> in;
+    if (has)
+      in.load(static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D + c0);
+    else
+      in.zero();
+    float x[8], ss = 0.0f;
+    in.get(x);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      x[e] = load_f32<TIn>(src + lane + 64 * e);
-      ss = fmaf(x[e], x[e], ss);
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    const float rn = 1.0f / sqrtf(R::sum(ss) + 1e-6f);
+    if (has) {
+      float *dst = (w ? kn : qn) + row * D + c0;
+      *reinterpret_cast<float4 *>(dst) = make_float4(x[0] * rn, x[1] * rn, x[2] * rn, x[3] * rn);
+      *reinterpret_cast<float4 *>(dst + 4) =
+          make_float4(x[4] * rn, x[5] * rn, x[6] * rn, x[7] * rn);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    const float rn = 1.0f / sqrtf(ss + 1e-6f);
-#pragma unroll
-    for (int e = 0; e < E; ++e) dst[lane + 64 * e] = x[e] * rn;
   }
 }
 
@@ -1704,33 +1723,44 @@ __global__ void bwd_gates_kernel(const BackwardParams p, float *g, float *beta, 
 }
 
 // dx = (dx^ - x^ (x^ . dx^)) / n with n = sqrt(sum x^2 + 1e-6), x^ = x / n, in place
-// on dq and dk (one wave per row)
+// on dq and dk (rows as in the norm kernel above)
 template <typename TIn, int D>
-__global__ void bwd_l2norm_grad_kernel(const BackwardParams p, long rows_q, long rows) {
-  const long row = static_cast<long>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
+__global__ void __launch_bounds__(256) bwd_l2norm_grad_kernel(const BackwardParams p, long rows_q,
+                                                              long rows) {
+  using R = L2Rows<D>;
   const int lane = threadIdx.x & 63;
-  constexpr int E = D / 64;
-  for (int w = row < rows_q ? 0 : 1; w < 2; ++w) {
-    const TIn *src = static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D;
-    float *dx = (w ? p.dk : p.dq) + row * D;
-    float x[E], d[E], ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      x[e] = load_f32<TIn>(src + lane + 64 * e);
-      d[e] = dx[lane + 64 * e];
-      ss = fmaf(x[e], x[e], ss);
+  const long row = (static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * R::RPW +
+                   lane / R::LPR;
+  const int c0 = 8 * (lane % R::LPR);
+  for (int w = 0; w < 2; ++w) {   // q rows exist below rows_q, k rows below rows
+    const bool has = row < (w ? rows : rows_q);
+    float *dx = (w ? p.dk : p.dq) + row * D + c0;
+    Seg8<TIn> in;
+    Seg8<float> din;
+    if (has) {
+      in.load(static_cast<const TIn *>(w ? p.k_raw : p.q_raw) + row * D + c0);
+      din.load(dx);
+    } else {
+      in.zero();
+      din.zero();
     }
+    float x[8], d[8], ss = 0.0f;
+    in.get(x);
+    din.get(d);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    const float rn = 1.0f / sqrtf(ss + 1e-6f);
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    const float rn = 1.0f / sqrtf(R::sum(ss) + 1e-6f);
     float dot = 0.0f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) dot = fmaf(x[e] * rn, d[e], dot);
+    for (int e = 0; e < 8; ++e) dot = fmaf(x[e] * rn, d[e], dot);
+    dot = R::sum(dot);
+    if (has) {
+      float o[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
-#pragma unroll
-    for (int e = 0; e < E; ++e) dx[lane + 64 * e] = (d[e] - x[e] * rn * dot) * rn;
+      for (int e = 0; e < 8; ++e) o[e] = (d[e] - x[e] * rn * dot) * rn;
+      *reinterpret_cast<float4 *>(dx) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4 *>(dx + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
   }
 }
 
@@ -1824,14 +1854,15 @@ hipError_t launch_backward_table(const BackwardParams &p, hipStream_t stream) {
 
 template <typename TIn, int D>
 hipError_t launch_pro_d(const BackwardParams &p, hipStream_t s) {
-  if (p.q_raw) {
-    const long rows_q = p.tokens * p.Hk, rows = rows_q * p.nh;
-    hipLaunchKernelGGL((bwd_l2norm_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s, p,
-                       const_cast<float *>(static_cast<const float *>(p.q)),
+  const long rows_q = p.tokens * p.Hk, rows = rows_q * p.nh;
+  if (p.q_raw && rows > 0) {   // (an empty grid is a launch error)
+    constexpr long RPB = L2Rows<D>::RPB;
+    hipLaunchKernelGGL((bwd_l2norm_kernel<TIn, D>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
+                       p, const_cast<float *>(static_cast<const float *>(p.q)),
                        const_cast<float *>(static_cast<const float *>(p.k)), rows_q, rows);
   }
-  if (p.alpha_raw) {
-    const long n_tok = p.tokens * p.Hv, n_row = n_tok * p.nh;
+  const long n_tok = p.tokens * p.Hv, n_row = n_tok * p.nh;
+  if (p.alpha_raw && n_row > 0) {
     hipLaunchKernelGGL(bwd_gates_kernel, dim3((n_row + 255) / 256), dim3(256), 0, s, p,
                        const_cast<float *>(p.g), const_cast<float *>(p.beta), n_tok, n_row);
   }
@@ -1841,9 +1872,10 @@ hipError_t launch_pro_d(const BackwardParams &p, hipStream_t s) {
 template <typename TIn, int D>
 hipError_t launch_epi_d(const BackwardParams &p, hipStream_t s) {
   const long rows_q = p.tokens * p.Hk, rows = rows_q * p.nh;
+  constexpr long RPB = L2Rows<D>::RPB;
   if (p.q_raw && rows > 0)
-    hipLaunchKernelGGL((bwd_l2norm_grad_kernel<TIn, D>), dim3((rows + 3) / 4), dim3(256), 0, s,
-                       p, rows_q, rows);
+    hipLaunchKernelGGL((bwd_l2norm_grad_kernel<TIn, D>), dim3((rows + RPB - 1) / RPB), dim3(256),
+                       0, s, p, rows_q, rows);
   if (p.alpha_raw) hipLaunchKernelGGL(bwd_gates_grad_kernel, dim3(p.Hv), dim3(256), 0, s, p);
   return hipGetLastError();
 }
