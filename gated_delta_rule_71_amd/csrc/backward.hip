@@ -1876,7 +1876,9 @@ hipError_t launch_epi_d(const BackwardParams &p, hipStream_t s) {
   if (p.q_raw && rows > 0)
     hipLaunchKernelGGL((bwd_l2norm_grad_kernel<TIn, D>), dim3((rows + RPB - 1) / RPB), dim3(256),
                        0, s, p, rows_q, rows);
-  if (p.alpha_raw) hipLaunchKernelGGL(bwd_gates_grad_kernel, dim3(p.Hv), dim3(256), 0, s, p);
+  // gate mode (dA_log is set exactly then): runs with no tokens too, so that dA_log and
+  // ddt_bias are written (zeros) even when the projections are empty
+  if (p.dA_log) hipLaunchKernelGGL(bwd_gates_grad_kernel, dim3(p.Hv), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1892,7 +1894,7 @@ hipError_t launch_backward_prologue(const BackwardParams &p, int qkv_f32, int he
 
 hipError_t launch_backward_epilogue(const BackwardParams &p, int qkv_f32, int head,
                                     hipStream_t stream) {
-  if (p.alpha_raw == nullptr && p.q_raw == nullptr) return hipSuccess;
+  if (p.dA_log == nullptr && p.q_raw == nullptr) return hipSuccess;   // no norm, no gate mode
   if (head == 64) return qkv_f32 ? launch_epi_d<float, 64>(p, stream)
                                  : launch_epi_d<uint16_t, 64>(p, stream);
   if (head == 128) return qkv_f32 ? launch_epi_d<float, 128>(p, stream)

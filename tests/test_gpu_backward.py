@@ -159,6 +159,28 @@ def _raw_inputs(bw: W.BackwardWorkload, seed):
     return q, k, alpha, b, A_log, dt_bias
 
 
+def test_backward_no_tokens_l2norm_raw_gates():
+    # every sequence empty, with the in-kernel norm and raw gates: the norm and gate
+    # kernels have no rows (no launch), dH_T passes straight to dH0 and the per-head
+    # parameter gradients are zero
+    import torch
+    import gated_delta_rule_71_amd as gdr
+    bw = W.backward_workload("bwd_none", 24, Hk=1, Hv=2, D=128, dtype=W.BF16,
+                             lengths=[0, 0], decay="slow")
+    f = bw.fwd
+    q, k, alpha, b, A_log, dt_bias = _raw_inputs(bw, 24)
+    cu = torch.from_numpy(f.cu_seqlens).cuda()
+    out = gdr.chunk_gated_delta_rule_backward(
+        to_dev(q), to_dev(k), to_dev(f.v), to_dev(alpha), to_dev(b), to_dev(bw.do),
+        dht=to_dev(bw.dht), initial_state=to_dev(f.initial_state), cu_seqlens=cu,
+        use_qk_l2norm_in_kernel=True, A_log=to_dev(A_log), dt_bias=to_dev(dt_bias))
+    torch.cuda.synchronize()
+    x = {n: t.cpu().numpy() for n, t in zip(NAMES + ("dA_log", "ddt_bias"), out)}
+    assert np.array_equal(x["dh0"], bw.dht)
+    assert not np.any(x["dA_log"]) and not np.any(x["ddt_bias"])
+    assert all(x[n].size == 0 for n in ("dq", "dk", "dv", "dg", "dbeta"))
+
+
 @pytest.mark.parametrize("dtype", [W.F32, W.BF16])
 def test_backward_l2norm_and_raw_gates(dtype):
     import torch
