@@ -202,3 +202,17 @@ def test_ns4_full_varlen_boundary_states(raw_gates):
     print(f"NS=4 boundary entries ({len(rx)} sampled): err {e:.3e}", flush=True)
     # entries of heads that were not sampled are written too (no NaN left)
     assert np.all(np.isfinite(got)), "a boundary entry was not written"
+
+
+def test_packed_all_empty_slots_l2norm_raw_gates():
+    """Every packed sequence empty (no tokens at all) over a slot cache with one padding
+    entry, with the in-kernel norm and raw gates: each sequence's state passes through
+    its slot and the padding slot is not written, so the cache is bitwise unchanged."""
+    wl = W.with_raw_gates(W.prefill_packed("none", 71, [0, 0, 0], 2, 4, 128, 128, W.BF16, 64,
+                                           num_slots=6, slot_init="random"), 71)
+    wl.state_indices = wl.state_indices.copy()
+    wl.state_indices[1] = -1
+    before = wl.initial_state.copy()
+    o, st, _ = gpu_prefill(wl, out_dtype="bf16", use_qk_l2norm=True)
+    assert o.numel() == 0
+    assert np.array_equal(to_host(st), before)
